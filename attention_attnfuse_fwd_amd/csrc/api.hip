@@ -1,0 +1,272 @@
+// C ABI of the fused attention library: descriptor validation, variant
+// dispatch and launch.  Everything here runs on the host; validation touches
+// no device memory and makes no HIP call, so every error return happens
+// before any GPU work is enqueued.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attnfuse.h"
+#include "launch.h"
+
+using attnfuse::AttnParams;
+using attnfuse::kBandInf;
+
+namespace {
+
+constexpr long long kMaxLen = 1LL << 30;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape, dtype, stride, position and mask checks shared by fwd and decode.
+int validate_common(const attnfuse_variant_desc* d) {
+  if (!d || d->struct_size != sizeof(attnfuse_variant_desc)) return ATTNFUSE_ERR_INVALID;
+  if (d->dtype != ATTNFUSE_BF16 && d->dtype != ATTNFUSE_FP32) return ATTNFUSE_ERR_INVALID;
+  if (d->norm == ATTNFUSE_NORM_RELU) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->norm != ATTNFUSE_NORM_SOFTMAX) return ATTNFUSE_ERR_INVALID;
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->Nq < 0 || d->Nk < 0 || d->D < 1)
+    return ATTNFUSE_ERR_INVALID;
+  if (d->Hq % d->Hkv) return ATTNFUSE_ERR_INVALID;
+  if (d->D % 2) return ATTNFUSE_ERR_INVALID;
+  if (d->D != 64 && d->D != 128) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->Nq >= kMaxLen || d->Nk >= kMaxLen) return ATTNFUSE_ERR_UNSUPPORTED;
+  const int vec = d->dtype == ATTNFUSE_BF16 ? 8 : 4;  // elements per 16-byte access
+  const int64_t* strides[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
+  for (const int64_t* s : strides)
+    for (int a = 0; a < 3; ++a) {
+      if (s[a] < 0) return ATTNFUSE_ERR_INVALID;
+      if (s[a] % vec) return ATTNFUSE_ERR_UNSUPPORTED;
+    }
+  if (!(d->scale >= 0.f) || !isfinite(d->scale)) return ATTNFUSE_ERR_INVALID;
+  if (d->q_pos0 < 0 || d->k_pos0 < 0 || d->q_pos0 + d->Nq >= kMaxLen ||
+      d->k_pos0 + d->Nk >= kMaxLen)
+    return ATTNFUSE_ERR_INVALID;
+  if (d->causal != 0 && d->causal != 1) return ATTNFUSE_ERR_INVALID;
+  if (d->window < 0) return ATTNFUSE_ERR_INVALID;
+  if (d->rope) {
+    if (!d->rope_cos || !d->rope_sin || !(d->rope_theta > 0.0)) return ATTNFUSE_ERR_INVALID;
+    if (!aligned16(d->rope_cos) || !aligned16(d->rope_sin)) return ATTNFUSE_ERR_INVALID;
+    const int64_t need = (d->q_pos0 + d->Nq > d->k_pos0 + d->Nk) ? d->q_pos0 + d->Nq
+                                                                   : d->k_pos0 + d->Nk;
+    if (d->rope_table_len < need || d->rope_table_len < 1) return ATTNFUSE_ERR_INVALID;
+  }
+  if (d->bias)
+    for (int a = 0; a < 4; ++a)
+      if (d->bias_stride[a] < 0) return ATTNFUSE_ERR_INVALID;
+  if (d->bs_row_ptr) {
+    if (d->bs_block_m < 1 || d->bs_block_n < 1 || d->bs_nnz < 0 || d->bs_head_stride < 0)
+      return ATTNFUSE_ERR_INVALID;
+    if (d->bs_nnz > 0 && !d->bs_col_idx) return ATTNFUSE_ERR_INVALID;
+    const int64_t nqb = (d->Nq + d->bs_block_m - 1) / d->bs_block_m;
+    if (d->bs_head_stride > 0 && d->bs_head_stride < nqb + 1) return ATTNFUSE_ERR_INVALID;
+  }
+  return ATTNFUSE_OK;
+}
+
+// Fill the kernel parameters that fwd and decode share.
+AttnParams base_params(const void* q, const void* k, const void* v, void* out,
+                       const attnfuse_variant_desc* d) {
+  AttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = out;
+  p.B = d->B;
+  p.Hq = d->Hq;
+  p.Hkv = d->Hkv;
+  p.Nq = d->Nq;
+  p.Nk = d->Nk;
+  p.G = d->Hq / d->Hkv;
+  p.qsb = d->q_stride[0]; p.qsh = d->q_stride[1]; p.qsn = d->q_stride[2];
+  p.ksb = d->k_stride[0]; p.ksh = d->k_stride[1]; p.ksn = d->k_stride[2];
+  p.vsb = d->v_stride[0]; p.vsh = d->v_stride[1]; p.vsn = d->v_stride[2];
+  p.osb = d->o_stride[0]; p.osh = d->o_stride[1]; p.osn = d->o_stride[2];
+  const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->D);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  p.rcos = d->rope ? d->rope_cos : nullptr;
+  p.rsin = d->rope ? d->rope_sin : nullptr;
+  p.q_pos0 = (int)d->q_pos0;
+  p.k_pos0 = (int)d->k_pos0;
+  // Band in position space: lo <= p_k - p_q <= hi; then shifted to index space.
+  long long lo = -kBandInf, hi = kBandInf;
+  if (d->causal) hi = 0;
+  if (d->window > 0) {
+    lo = -(long long)(d->window - 1);
+    if (!d->causal) hi = d->window - 1;
+  }
+  p.has_band = (d->causal || d->window > 0) ? 1 : 0;
+  const long long dpos = d->k_pos0 - d->q_pos0;
+  auto clampb = [](long long x) {
+    return (int)(x < -kBandInf ? -kBandInf : (x > kBandInf ? kBandInf : x));
+  };
+  p.band_lo = lo <= -kBandInf ? -kBandInf : clampb(lo - dpos);
+  p.band_hi = hi >= kBandInf ? kBandInf : clampb(hi - dpos);
+  p.alibi = d->alibi_slopes;
+  p.bias = d->bias;
+  p.bsb = d->bias_stride[0]; p.bsh = d->bias_stride[1];
+  p.bsi = d->bias_stride[2]; p.bsj = d->bias_stride[3];
+  p.row_ptr = d->bs_row_ptr;
+  p.col_idx = d->bs_col_idx;
+  p.bm = d->bs_block_m;
+  p.bn = d->bs_block_n;
+  p.bs_head_stride = d->bs_head_stride;
+  p.bs_nnz = d->bs_nnz;
+  p.lse = d->lse;
+  return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTNFUSE_OK : ATTNFUSE_ERR_HIP; }
+
+int largest_pow2_divisor(int g, int cap) {
+  int hp = 1;
+  while (hp * 2 <= cap && g % (hp * 2) == 0) hp *= 2;
+  return hp;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attnfuse_status_string(int status) {
+  switch (status) {
+    case ATTNFUSE_OK: return "ok";
+    case ATTNFUSE_ERR_INVALID: return "invalid argument or descriptor";
+    case ATTNFUSE_ERR_UNSUPPORTED: return "unsupported variant or shape";
+    case ATTNFUSE_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case ATTNFUSE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
+                 const attnfuse_variant_desc* desc, void* stream) {
+  int st = validate_common(desc);
+  if (st != ATTNFUSE_OK) return st;
+  const attnfuse_variant_desc* d = desc;
+  // K and V may be NULL only when there are no keys (an empty tensor).
+  if (!q || !out || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return ATTNFUSE_ERR_UNSUPPORTED;
+  const bool sparse = d->bs_row_ptr != nullptr;
+  const bool bf16 = d->dtype == ATTNFUSE_BF16;
+  if (sparse) {
+    if (bf16 && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;
+    if (!bf16 && (d->bs_block_m % 64 || d->bs_block_n % 32)) return ATTNFUSE_ERR_UNSUPPORTED;
+  }
+  if (d->Nq == 0) return ATTNFUSE_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  AttnParams p = base_params(q, k, v, out, d);
+  if (d->Nk == 0) p.row_ptr = nullptr;  // nothing to visit: every row is empty
+  const bool use_sparse = p.row_ptr != nullptr;
+  p.longest_first = (d->causal && d->window == 0 && !use_sparse) ? 1 : 0;
+
+  if (!bf16) {
+    p.n_qblk = (d->Nq + 63) / 64;
+    const long long grid = (long long)d->B * d->Hq * p.n_qblk;
+    if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+    return hip_status(attnfuse::launch_fwd_fp32(p, d->D, (unsigned)grid, s));
+  }
+
+  // bf16 MFMA kernel: choose waves per workgroup (NW) and q-heads per
+  // workgroup (hp); the workgroup covers 32 * NW / hp query rows.
+  int NW = 8;
+  int hp = largest_pow2_divisor(p.G, 8);
+  if (use_sparse) {
+    if (d->bs_head_stride > 0) hp = 1;  // per-head masks: one head per workgroup
+    // The workgroup's 32 * NW / hp rows must lie inside one CSR block row.
+    bool found = false;
+    for (int nw = 8; nw >= 2 && !found; nw /= 2) {
+      const int h2 = hp < nw ? hp : nw;
+      if (d->bs_block_m % (32 * (nw / h2)) == 0) {
+        NW = nw;
+        hp = h2;
+        found = true;
+      }
+    }
+    if (!found) return ATTNFUSE_ERR_UNSUPPORTED;
+  } else {
+    const int rb_need = (d->Nq + 31) / 32;
+    while (NW > 2 && NW > hp && (NW / hp) / 2 >= rb_need) NW /= 2;
+  }
+  p.hp = hp;
+  const int RB = NW / hp;
+  p.n_units = d->B * d->Hkv * (p.G / hp);
+  p.n_qblk = (d->Nq + 32 * RB - 1) / (32 * RB);
+  const long long grid = (long long)p.n_units * p.n_qblk;
+  if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+  const bool rope = d->rope != 0;
+  const bool scoremod = d->alibi_slopes != nullptr || d->bias != nullptr;
+  hipError_t e;
+  if (d->D == 128) {
+    if (NW == 8) e = attnfuse::launch_fwd_bf16<128, 8>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+    else if (NW == 4) e = attnfuse::launch_fwd_bf16<128, 4>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+    else e = attnfuse::launch_fwd_bf16<128, 2>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+  } else {
+    if (NW == 8) e = attnfuse::launch_fwd_bf16<64, 8>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+    else if (NW == 4) e = attnfuse::launch_fwd_bf16<64, 4>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+    else e = attnfuse::launch_fwd_bf16<64, 2>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+  }
+  return hip_status(e);
+}
+
+size_t attnfuse_decode_workspace_size(const attnfuse_variant_desc* desc, int32_t num_splits) {
+  if (validate_common(desc) != ATTNFUSE_OK || num_splits < 1 || num_splits > 4096) return 0;
+  return (size_t)desc->B * desc->Hq * num_splits * (desc->D + 2) * sizeof(float);
+}
+
+int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                    const attnfuse_variant_desc* desc, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = validate_common(desc);
+  if (st != ATTNFUSE_OK) return st;
+  const attnfuse_variant_desc* d = desc;
+  if (!q || !k_cache || !v_cache || !out) return ATTNFUSE_ERR_INVALID;
+  if (d->Nq != 1 || num_splits < 1 || num_splits > 4096) return ATTNFUSE_ERR_INVALID;
+  if (d->dtype != ATTNFUSE_BF16 || d->bias || d->bs_row_ptr) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return ATTNFUSE_ERR_UNSUPPORTED;
+  const size_t need = attnfuse_decode_workspace_size(d, num_splits);
+  if (!workspace || workspace_bytes < need) return ATTNFUSE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTNFUSE_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  AttnParams p = base_params(q, k_cache, v_cache, out, d);
+  p.splits = num_splits;
+  p.chunk = (d->Nk + num_splits - 1) / num_splits;
+  if (p.chunk < 1) p.chunk = 1;
+  p.n_hgrp = (p.G + 31) / 32;
+  p.ws = reinterpret_cast<float*>(workspace);
+  const long long U = (long long)d->B * d->Hkv * p.n_hgrp;
+  const long long grid = 8 * U * ((num_splits + 7) / 8);
+  if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+  hipError_t e = attnfuse::launch_decode_split(p, d->D, d->rope != 0, (unsigned)grid, s);
+  if (e != hipSuccess) return ATTNFUSE_ERR_HIP;
+  return hip_status(attnfuse::launch_decode_combine(p, d->D, s));
+}
+
+int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, float* sin_out,
+                        void* stream) {
+  if (!(theta > 0.0) || !isfinite(theta) || D < 2 || D > 1024 || D % 2 || len < 1 ||
+      len >= kMaxLen || !cos_out || !sin_out)
+    return ATTNFUSE_ERR_INVALID;
+  return hip_status(attnfuse::launch_rope_table(theta, D, len, cos_out, sin_out,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* desc,
+                       int32_t which, void* stream) {
+  int st = validate_common(desc);
+  if (st != ATTNFUSE_OK) return st;
+  const attnfuse_variant_desc* d = desc;
+  if (!x || !x_rot || !d->rope || (which != 0 && which != 1)) return ATTNFUSE_ERR_INVALID;
+  const int H = which == 0 ? d->Hq : d->Hkv;
+  const int N = which == 0 ? d->Nq : d->Nk;
+  const int64_t* str = which == 0 ? d->q_stride : d->k_stride;
+  const int pos0 = (int)(which == 0 ? d->q_pos0 : d->k_pos0);
+  if (N == 0) return ATTNFUSE_OK;
+  const bool vec_ok = aligned16(x) && aligned16(x_rot);
+  return hip_status(attnfuse::launch_prerotate(
+      x, x_rot, d->dtype == ATTNFUSE_BF16, vec_ok, d->D, d->B, H, N, str[0], str[1], str[2],
+      pos0, d->rope_cos, d->rope_sin, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Fragment conventions (CDNA4 v_mfma_f32_32x32x16_bf16, wave64):
+//   A operand (32 x 16, row-major M x K): lane l holds row l % 32, K elements
+//     8 * (l / 32) .. 8 * (l / 32) + 7.
+//   B operand (16 x 32, K x N):           lane l holds column l % 32, K elements
+//     8 * (l / 32) .. + 7.
+//   C / D (32 x 32 fp32, 16 registers):   lane l, register r holds row
+//     8 * (r / 4) + 4 * (l / 32) + (r % 4), column l % 32.
+// The attention kernels compute S^T = K' . Q'^T (keys on rows, queries on
+// columns) so that a lane owns one query column: the row-wise softmax then
+// reduces in-lane plus one swap with lane l ^ 32, and the probability tile
+// P^T is already the B operand of O^T += V^T . P^T with no data movement.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnfuse {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBandInf = 1 << 30;  // "unbounded" band edge in index space
+
+// Kernel parameters (host fills, passed by value).
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int B, Hq, Hkv, Nq, Nk, G;  // G = Hq / Hkv
+  long long qsb, qsh, qsn;
+  long long ksb, ksh, ksn;
+  long long vsb, vsh, vsn;
+  long long osb, osh, osn;
+  float scale_log2;           // softmax scale times log2(e)
+  const float* rcos;          // RoPE tables [len][D/2] or nullptr
+  const float* rsin;
+  int q_pos0, k_pos0;
+  // Allowed iff band_lo <= j - i <= band_hi (row/column index space; the
+  // position offset k_pos0 - q_pos0 is already folded in).  has_band = 0
+  // skips the test.
+  int has_band, band_lo, band_hi;
+  const float* alibi;         // slopes [Hq] or nullptr
+  const float* bias;          // fp32 bias or nullptr
+  long long bsb, bsh, bsi, bsj;
+  const int* row_ptr;         // CSR block mask or nullptr
+  const int* col_idx;
+  int bm, bn;
+  long long bs_head_stride, bs_nnz;
+  float* lse;                 // [B, Hq, Nq] or nullptr
+  // prefill grid decomposition
+  int hp;                     // q-heads per workgroup
+  int n_units;                // B * Hkv * (G / hp)
+  int n_qblk;                 // query blocks per unit
+  int longest_first;          // schedule later (longer) query blocks first
+  // split-KV decode
+  int splits, chunk, n_hgrp;
+  float* ws;
+};
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float partner32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const int lane = threadIdx.x & 63;
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// 8 consecutive fp32 values (two 16-byte loads).
+struct F8 {
+  float4 a, b;
+};
+__device__ __forceinline__ F8 ld_f8(const float* p) {
+  F8 r;
+  r.a = *reinterpret_cast<const float4*>(p);
+  r.b = *reinterpret_cast<const float4*>(p + 4);
+  return r;
+}
+__device__ __forceinline__ float f8_at(const F8& f, int e) {
+  switch (e) {
+    case 0: return f.a.x; case 1: return f.a.y; case 2: return f.a.z; case 3: return f.a.w;
+    case 4: return f.b.x; case 5: return f.b.y; case 6: return f.b.z; default: return f.b.w;
+  }
+}
+
+// NeoX rotation of one (low, high) pair of 8-element bf16 chunks:
+//   lo' = lo * c - hi * s,  hi' = hi * c + lo * s   (fp32 math, bf16 result)
+__device__ __forceinline__ void rope_rotate_bf16x8(uint4& lo, uint4& hi, const F8& c, const F8& s) {
+  const uint32_t* wl = reinterpret_cast<const uint32_t*>(&lo);
+  const uint32_t* wh = reinterpret_cast<const uint32_t*>(&hi);
+  uint32_t ol[4], oh[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float l0 = bf16lo(wl[w]), l1 = bf16hi(wl[w]);
+    const float h0 = bf16lo(wh[w]), h1 = bf16hi(wh[w]);
+    const float c0 = f8_at(c, 2 * w), c1 = f8_at(c, 2 * w + 1);
+    const float s0 = f8_at(s, 2 * w), s1 = f8_at(s, 2 * w + 1);
+    ol[w] = pack_bf16x2(l0 * c0 - h0 * s0, l1 * c1 - h1 * s1);
+    oh[w] = pack_bf16x2(h0 * c0 + l0 * s0, h1 * c1 + l1 * s1);
+  }
+  lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+  hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+}
+
+// Column of key `k` (index within a tile) in the transposed V tile in LDS.
+// Keys are stored with bits 2 and 3 of the index swapped, so that the 8
+// probabilities a lane holds for one 16-key MFMA step (S^T accumulator rows
+// 8*(r/4) + 4*(l/32) + r%4) meet 8 contiguous V^T elements.
+__device__ __forceinline__ constexpr int vcol(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+// Transpose a 4-key x 8-d bf16 block (4 x uint4, one per key) into 8 rows of
+// 4 keys (uint2 per d) and store row dd at dst + dd * row_stride (elements).
+__device__ __forceinline__ void store_vt_4x8(__bf16* dst, int row_stride, const uint4 (&v)[4]) {
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&v[0]);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&v[1]);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&v[2]);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&v[3]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint2 even = make_uint2(lo16x2(w0[w], w1[w]), lo16x2(w2[w], w3[w]));
+    uint2 odd = make_uint2(hi16x2(w0[w], w1[w]), hi16x2(w2[w], w3[w]));
+    *reinterpret_cast<uint2*>(dst + (2 * w) * row_stride) = even;
+    *reinterpret_cast<uint2*>(dst + (2 * w + 1) * row_stride) = odd;
+  }
+}
+
+}  // namespace attnfuse

@@ -1,0 +1,7 @@
+// bf16 prefill kernel variants for head dim 128, 2 waves per workgroup.
+#include "fwd_bf16_launch.h"
+
+namespace attnfuse {
+template hipError_t launch_fwd_bf16<128, 2>(const AttnParams&, bool, bool, bool, unsigned,
+                                                 hipStream_t);
+}  // namespace attnfuse

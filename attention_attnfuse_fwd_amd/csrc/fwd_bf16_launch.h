@@ -1,0 +1,30 @@
+// Explicit instantiation helper for the bf16 prefill kernel variants.
+#pragma once
+
+#include "fwd_bf16_kernel.h"
+#include "launch.h"
+
+namespace attnfuse {
+
+template <int D, int NW>
+hipError_t launch_fwd_bf16(const AttnParams& p, bool rope, bool scoremod, bool sparse,
+                           unsigned grid, hipStream_t stream) {
+#define ATTNFUSE_CASE(R, S, SP)                                                          \
+  if (rope == R && scoremod == S && sparse == SP) {                                      \
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, R, S, SP>), dim3(grid), dim3(NW * 64), 0, \
+                       stream, p);                                                       \
+    return hipGetLastError();                                                            \
+  }
+  ATTNFUSE_CASE(false, false, false)
+  ATTNFUSE_CASE(false, false, true)
+  ATTNFUSE_CASE(false, true, false)
+  ATTNFUSE_CASE(false, true, true)
+  ATTNFUSE_CASE(true, false, false)
+  ATTNFUSE_CASE(true, false, true)
+  ATTNFUSE_CASE(true, true, false)
+  ATTNFUSE_CASE(true, true, true)
+#undef ATTNFUSE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attnfuse

@@ -1,0 +1,31 @@
+// Internal launchers (C++ linkage, not part of the C ABI).  Each returns the
+// hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace attnfuse {
+
+// bf16 MFMA prefill kernel for head dim D with NW waves per workgroup.
+template <int D, int NW>
+hipError_t launch_fwd_bf16(const AttnParams& p, bool rope, bool scoremod, bool sparse,
+                           unsigned grid, hipStream_t stream);
+
+// fp32 prefill kernel (64 query rows per workgroup).
+hipError_t launch_fwd_fp32(const AttnParams& p, int D, unsigned grid, hipStream_t stream);
+
+// Split-KV decode phase 1 (partials into p.ws) and phase 2 (LSE merge).
+hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned grid,
+                               hipStream_t stream);
+hipError_t launch_decode_combine(const AttnParams& p, int D, hipStream_t stream);
+
+// RoPE cos / sin tables and the stand-alone pre-rotation pass.
+hipError_t launch_rope_table(double theta, int D, long long len, float* cos_out, float* sin_out,
+                             hipStream_t stream);
+hipError_t launch_prerotate(const void* x, void* x_rot, bool bf16, bool vec_ok, int D, int B,
+                            int H, int N, long long sb, long long sh, long long sn, int pos0,
+                            const float* rcos, const float* rsin, hipStream_t stream);
+
+}  // namespace attnfuse

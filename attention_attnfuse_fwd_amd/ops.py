@@ -1,0 +1,291 @@
+"""PyTorch-facing entry points over the C ABI (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of ``libattnfuse.so``;
+PyTorch supplies device memory and the current HIP stream.  Names follow the
+AttnFuse pages ("AttnFuse: A Composable DSL for Compiling Attentions to Fused
+GPU Kernels"): ``fwd`` is the fused forward of "3.3 Runtime Dispatch" with its
+decode fast path, ``decode`` the split-KV path of "4.2 Flash Decoding",
+``create_block_mask`` builds the CSR BlockMask of "4.3 Block-Sparse
+Attention", ``rope_tables`` the precomputed cos / sin tables of "4.1 Fused
+RoPE", and ``prerotate`` the separate rotation pass that fusion replaces.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Callable, Optional
+
+import numpy as np
+import torch
+
+from . import _abi
+
+
+class AttnfuseError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"attnfuse error {status} ({_abi.status_string(status)}){': ' + what if what else ''}")
+
+
+def _check(status: int, what: str = ""):
+    if status != _abi.OK:
+        raise AttnfuseError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _abi.BF16
+    if t.dtype == torch.float32:
+        return _abi.FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+# ----------------------------------------------------------------------------
+# RoPE tables
+# ----------------------------------------------------------------------------
+
+_ROPE_CACHE: dict = {}
+
+
+def rope_tables(theta: float, D: int, length: int, device) -> tuple:
+    """(cos, sin) fp32 tables [L][D/2] with L >= length, built on the device and cached."""
+    device = torch.device(device)
+    key = (float(theta), int(D), device.index if device.index is not None else torch.cuda.current_device())
+    hit = _ROPE_CACHE.get(key)
+    if hit is not None and hit[0].shape[0] >= length:
+        return hit
+    L = max(int(length), 1)
+    if hit is not None:
+        L = max(L, 2 * hit[0].shape[0])
+    cos = torch.empty((L, D // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check(_abi.load().attnfuse_rope_table(float(theta), int(D), int(L), _ptr(cos), _ptr(sin),
+                                           _stream(device)), "rope_table")
+    _ROPE_CACHE[key] = (cos, sin)
+    return cos, sin
+
+
+# ----------------------------------------------------------------------------
+# Block masks
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class BlockMask:
+    """CSR block mask: per query block, the list of active key blocks."""
+    row_ptr: torch.Tensor        # int32 [nqb + 1] (shared) or [H, nqb + 1] (per q-head)
+    col_idx: torch.Tensor        # int32 [nnz]
+    block_m: int
+    block_n: int
+
+    @property
+    def nnz(self) -> int:
+        return int(self.col_idx.numel())
+
+    @property
+    def per_head(self) -> bool:
+        return self.row_ptr.dim() == 2
+
+
+def block_mask_from_csr(row_ptr, col_idx, block_m: int, block_n: int, device) -> BlockMask:
+    rp = torch.as_tensor(np.asarray(row_ptr, dtype=np.int32)).to(device)
+    ci = torch.as_tensor(np.asarray(col_idx, dtype=np.int32)).to(device)
+    if ci.numel() == 0:
+        ci = torch.zeros(1, dtype=torch.int32, device=device)[:0]
+    return BlockMask(rp.contiguous(), ci.contiguous(), int(block_m), int(block_n))
+
+
+def create_block_mask(predicate: Callable, n_qblocks: int, n_kblocks: int, block_m: int,
+                      block_n: int, device, heads: Optional[int] = None) -> BlockMask:
+    """Evaluate ``predicate(qb, kb)`` (or ``predicate(h, qb, kb)`` with ``heads``)
+    once for every block pair on the host and return the CSR BlockMask."""
+    rows = []
+    cols = []
+    for h in range(heads or 1):
+        rp = [len(cols)]
+        for qb in range(n_qblocks):
+            for kb in range(n_kblocks):
+                ok = predicate(h, qb, kb) if heads else predicate(qb, kb)
+                if ok:
+                    cols.append(kb)
+            rp.append(len(cols))
+        rows.append(rp)
+    row_ptr = np.asarray(rows if heads else rows[0], dtype=np.int32)
+    return block_mask_from_csr(row_ptr, np.asarray(cols, dtype=np.int32), block_m, block_n, device)
+
+
+# ----------------------------------------------------------------------------
+# Descriptor marshalling
+# ----------------------------------------------------------------------------
+
+def _strides3(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, N, D]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous last (head) dimension")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def _make_desc(q, k, v, out, *, scale, causal, window, rope_theta, q_pos0, k_pos0,
+               alibi_slopes, bias, block_mask, lse, keep):
+    d = _abi.VariantDesc.new()
+    d.dtype = _dtype_code(q)
+    B, Hq, Nq, D = q.shape
+    _, Hkv, Nk, _ = k.shape
+    d.B, d.Hq, d.Hkv, d.Nq, d.Nk, d.D = B, Hq, Hkv, Nq, Nk, D
+    for name, t, field in (("q", q, "q_stride"), ("k", k, "k_stride"), ("v", v, "v_stride"),
+                           ("out", out, "o_stride")):
+        s = _strides3(t, name)
+        arr = getattr(d, field)
+        arr[0], arr[1], arr[2] = s
+    d.scale = 0.0 if scale is None else float(scale)
+    d.norm = _abi.NORM_SOFTMAX
+    d.q_pos0, d.k_pos0 = int(q_pos0), int(k_pos0)
+    d.causal = 1 if causal else 0
+    d.window = int(window or 0)
+    if rope_theta is not None:
+        need = max(int(q_pos0) + Nq, int(k_pos0) + Nk)
+        cos, sin = rope_tables(rope_theta, D, need, q.device)
+        keep.extend([cos, sin])
+        d.rope = 1
+        d.rope_theta = float(rope_theta)
+        d.rope_cos, d.rope_sin = cos.data_ptr(), sin.data_ptr()
+        d.rope_table_len = cos.shape[0]
+    if alibi_slopes is not None:
+        a = torch.as_tensor(alibi_slopes, dtype=torch.float32).to(q.device).contiguous()
+        if a.numel() != Hq:
+            raise ValueError("alibi_slopes needs one slope per query head")
+        keep.append(a)
+        d.alibi_slopes = a.data_ptr()
+    if bias is not None:
+        bt = torch.as_tensor(bias).to(device=q.device, dtype=torch.float32)
+        if bt.dim() != 4:
+            raise ValueError("bias must be 4-D, broadcastable to [B, Hq, Nq, Nk]")
+        bt = bt.expand(B, Hq, Nq, Nk)
+        keep.append(bt)
+        d.bias = bt.data_ptr()
+        for a in range(4):
+            d.bias_stride[a] = bt.stride(a)
+    if block_mask is not None:
+        keep.extend([block_mask.row_ptr, block_mask.col_idx])
+        d.bs_row_ptr = block_mask.row_ptr.data_ptr()
+        d.bs_col_idx = block_mask.col_idx.data_ptr() if block_mask.nnz else None
+        d.bs_block_m, d.bs_block_n = block_mask.block_m, block_mask.block_n
+        d.bs_head_stride = block_mask.row_ptr.shape[1] if block_mask.per_head else 0
+        d.bs_nnz = block_mask.nnz
+    if lse is not None:
+        d.lse = lse.data_ptr()
+    return d
+
+
+def _check_inputs(q, k, v):
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+
+
+def default_num_splits(B: int, Hkv: int, G: int, Nk: int, target_wgs: int = 512) -> int:
+    """Split count that gives the decode phase 1 about ``target_wgs`` workgroups."""
+    units = B * Hkv * ((G + 31) // 32)
+    s = max(1, round(target_wgs / max(units, 1)))
+    return int(max(1, min(s, max(1, math.ceil(Nk / 128)), 4096)))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+        window: int = 0, rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
+        alibi_slopes=None, bias=None, block_mask: Optional[BlockMask] = None,
+        scale: Optional[float] = None, return_lse: bool = False,
+        out: Optional[torch.Tensor] = None, decode_fast_path: bool = True):
+    """Fused attention forward; q [B, Hq, Nq, D], k / v [B, Hkv, Nk, D] on the GPU.
+
+    A single query row (Nq == 1, bf16, no bias or block mask) takes the split-KV
+    decode path, as the pages' runtime dispatch does.
+    """
+    _check_inputs(q, k, v)
+    if (decode_fast_path and q.shape[2] == 1 and q.dtype == torch.bfloat16 and bias is None
+            and block_mask is None and k.shape[2] > 0):
+        return decode(q, k, v, causal=causal, window=window, rope_theta=rope_theta,
+                      q_pos0=q_pos0, k_pos0=k_pos0, alibi_slopes=alibi_slopes, scale=scale,
+                      return_lse=return_lse, out=out)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    keep = []
+    d = _make_desc(q, k, v, out, scale=scale, causal=causal, window=window,
+                   rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0,
+                   alibi_slopes=alibi_slopes, bias=bias, block_mask=block_mask, lse=lse,
+                   keep=keep)
+    _check(_abi.load().attnfuse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(d),
+                                    _stream(q.device)), "fwd")
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_size(q, k_cache, num_splits: int) -> int:
+    d = _abi.VariantDesc.new()
+    d.dtype = _dtype_code(q)
+    d.B, d.Hq, d.Nq, d.D = q.shape
+    d.Hkv, d.Nk = k_cache.shape[1], k_cache.shape[2]
+    for f, t in (("q_stride", q), ("k_stride", k_cache), ("v_stride", k_cache), ("o_stride", q)):
+        arr = getattr(d, f)
+        arr[0], arr[1], arr[2] = _strides3(t, f)
+    return int(_abi.load().attnfuse_decode_workspace_size(ctypes.byref(d), int(num_splits)))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
+           num_splits: Optional[int] = None, causal: bool = False, window: int = 0,
+           rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
+           alibi_slopes=None, scale: Optional[float] = None, return_lse: bool = False,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Split-KV single-query decode (q [B, Hq, 1, D] bf16) with a log-sum-exp combine."""
+    _check_inputs(q, k_cache, v_cache)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if num_splits is None:
+        num_splits = default_num_splits(B, Hkv, Hq // max(Hkv, 1), Nk)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if return_lse else None
+    keep = []
+    d = _make_desc(q, k_cache, v_cache, out, scale=scale, causal=causal, window=window,
+                   rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0,
+                   alibi_slopes=alibi_slopes, bias=None, block_mask=None, lse=lse, keep=keep)
+    lib = _abi.load()
+    need = int(lib.attnfuse_decode_workspace_size(ctypes.byref(d), int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.attnfuse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), ctypes.byref(d),
+                               int(num_splits), _ptr(workspace), nbytes, _stream(q.device)),
+           "decode")
+    return (out, lse) if return_lse else out
+
+
+def prerotate(x: torch.Tensor, *, rope_theta: float, pos0: int = 0, out: Optional[torch.Tensor] = None):
+    """RoPE(x) into a new tensor (the separate pre-rotation pass)."""
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.stride() != x.stride():
+        raise ValueError("out must have the same strides as x")
+    keep = []
+    # Describe x as the key tensor (which = 1) of a one-query problem.
+    qdummy = x[:, :1, :1]
+    d = _make_desc(qdummy, x, x, qdummy, scale=None, causal=False, window=0,
+                   rope_theta=rope_theta, q_pos0=0, k_pos0=pos0, alibi_slopes=None, bias=None,
+                   block_mask=None, lse=None, keep=keep)
+    d.Hq = d.Hkv = x.shape[1]
+    _check(_abi.load().attnfuse_prerotate(_ptr(x), _ptr(out), ctypes.byref(d), 1, _stream(x.device)),
+           "prerotate")
+    return out

@@ -1,0 +1,187 @@
+/*
+ * attnfuse.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * Operation (AttnFuse: A Composable DSL for Compiling Attentions to Fused GPU
+ * Kernels, arXiv 2609.13612):
+ *
+ *     out = softmax(mask(bias(RoPE(Q) . RoPE(K)^T * scale))) . V
+ *
+ * computed exactly (online softmax, "2 Background / FlashAttention and online
+ * softmax") in one fused kernel per call.  The variant descriptor carries one
+ * field group per building block of "3.1 The Researcher Interface":
+ * scaled_dot_product (scale), rope (cos/sin table), causal, sliding_window,
+ * full (no mask field set), block_sparse (CSR BlockMask, "4.3 Block-Sparse
+ * Attention"), alibi (slopes), additive_bias (bias tensor), softmax (norm).
+ * relu_attention is named on the pages but never defined there; its enum
+ * value is reserved and rejected with ATTNFUSE_ERR_UNSUPPORTED.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  * Tensors are [B, H, N, D] with D contiguous (stride 1); the b, h, n strides
+ *    are given in elements.  Q is [B, Hq, Nq, D]; K and V are [B, Hkv, Nk, D];
+ *    the output has Q's shape with its own strides.  Hq must be a multiple of
+ *    Hkv; q-head h reads kv-head h / (Hq / Hkv) (grouped-query attention).
+ *  * dtype ATTNFUSE_BF16: Q, K, V, out are bf16; products accumulate in fp32.
+ *    dtype ATTNFUSE_FP32: everything is fp32 (no bf16 rounding anywhere).
+ *  * Positions: query row i sits at q_pos0 + i, key row j at k_pos0 + j.
+ *    They drive RoPE angles, the causal / window masks and ALiBi distances.
+ *  * Every pointer argument is caller-owned DEVICE memory (except `desc`,
+ *    which is host memory read during the call only).  The library
+ *    allocates nothing, keeps no pointer after returning, and holds no mutable
+ *    global state, so calls from several host threads are safe.
+ *  * `stream` is a hipStream_t (NULL = the default stream).  All GPU work is
+ *    enqueued asynchronously on it; the caller keeps buffers alive until the
+ *    stream has completed the work.  No call synchronises.
+ *  * Errors: argument validation happens on the host before any GPU work and
+ *    returns ATTNFUSE_ERR_INVALID (malformed arguments) or
+ *    ATTNFUSE_ERR_UNSUPPORTED (well formed but not implemented) with nothing
+ *    enqueued.  A failed kernel launch returns ATTNFUSE_ERR_HIP.  No C++
+ *    exception crosses this interface.
+ */
+#ifndef ATTNFUSE_H_
+#define ATTNFUSE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attnfuse_status {
+  ATTNFUSE_OK = 0,
+  ATTNFUSE_ERR_INVALID = -1,     /* malformed descriptor or argument          */
+  ATTNFUSE_ERR_UNSUPPORTED = -2, /* well formed, but no kernel implements it  */
+  ATTNFUSE_ERR_WORKSPACE = -3,   /* decode workspace missing or too small     */
+  ATTNFUSE_ERR_HIP = -4          /* a HIP runtime call or launch failed        */
+} attnfuse_status;
+
+typedef enum attnfuse_dtype {
+  ATTNFUSE_BF16 = 0,
+  ATTNFUSE_FP32 = 1
+} attnfuse_dtype;
+
+typedef enum attnfuse_norm {
+  ATTNFUSE_NORM_SOFTMAX = 0,
+  ATTNFUSE_NORM_RELU = 1 /* reserved: rejected with ATTNFUSE_ERR_UNSUPPORTED */
+} attnfuse_norm;
+
+/* Variant descriptor: one field group per building block.  Zero-initialise,
+ * set struct_size = sizeof(attnfuse_variant_desc), then fill what is used. */
+typedef struct attnfuse_variant_desc {
+  uint32_t struct_size;   /* must equal sizeof(attnfuse_variant_desc)               */
+  int32_t dtype;          /* attnfuse_dtype                                          */
+  int32_t B, Hq, Hkv;     /* batch, query heads, key/value heads (Hq % Hkv == 0)     */
+  int32_t Nq, Nk, D;      /* query rows, key rows, head dim (D in {64, 128})         */
+  int64_t q_stride[3];    /* element strides of Q over (b, h, n); d stride is 1      */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+
+  /* scaled_dot_product: scores are <q', k'> * scale; scale 0 means 1/sqrt(D). */
+  float scale;
+  int32_t norm;           /* attnfuse_norm                                           */
+
+  /* rope ("4.1 Fused RoPE", NeoX half-split pairs (r, r + D/2)).  rope != 0
+   * applies the rotation in-kernel to Q (once) and to every K tile.  The
+   * tables hold cos / sin of position * theta^(-2r/D) as fp32, row-major
+   * [rope_table_len][D/2]; build them with attnfuse_rope_table.  Every
+   * position used (q_pos0 + Nq - 1, k_pos0 + Nk - 1) must be below
+   * rope_table_len.  rope_theta records the base the tables were built with. */
+  int32_t rope;
+  double rope_theta;
+  const float* rope_cos;
+  const float* rope_sin;
+  int64_t rope_table_len;
+
+  int64_t q_pos0, k_pos0; /* positions of query row 0 and key row 0 (>= 0)          */
+
+  /* causal: keep p_k <= p_q.  sliding_window: window > 0 keeps
+   * 0 <= p_q - p_k < window when causal, |p_q - p_k| < window otherwise. */
+  int32_t causal;
+  int32_t window;
+
+  /* alibi: adds alibi_slopes[h] * (p_k - p_q) to the score of q-head h.
+   * NULL = off.  fp32 [Hq]. */
+  const float* alibi_slopes;
+
+  /* additive_bias: adds bias[b, h, i, j] (fp32) to the score.  Strides are in
+   * elements over (b, h, i, j); a stride of 0 broadcasts that axis.  NULL = off.
+   * Supported by attnfuse_fwd only. */
+  const float* bias;
+  int64_t bias_stride[4];
+
+  /* block_sparse (CSR BlockMask): query row i may see key j only when key
+   * block j / bs_block_n is listed in CSR row i / bs_block_m.  bs_row_ptr
+   * holds ceil(Nq / bs_block_m) + 1 offsets into bs_col_idx (bs_nnz
+   * entries); with bs_head_stride > 0, q-head h uses the row_ptr block that
+   * starts at bs_row_ptr + h * bs_head_stride (one mask per head), with 0 one
+   * mask serves every head.  The same mask serves every batch index.  Offsets
+   * are clamped to [0, bs_nnz] and columns outside the key range are skipped,
+   * so a malformed mask gives wrong numbers but no out-of-bounds access.
+   * bf16: bs_block_m % 32 == 0 and bs_block_n % 64 == 0.
+   * fp32: bs_block_m % 64 == 0 and bs_block_n % 32 == 0.
+   * NULL bs_row_ptr = dense.  Supported by attnfuse_fwd only. */
+  const int32_t* bs_row_ptr;
+  const int32_t* bs_col_idx;
+  int32_t bs_block_m, bs_block_n;
+  int64_t bs_head_stride;
+  int64_t bs_nnz;
+
+  /* Saved row statistic ("4.4 Backward Pass": L = m + log l, natural log):
+   * optional fp32 output [B, Hq, Nq], contiguous.  Rows with no visible key
+   * get -inf (and an all-zero output row).  NULL = not written. */
+  float* lse;
+} attnfuse_variant_desc;
+
+/* Fused attention forward: out = attention(q, k, v) under `desc`.
+ * q, k, v, out: device pointers laid out as described above (dtype from
+ * desc->dtype); k and v may be NULL when desc->Nk == 0 (every output row is
+ * then zero and its lse -inf).  Returns an attnfuse_status. */
+int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
+                 const attnfuse_variant_desc* desc, void* stream);
+
+/* Bytes of workspace attnfuse_decode needs for `desc` and `num_splits`
+ * (B * Hq * num_splits * (D + 2) * 4).  Returns 0 for an invalid descriptor. */
+size_t attnfuse_decode_workspace_size(const attnfuse_variant_desc* desc, int32_t num_splits);
+
+/* Split-KV single-query decode ("4.2 Flash Decoding").  desc->Nq must be 1;
+ * k_cache / v_cache are [B, Hkv, Nk, D] with key j at position k_pos0 + j.
+ * Phase 1 splits the Nk keys into num_splits chunks of ceil(Nk / num_splits)
+ * keys (trailing chunks may be short or empty), and writes one partial
+ * (m, l, acc[D]) per (b, q-head, chunk) into `workspace`; phase 2 merges the
+ * partials by log-sum-exp into `out` (and desc->lse when set).  Both kernels
+ * run on `stream`.  Supports rope, causal, window, alibi; bias and
+ * block_sparse return ATTNFUSE_ERR_UNSUPPORTED.  workspace is caller-owned
+ * device memory of at least attnfuse_decode_workspace_size bytes (else
+ * ATTNFUSE_ERR_WORKSPACE); its contents on entry do not matter.
+ * 1 <= num_splits <= 4096. */
+int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                    const attnfuse_variant_desc* desc, int32_t num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* RoPE tables ("4.1 Fused RoPE": a precomputed cos / sin table):
+ * cos_out[p][r] = cos(p * theta^(-2r/D)), sin_out likewise, for
+ * 0 <= p < len and 0 <= r < D/2, with the angle formed in fp64 and the results
+ * rounded to fp32.  cos_out, sin_out: device buffers of len * D/2 floats.
+ * D even, 2 <= D <= 1024, len >= 1, theta > 0. */
+int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, float* sin_out,
+                        void* stream);
+
+/* Pre-rotation pass (the "apply RoPE in a separate kernel" baseline of
+ * "1 Introduction" and "5.3 The Rotation Calculus"): writes RoPE(x) to x_rot.
+ * which = 0 rotates a Q-shaped tensor ([B, Hq, Nq, D], q_stride, positions
+ * q_pos0 + i); which = 1 a K-shaped one ([B, Hkv, Nk, D], k_stride,
+ * positions k_pos0 + j).  x_rot uses the same strides as x.  Uses desc's
+ * dtype, D and rope tables (desc->rope must be non-zero). */
+int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* desc,
+                       int32_t which, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* attnfuse_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNFUSE_H_ */

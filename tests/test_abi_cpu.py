@@ -1,0 +1,175 @@
+"""C-ABI checks that need no GPU: exports, struct layout, host-side validation.
+
+Every call here returns from argument validation before any HIP call or
+launch (validation is pure host code), so nothing touches a device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from attention_attnfuse_fwd_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnfuse.h")
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attnfuse_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_exactly_the_binding_exports():
+    assert _declared_functions() == sorted(_abi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    res = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True,
+                         text=True, check=True)
+    exported = set(re.findall(r"\bT (attnfuse_\w+)", res.stdout))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in _abi.VariantDesc._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){",
+            'printf("size %zu\\n", sizeof(attnfuse_variant_desc));']
+    for f in fields:
+        prog.append(f'printf("{f} %zu\\n", offsetof(attnfuse_variant_desc, {f}));')
+    prog.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", str(c), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(_abi.VariantDesc)
+    for f in fields:
+        assert int(out[f]) == getattr(_abi.VariantDesc, f).offset, f
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(_abi.status_string(s), str) and _abi.status_string(s)
+
+
+def _good_desc(**kw):
+    d = _abi.VariantDesc.new()
+    d.dtype = _abi.BF16
+    d.B, d.Hq, d.Hkv, d.Nq, d.Nk, d.D = 1, 4, 2, 64, 64, 128
+    for f, H, N in (("q_stride", 4, 64), ("k_stride", 2, 64), ("v_stride", 2, 64), ("o_stride", 4, 64)):
+        arr = getattr(d, f)
+        arr[0], arr[1], arr[2] = H * N * 128, N * 128, 128
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _fwd(lib, d):
+    return lib.attnfuse_fwd(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), None)
+
+
+def test_empty_query_is_ok_without_work(lib):
+    assert _fwd(lib, _good_desc(Nq=0)) == _abi.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), _abi.ERR_INVALID),
+    (dict(dtype=5), _abi.ERR_INVALID),
+    (dict(norm=_abi.NORM_RELU, Nq=0), _abi.ERR_UNSUPPORTED),
+    (dict(norm=9), _abi.ERR_INVALID),
+    (dict(Hq=3), _abi.ERR_INVALID),
+    (dict(D=96), _abi.ERR_UNSUPPORTED),
+    (dict(D=63), _abi.ERR_INVALID),
+    (dict(B=0), _abi.ERR_INVALID),
+    (dict(Nq=-1), _abi.ERR_INVALID),
+    (dict(scale=-1.0), _abi.ERR_INVALID),
+    (dict(scale=float("nan")), _abi.ERR_INVALID),
+    (dict(causal=2), _abi.ERR_INVALID),
+    (dict(window=-3), _abi.ERR_INVALID),
+    (dict(q_pos0=-1), _abi.ERR_INVALID),
+    (dict(rope=1), _abi.ERR_INVALID),                        # no tables
+    (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=10),
+     _abi.ERR_INVALID),                                      # table shorter than the positions
+    (dict(rope=1, rope_theta=1e4, rope_cos=0x1004, rope_sin=0x2000, rope_table_len=100),
+     _abi.ERR_INVALID),                                      # misaligned table
+    (dict(bs_row_ptr=0x1000, bs_block_m=0, bs_block_n=64), _abi.ERR_INVALID),
+    (dict(bs_row_ptr=0x1000, bs_block_m=64, bs_block_n=64, bs_nnz=3), _abi.ERR_INVALID),  # no col_idx
+    (dict(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=48, bs_block_n=64, bs_nnz=3),
+     _abi.ERR_UNSUPPORTED),
+    (dict(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=64, bs_block_n=32, bs_nnz=3),
+     _abi.ERR_UNSUPPORTED),
+    (dict(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=64, bs_block_n=64, bs_nnz=3,
+          bs_head_stride=1), _abi.ERR_INVALID),             # head stride shorter than a row_ptr
+])
+def test_fwd_rejects(lib, kw, status):
+    assert _fwd(lib, _good_desc(**kw)) == status
+
+
+def test_fwd_rejects_bad_strides_and_pointers(lib):
+    d = _good_desc()
+    d.q_stride[2] = 100  # not a multiple of 8 bf16 elements
+    assert _fwd(lib, d) == _abi.ERR_UNSUPPORTED
+    d = _good_desc()
+    d.k_stride[1] = -8
+    assert _fwd(lib, d) == _abi.ERR_INVALID
+    d = _good_desc()
+    assert lib.attnfuse_fwd(None, FAKE, FAKE, FAKE, ctypes.byref(d), None) == _abi.ERR_INVALID
+    assert lib.attnfuse_fwd(ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, ctypes.byref(d), None) \
+        == _abi.ERR_UNSUPPORTED
+    assert lib.attnfuse_fwd(FAKE, FAKE, FAKE, FAKE, None, None) == _abi.ERR_INVALID
+
+
+def test_decode_validation(lib):
+    d = _good_desc(Nq=1)
+    ws_need = lib.attnfuse_decode_workspace_size(ctypes.byref(d), 16)
+    assert ws_need == 1 * 4 * 16 * (128 + 2) * 4
+    assert lib.attnfuse_decode_workspace_size(ctypes.byref(d), 0) == 0
+    assert lib.attnfuse_decode_workspace_size(ctypes.byref(_good_desc(D=96)), 4) == 0
+    call = lambda d, s, ws, nb: lib.attnfuse_decode(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), s, ws, nb, None)
+    assert call(_good_desc(Nq=2), 16, FAKE, ws_need) == _abi.ERR_INVALID
+    assert call(d, 0, FAKE, ws_need) == _abi.ERR_INVALID
+    assert call(d, 5000, FAKE, ws_need) == _abi.ERR_INVALID
+    assert call(d, 16, FAKE, ws_need - 4) == _abi.ERR_WORKSPACE
+    assert call(d, 16, None, ws_need) == _abi.ERR_WORKSPACE
+    assert call(_good_desc(Nq=1, bias=0x1000), 16, FAKE, ws_need) == _abi.ERR_UNSUPPORTED
+    assert call(_good_desc(Nq=1, dtype=_abi.FP32), 16, FAKE, 10**9) == _abi.ERR_UNSUPPORTED
+
+
+def test_rope_table_and_prerotate_validation(lib):
+    assert lib.attnfuse_rope_table(0.0, 64, 10, FAKE, FAKE, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_rope_table(1e4, 63, 10, FAKE, FAKE, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_rope_table(1e4, 64, 0, FAKE, FAKE, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_rope_table(1e4, 64, 10, None, FAKE, None) == _abi.ERR_INVALID
+    d = _good_desc()
+    assert lib.attnfuse_prerotate(FAKE, FAKE, ctypes.byref(d), 1, None) == _abi.ERR_INVALID  # rope off
+    d = _good_desc(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=100)
+    assert lib.attnfuse_prerotate(FAKE, FAKE, ctypes.byref(d), 2, None) == _abi.ERR_INVALID
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(_abi.LibraryNotBuilt):
+        _abi.load()
+
+
+def test_product_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "attention_attnfuse_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", txt, flags=re.M), f
+                assert "oracle/" not in txt, f

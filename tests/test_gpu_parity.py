@@ -1,0 +1,354 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Small shapes are compared element by element; the full-size workloads, in the
+launch configuration the benchmark times, are compared on sampled query rows
+that the oracle computes one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_attnfuse_fwd_amd as af
+import oracle
+import workloads
+from gpu_helpers import check_close, check_lse, dev_inputs, host, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.WORKLOADS
+
+
+def _oracle_kw(w: workloads.Workload, inp: workloads.Inputs):
+    kw = dict(rope_theta=w.rope_theta, causal=w.causal, window=w.window, q_pos0=w.q_pos0,
+              k_pos0=w.k_pos0)
+    if inp.alibi_slopes is not None:
+        kw["alibi_slopes"] = inp.alibi_slopes.astype(np.float64)
+    if inp.bs_row_ptr is not None:
+        kw["block_mask"] = (inp.bs_row_ptr, inp.bs_col_idx, w.bigbird_block, w.bigbird_block)
+    return kw
+
+
+def _gpu_kw(w: workloads.Workload, inp: workloads.Inputs):
+    kw = dict(rope_theta=w.rope_theta, causal=w.causal, window=w.window, q_pos0=w.q_pos0,
+              k_pos0=w.k_pos0)
+    if inp.alibi_slopes is not None:
+        kw["alibi_slopes"] = torch.from_numpy(inp.alibi_slopes).cuda()
+    if inp.bs_row_ptr is not None:
+        kw["block_mask"] = af.block_mask_from_csr(inp.bs_row_ptr, inp.bs_col_idx, w.bigbird_block,
+                                                  w.bigbird_block, "cuda")
+    return kw
+
+
+def _run(w, inp, **extra):
+    q, k, v = dev_inputs(inp)
+    kw = _gpu_kw(w, inp)
+    kw.update(extra)
+    out, lse = af.fwd(q, k, v, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return host(out), host(lse)
+
+
+# ----------------------------------------------------------------------------
+# Element-by-element parity at oracle-sized shapes (several tiles + ragged tails)
+# ----------------------------------------------------------------------------
+
+def test_fp32_rope_causal_full_config():
+    w = W["rope_causal_fp32_n256"]
+    inp = workloads.make_inputs(w)
+    log(f"case {w.name} seed {w.seed}")
+    out, lse = _run(w, inp)
+    ref, rlse = oracle.attention(inp.q, inp.k, inp.v, **_oracle_kw(w, inp))
+    check_close(out, ref, "fp32", w.name)
+    check_lse(lse, rlse, 1e-4, w.name)
+
+
+SMALL = [
+    # (name, base workload, overrides)
+    ("llama8b_rope_causal_ragged", "llama3_8b_rope_causal_n4096", dict(Nq=300, Nk=300)),
+    ("llama8b_rope_causal_n1024", "llama3_8b_rope_causal_n4096", dict(Nq=1024, Nk=1024, B=1, Hq=8, Hkv=2)),
+    ("alibi_window_small", "alibi_causal_window1024_n8192", dict(B=1, Hq=4, Hkv=4, Nq=777, Nk=777, window=100)),
+    ("bigbird_small", "bigbird_rope_n4096", dict(B=1, Hq=4, Hkv=4, Nq=1024, Nk=1024)),
+    ("bigbird_ragged", "bigbird_rope_n4096", dict(B=1, Hq=2, Hkv=2, Nq=1000, Nk=1000)),
+]
+
+
+@pytest.mark.parametrize("name,base,over", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes_elementwise(name, base, over):
+    w = W[base].with_(**over)
+    inp = workloads.make_inputs(w)
+    log(f"case {name}: {w}")
+    out, lse = _run(w, inp)
+    ref, rlse = oracle.attention(inp.q, inp.k, inp.v, **_oracle_kw(w, inp))
+    check_close(out, ref, w.dtype, name)
+    check_lse(lse, rlse, 2e-2, name)
+
+
+VARIANTS = [
+    dict(),
+    dict(causal=True),
+    dict(window=37),
+    dict(causal=True, window=1),
+    dict(causal=True, window=65),
+    dict(rope_theta=1e4, causal=True, q_pos0=1000, k_pos0=1000),
+    dict(rope_theta=1e4, q_pos0=64, k_pos0=0),
+    dict(rope_theta=1e4, causal=True, q_pos0=200, k_pos0=0),   # queries after the keys
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("vi", range(len(VARIANTS)))
+def test_variant_grid(D, dtype, vi):
+    kw = VARIANTS[vi]
+    rng = np.random.default_rng(100 + vi + D)
+    B, Hq, Hkv, Nq, Nk = 2, 4, 2, 150, 200
+    shape_q, shape_k = (B, Hq, Nq, D), (B, Hkv, Nk, D)
+    if dtype == "bf16":
+        (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16(s, rng) for s in (shape_q, shape_k, shape_k))
+    else:
+        q, k, v = (rng.standard_normal(s).astype(np.float32) for s in (shape_q, shape_k, shape_k))
+        qb, kb, vb = q, k, v
+        q, k, v = (x.astype(np.float64) for x in (q, k, v))
+    log(f"case variant {kw} D={D} {dtype}")
+    out, lse = af.fwd(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), return_lse=True,
+                      decode_fast_path=False, **kw)
+    ref, rlse = oracle.attention(q, k, v, **kw)
+    check_close(host(out), ref, dtype, f"variant {kw}")
+    check_lse(host(lse), rlse, 2e-2 if dtype == "bf16" else 1e-4, f"variant {kw}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_alibi_and_additive_bias(dtype):
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, N, D = 2, 4, 4, 130, 64
+    if dtype == "bf16":
+        (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16((B, h, N, D), rng) for h in (Hq, Hkv, Hkv))
+    else:
+        q, k, v = (rng.standard_normal((B, h, N, D)).astype(np.float32) for h in (Hq, Hkv, Hkv))
+        qb, kb, vb = q, k, v
+        q, k, v = (x.astype(np.float64) for x in (q, k, v))
+    slopes = workloads.alibi_slopes(Hq)
+    bias = rng.standard_normal((1, Hq, N, N)).astype(np.float32)  # broadcast over batch
+    for kw_dev, kw_ref in [
+        (dict(alibi_slopes=torch.from_numpy(slopes).cuda(), causal=True),
+         dict(alibi_slopes=slopes.astype(np.float64), causal=True)),
+        (dict(bias=torch.from_numpy(bias).cuda()), dict(bias=bias.astype(np.float64))),
+        (dict(bias=torch.from_numpy(bias).cuda(), alibi_slopes=torch.from_numpy(slopes).cuda(),
+              rope_theta=1e4, window=50),
+         dict(bias=bias.astype(np.float64), alibi_slopes=slopes.astype(np.float64),
+              rope_theta=1e4, window=50)),
+    ]:
+        log(f"case bias/alibi {dtype} {sorted(kw_ref)}")
+        out, lse = af.fwd(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), return_lse=True,
+                          **kw_dev)
+        ref, rlse = oracle.attention(q, k, v, **kw_ref)
+        check_close(host(out), ref, dtype, f"bias {sorted(kw_ref)}")
+        check_lse(host(lse), rlse, 2e-2 if dtype == "bf16" else 1e-4, "bias")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_block_sparse_per_head_with_empty_rows(dtype):
+    rng = np.random.default_rng(8)
+    B, H, N, D, bs = 1, 4, 320, 64, 64
+    if dtype == "bf16":
+        (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16((B, H, N, D), rng) for _ in range(3))
+    else:
+        q, k, v = (rng.standard_normal((B, H, N, D)).astype(np.float32) for _ in range(3))
+        qb, kb, vb = q, k, v
+        q, k, v = (x.astype(np.float64) for x in (q, k, v))
+    nb = N // bs
+    rp, ci = workloads.random_csr(nb, nb, 0.4, seed=3, n_heads=H)
+    # head 0, block row 1: make it empty by rebuilding its CSR rows
+    rows = [[list(ci[rp[h, r]:rp[h, r + 1]]) for r in range(nb)] for h in range(H)]
+    rows[0][1] = []
+    rows[2][nb - 1] = []
+    flat, rps = [], []
+    for h in range(H):
+        r = [len(flat)]
+        for rr in rows[h]:
+            flat.extend(rr)
+            r.append(len(flat))
+        rps.append(r)
+    rp = np.asarray(rps, dtype=np.int32)
+    ci = np.asarray(flat, dtype=np.int32)
+    mask = af.block_mask_from_csr(rp, ci, bs, bs, "cuda")
+    log(f"case block sparse per head {dtype} nnz={ci.size}")
+    out, lse = af.fwd(to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype), return_lse=True,
+                      block_mask=mask, rope_theta=1e4)
+    ref, rlse = oracle.attention(q, k, v, rope_theta=1e4, block_mask=(rp, ci, bs, bs))
+    check_close(host(out), ref, dtype, "block sparse per head")
+    check_lse(host(lse), rlse, 2e-2 if dtype == "bf16" else 1e-4, "block sparse per head")
+    assert np.all(host(out)[0, 0, 64:128] == 0.0)
+    assert np.all(np.isneginf(host(lse)[0, 0, 64:128]))
+
+
+def test_create_block_mask_predicate_matches_csr():
+    nb = 6
+    m = af.create_block_mask(lambda qb, kb: kb <= qb or kb == 0, nb, nb, 64, 64, "cuda")
+    rp = m.row_ptr.cpu().numpy()
+    ci = m.col_idx.cpu().numpy()
+    for qb in range(nb):
+        assert list(ci[rp[qb]:rp[qb + 1]]) == [kb for kb in range(nb) if kb <= qb or kb == 0]
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads: sampled rows + properties
+# ----------------------------------------------------------------------------
+
+def _sample_rows(N, rng, extra=()):
+    fixed = {0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 255, 256, 511, 1023, 1024, N // 2, N - 2, N - 1}
+    fixed |= set(int(x) for x in rng.integers(0, N, 12))
+    fixed |= set(extra)
+    return sorted(r for r in fixed if 0 <= r < N)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_rope_causal_n4096", "alibi_causal_window1024_n8192",
+                                  "bigbird_rope_n4096"])
+def test_full_size_sampled_rows(name):
+    w = W[name]
+    inp = workloads.make_inputs(w)
+    log(f"case {name} full size, seed {w.seed}")
+    out, lse = _run(w, inp)
+    rng = np.random.default_rng(99)
+    rows = _sample_rows(w.Nq, rng, extra=(w.window - 1, w.window, w.window + 1) if w.window else ())
+    heads = [(0, 0), (w.B - 1, w.Hq - 1), (0, w.Hq // 2), (w.B - 1, 1)]
+    ref, rlse = oracle.attention(inp.q, inp.k, inp.v, rows=rows, heads=heads, **_oracle_kw(w, inp))
+    for b, h in heads:
+        check_close(out[b, h, rows], ref[b, h], w.dtype, f"{name} b{b} h{h}")
+        check_lse(lse[b, h, rows], rlse[b, h], 2e-2, f"{name} b{b} h{h}")
+    if w.causal:
+        # row 0 sees only key 0: output equals V[0] exactly (all heads)
+        G = w.Hq // w.Hkv
+        v0 = inp.v[:, np.arange(w.Hq) // G, 0, :]
+        np.testing.assert_array_equal(out[:, :, 0, :], v0)
+    assert np.all(np.isfinite(out))
+
+
+# ----------------------------------------------------------------------------
+# Decode (split-KV + LSE combine)
+# ----------------------------------------------------------------------------
+
+def test_decode_full_config_and_split_invariance():
+    w = W["llama3_70b_decode_32k"]
+    inp = workloads.make_inputs(w)
+    q, k, v = dev_inputs(inp)
+    ref, rlse = oracle.attention(inp.q, inp.k, inp.v, **_oracle_kw(w, inp))
+    outs = {}
+    for splits in (64, 1, 7, 100):
+        log(f"case decode 70b splits={splits}")
+        out, lse = af.decode(q, k, v, num_splits=splits, rope_theta=w.rope_theta, q_pos0=w.q_pos0,
+                             k_pos0=w.k_pos0, return_lse=True)
+        torch.cuda.synchronize()
+        outs[splits] = host(out)
+        check_close(outs[splits], ref, "bf16", f"decode splits={splits}")
+        check_lse(host(lse), rlse, 2e-2, f"decode splits={splits}")
+    for s in (1, 7, 100):
+        assert np.max(np.abs(outs[s] - outs[64])) <= 2e-2
+
+
+@pytest.mark.parametrize("kw", [dict(window=1000, causal=True), dict(alibi=True),
+                                dict(rope_theta=1e4, k_pos0=5)], ids=str)
+def test_decode_variants_small(kw):
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, Nk, D = 2, 8, 2, 3000, 128
+    (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16(s, rng) for s in
+                                 ((B, Hq, 1, D), (B, Hkv, Nk, D), (B, Hkv, Nk, D)))
+    kw = dict(kw)
+    okw = dict(q_pos0=Nk + kw.get("k_pos0", 0), k_pos0=kw.get("k_pos0", 0),
+               rope_theta=kw.get("rope_theta"), causal=kw.get("causal", False),
+               window=kw.get("window", 0))
+    dkw = dict(okw)
+    if kw.get("alibi"):
+        sl = workloads.alibi_slopes(Hq)
+        okw["alibi_slopes"] = sl.astype(np.float64)
+        dkw["alibi_slopes"] = torch.from_numpy(sl).cuda()
+    log(f"case decode variant {kw}")
+    out = af.decode(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), num_splits=13, **dkw)
+    ref, _ = oracle.attention(q, k, v, **okw)
+    check_close(host(out), ref, "bf16", f"decode {kw}")
+
+
+def test_fwd_single_query_uses_decode_and_matches_prefill_kernel():
+    rng = np.random.default_rng(6)
+    (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16(s, rng) for s in
+                                 ((1, 8, 1, 128), (1, 2, 777, 128), (1, 2, 777, 128)))
+    kw = dict(rope_theta=5e5, q_pos0=777)
+    a = host(af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), **kw))
+    b = host(af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"),
+                    decode_fast_path=False, **kw))
+    ref, _ = oracle.attention(q, k, v, **kw)
+    check_close(a, ref, "bf16", "fwd Nq=1 (decode)")
+    check_close(b, ref, "bf16", "fwd Nq=1 (prefill kernel)")
+
+
+# ----------------------------------------------------------------------------
+# Edge cases and properties
+# ----------------------------------------------------------------------------
+
+def test_empty_keys_give_zero_rows():
+    q = torch.randn(1, 2, 40, 128, device="cuda").bfloat16()
+    k = torch.randn(1, 2, 0, 128, device="cuda").bfloat16()
+    out, lse = af.fwd(q, k, k, return_lse=True)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_window_one_is_identity_exactly():
+    rng = np.random.default_rng(9)
+    (qb, _), (kb, _), (vb, v) = (workloads.normal_bf16((1, 4, 257, 128), rng) for _ in range(3))
+    out = af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), causal=True, window=1,
+                 rope_theta=1e4)
+    np.testing.assert_array_equal(host(out), v)
+
+
+def test_rope_shift_invariance_on_gpu():
+    rng = np.random.default_rng(10)
+    (qb, _), (kb, _), (vb, _) = (workloads.normal_bf16((1, 4, 200, 128), rng) for _ in range(3))
+    a = host(af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), causal=True, rope_theta=1e4))
+    b = host(af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), causal=True, rope_theta=1e4,
+                    q_pos0=1000, k_pos0=1000))
+    assert np.max(np.abs(a - b)) <= 2e-2 and np.mean(np.abs(a - b)) <= 2e-3
+
+
+def test_deterministic_bitwise():
+    w = W["llama3_8b_rope_causal_n4096"].with_(Nq=512, Nk=512)
+    inp = workloads.make_inputs(w)
+    a, _ = _run(w, inp)
+    b, _ = _run(w, inp)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_rope_table_matches_fp64():
+    D, L, theta = 128, 40000, 5e5
+    cos, sin = af.rope_tables(theta, D, L, "cuda")
+    torch.cuda.synchronize()
+    pos = np.array([0, 1, 4095, 32768, 39999])
+    r = np.arange(D // 2)
+    ang = pos[:, None] * np.power(theta, -2.0 * r / D)[None, :]
+    np.testing.assert_allclose(cos.cpu().numpy()[pos], np.cos(ang), rtol=0, atol=1.2e-7)
+    np.testing.assert_allclose(sin.cpu().numpy()[pos], np.sin(ang), rtol=0, atol=1.2e-7)
+
+
+def test_prerotated_path_matches_oracle():
+    w = W["llama3_8b_rope_causal_n4096"].with_(Nq=640, Nk=640)
+    inp = workloads.make_inputs(w)
+    q, k, v = dev_inputs(inp)
+    qr = af.prerotate(q, rope_theta=w.rope_theta)
+    kr = af.prerotate(k, rope_theta=w.rope_theta)
+    out = host(af.fwd(qr, kr, v, causal=True))
+    fused = host(af.fwd(q, k, v, causal=True, rope_theta=w.rope_theta))
+    ref, _ = oracle.attention(inp.q, inp.k, inp.v, rope_theta=w.rope_theta, causal=True)
+    check_close(out, ref, "bf16", "pre-rotated path")
+    check_close(fused, ref, "bf16", "fused path")
+    # both paths round Q' and K' to bf16 the same way: they agree closely
+    assert np.max(np.abs(out - fused)) <= 2e-2
+
+
+def test_gqa_matches_repeated_heads():
+    rng = np.random.default_rng(12)
+    (qb, _), (kb, k), (vb, v) = (workloads.normal_bf16(s, rng) for s in
+                                 ((1, 8, 130, 128), (1, 2, 130, 128), (1, 2, 130, 128)))
+    kr = np.repeat(kb.reshape(1, 2, 130, 128), 4, axis=1)
+    vr = np.repeat(vb.reshape(1, 2, 130, 128), 4, axis=1)
+    a = host(af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), causal=True, rope_theta=1e4))
+    b = host(af.fwd(to_dev(qb, "bf16"), to_dev(kr, "bf16"), to_dev(vr, "bf16"), causal=True, rope_theta=1e4))
+    assert np.max(np.abs(a - b)) <= 2e-2
