@@ -119,7 +119,7 @@ typedef struct attnfuse_variant_desc {
    * mask serves every head.  The same mask serves every batch index.  Offsets
    * are clamped to [0, bs_nnz] and columns outside the key range are skipped,
    * so a malformed mask gives wrong numbers but no out-of-bounds access.
-   * bf16: bs_block_m % 32 == 0 and bs_block_n % 64 == 0.
+   * bf16: bs_block_m % 64 == 0 and bs_block_n % 64 == 0.
    * fp32: bs_block_m % 64 == 0 and bs_block_n % 32 == 0.
    * NULL bs_row_ptr = dense.  Supported by attnfuse_fwd only. */
   const int32_t* bs_row_ptr;
