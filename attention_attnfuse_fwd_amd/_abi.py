@@ -8,7 +8,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnfuse.so")
+# ATTNFUSE_LIB may point at another build of the same library (A/B timing of
+# kernel versions); by default the in-tree build next to this file is used.
+LIB_PATH = os.environ.get("ATTNFUSE_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libattnfuse.so")
 
 OK = 0
 ERR_INVALID = -1

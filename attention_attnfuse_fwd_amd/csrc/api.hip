@@ -174,7 +174,7 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   int hp = largest_pow2_divisor(p.G, 8);
   if (use_sparse) {
     if (d->bs_head_stride > 0) hp = 1;  // per-head masks: one head per workgroup
-    // The workgroup's 32 * NW / hp rows must lie inside one CSR block row.
+    // The workgroup's rows must lie inside one CSR block row.
     bool found = false;
     for (int nw = 8; nw >= 2 && !found; nw /= 2) {
       const int h2 = hp < nw ? hp : nw;
@@ -197,15 +197,16 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
   const bool rope = d->rope != 0;
   const bool scoremod = d->alibi_slopes != nullptr || d->bias != nullptr;
+  const unsigned g = (unsigned)grid;
   hipError_t e;
   if (d->D == 128) {
-    if (NW == 8) e = attnfuse::launch_fwd_bf16<128, 8>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
-    else if (NW == 4) e = attnfuse::launch_fwd_bf16<128, 4>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
-    else e = attnfuse::launch_fwd_bf16<128, 2>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+    if (NW == 8) e = attnfuse::launch_fwd_bf16<128, 8>(p, rope, scoremod, use_sparse, g, s);
+    else if (NW == 4) e = attnfuse::launch_fwd_bf16<128, 4>(p, rope, scoremod, use_sparse, g, s);
+    else e = attnfuse::launch_fwd_bf16<128, 2>(p, rope, scoremod, use_sparse, g, s);
   } else {
-    if (NW == 8) e = attnfuse::launch_fwd_bf16<64, 8>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
-    else if (NW == 4) e = attnfuse::launch_fwd_bf16<64, 4>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
-    else e = attnfuse::launch_fwd_bf16<64, 2>(p, rope, scoremod, use_sparse, (unsigned)grid, s);
+    if (NW == 8) e = attnfuse::launch_fwd_bf16<64, 8>(p, rope, scoremod, use_sparse, g, s);
+    else if (NW == 4) e = attnfuse::launch_fwd_bf16<64, 4>(p, rope, scoremod, use_sparse, g, s);
+    else e = attnfuse::launch_fwd_bf16<64, 2>(p, rope, scoremod, use_sparse, g, s);
   }
   return hip_status(e);
 }

@@ -3,5 +3,5 @@
 
 namespace attnfuse {
 template hipError_t launch_fwd_bf16<128, 4>(const AttnParams&, bool, bool, bool, unsigned,
-                                                 hipStream_t);
+                                             hipStream_t);
 }  // namespace attnfuse

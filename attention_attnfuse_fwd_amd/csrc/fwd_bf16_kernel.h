@@ -13,9 +13,14 @@
 // cross-half swap, P^T -> bf16, O^T += V^T P^T.  Tiles that the causal /
 // window band or the CSR block list rules out are never visited ("4.3
 // Block-Sparse Attention": work proportional to the active blocks).
-// The running maximum is only moved when it grows by more than 2^8 (in the
-// exp2 domain); the result is the same exact softmax, and the O^T rescale
-// becomes rare.
+//
+// Two waves share each SIMD.  The MFMA sections run at raised wave priority,
+// so while one wave is in its softmax (vector ALU) the other one's matrix
+// products win the issue slot and the two pipes overlap.  The running
+// maximum is only moved when it grows by more than 2^8 (exp2 domain); the
+// result is the same exact softmax and the O^T rescale becomes rare.  Row
+// sums are accumulated with bf16 dot products of the very P values that feed
+// the P V product, so the normalisation matches the weights used.
 #pragma once
 
 #include "common.h"
@@ -26,24 +31,36 @@ namespace attnfuse {
 template <int D, int NW>
 struct FwdCfg {
   static constexpr int NT = NW * 64;
-  static constexpr int BN = 64;                 // keys per tile
-  static constexpr int KSTR = D + 8;            // K row stride in LDS (elements)
-  static constexpr int VSTR = BN + 8;           // V^T row stride in LDS
+  static constexpr int BN = 64;        // keys per tile
+  static constexpr int KSTR = D + 8;   // K row stride in LDS (elements)
+  static constexpr int VSTR = BN + 8;  // V^T row stride in LDS
   static constexpr int KBUF = BN * KSTR;
   static constexpr int VBUF = D * VSTR;
-  static constexpr int BUF = KBUF + VBUF;       // one ring slot (elements)
+  static constexpr int BUF = KBUF + VBUF;  // one ring slot (elements)
 };
 
-// Offset (within a 64-key tile) of the key held in S^T subtile `st`, register r,
-// by a lane in half lh: 32*st + 8*(r/4) + 4*lh + r%4.  kOff omits the 4*lh term.
+// Offset (within a 64-key tile) of the key held in S^T subtile `st`, register
+// r, by a lane in half lh: 32*st + 8*(r/4) + 4*lh + r%4.  kOff omits 4*lh.
 __device__ __forceinline__ constexpr int kOff(int st, int r) { return 32 * st + 8 * (r / 4) + (r % 4); }
+
+// Maximum of 32 values as a balanced tree (exposes ILP; pairs fold into v_max3).
+__device__ __forceinline__ float tree_max32(const f32x16& a, const f32x16& b) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = fmaxf(a[i], b[i]);
+#pragma unroll
+  for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
+  return t[0];
+}
 
 template <int D, int NW, bool ROPE, bool SCOREMOD, bool SPARSE>
 __global__ void __launch_bounds__(NW * 64)
 fwd_bf16_kernel(const AttnParams p) {
   using C = FwdCfg<D, NW>;
-  constexpr int NKK = D / 16;   // MFMA k-steps over the head dim
-  constexpr int NDT = D / 32;   // 32-row tiles of O^T
+  constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
+  constexpr int NDT = D / 32;  // 32-row tiles of O^T
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * C::BUF];
 
   const int tid = threadIdx.x;
@@ -125,8 +142,9 @@ fwd_bf16_kernel(const AttnParams p) {
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY;  // running max, exp2 domain
-  float l_run = 0.f;        // this lane's partial row sum (half the keys)
+  float m_run = -INFINITY;                 // running max, exp2 domain
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   const float slope2 = (SCOREMOD && p.alibi) ? p.alibi[h] * kLog2e : 0.f;
   const int dpos = p.k_pos0 - p.q_pos0;
@@ -161,6 +179,7 @@ fwd_bf16_kernel(const AttnParams p) {
       f32x16 s[2];
       s[0] = f32x16{};
       s[1] = f32x16{};
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
@@ -169,10 +188,10 @@ fwd_bf16_kernel(const AttnParams p) {
           s[st] = mfma32(a, qf[kk], s[st]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
 
       // Score mods and masks, then the tile maximum.
       const int jd = k0 + 4 * lh - i;  // j - i at register offset 0
-      float mx = -INFINITY;
       if (SCOREMOD) {
         const float tb = (float)(jd + dpos);
         const float* brow = nullptr;
@@ -202,51 +221,48 @@ fwd_bf16_kernel(const AttnParams p) {
             s[st][r] = ok ? s[st][r] : -INFINITY;
           }
       }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
+      float mx = tree_max32(s[0], s[1]);
       mx = fmaxf(mx, partner32(mx));
       if (!SCOREMOD) mx *= p.scale_log2;
 
       // Online softmax with a lazily moved maximum.
       const float m_new = fmaxf(m_run, mx);
-      const bool grow = m_new > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f)) {
         const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
         m_run = m_new;
-        l_run *= alpha;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) l_part[q] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = SCOREMOD ? (s[st][r] - m_use) : __builtin_fmaf(s[st][r], p.scale_log2, -m_use);
-          const float pr = fast_exp2(x);
-          s[st][r] = pr;
-          lsum += pr;
+          s[st][r] = fast_exp2(x);
         }
-      l_run += lsum;
 
-      // P^T as bf16 B operands: 16-key step c takes registers 8*(c%2) .. +7 of subtile c/2.
+      // P^T as bf16 B operands: 16-key step c takes registers 8*(c%2) .. +7 of
+      // subtile c/2; the row sum takes the same bf16 values.
       bf16x8 pf[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int st = c / 2, r0 = 8 * (c % 2);
-        uint4 w;
-        w.x = pack_bf16x2(s[st][r0 + 0], s[st][r0 + 1]);
-        w.y = pack_bf16x2(s[st][r0 + 2], s[st][r0 + 3]);
-        w.z = pack_bf16x2(s[st][r0 + 4], s[st][r0 + 5]);
-        w.w = pack_bf16x2(s[st][r0 + 6], s[st][r0 + 7]);
-        pf[c] = __builtin_bit_cast(bf16x8, w);
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[q] = pack_bf16x2(s[st][r0 + 2 * q], s[st][r0 + 2 * q + 1]);
+          l_part[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]), ones,
+                                                      l_part[q], false);
+        }
+        pf[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       }
       // O^T += V^T P^T
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -254,6 +270,7 @@ fwd_bf16_kernel(const AttnParams p) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (32 * dt + lq) * C::VSTR + 16 * c + 8 * lh);
           o[dt] = mfma32(a, pf[c], o[dt]);
         }
+      __builtin_amdgcn_s_setprio(0);
     }
 
     if (more) stage.store(smem + ((t + 1) & 1) * C::BUF, tid);
@@ -261,6 +278,7 @@ fwd_bf16_kernel(const AttnParams p) {
   }
 
   // ---- epilogue: O = O^T / l, optional lse ----
+  const float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
   const float l_tot = l_run + partner32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (i < p.Nq) {

@@ -2,54 +2,104 @@
 //
 // A tile is BN consecutive keys of one kv-head.  K goes to LDS row-major
 // ([BN][D + 8], rotated when ROPE), V goes transposed ([D][BN + 8], key
-// columns permuted by vcol()).  load() only issues the global loads, so a
-// kernel can call it one tile ahead and hide their latency behind the
-// current tile's MFMA work; store() then rotates and writes LDS.
+// columns permuted by vcol()).  The load*() calls only issue global loads, so
+// a kernel can call them a tile (or two) ahead and hide their latency behind
+// MFMA work; store() then rotates and writes LDS.
 #pragma once
 
 #include "common.h"
 
 namespace attnfuse {
 
+// K part: unit = (key j, 8-wide chunk c of the low half) covering d in
+// [8c, 8c + 8) and its RoPE partner [D/2 + 8c, D/2 + 8c + 8).  Consecutive
+// units walk the chunks of one row (coalesced 16-byte loads); the row order
+// within each block of 16 keys is permuted so that the rows a 16-lane group
+// stores together sit CPR rows apart, which puts their 16-byte chunks on
+// disjoint LDS banks (the row stride is D + 8 elements).
 template <int D, int BN, int NT, bool ROPE>
-struct TileStage {
+struct KStage {
   static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = BN + 8;
-  static constexpr int KBUF = BN * KSTR;
-  static constexpr int KUNITS = BN * (D / 16);       // (key, chunk pair d / d + D/2)
-  static constexpr int KU = (KUNITS + NT - 1) / NT;
-  static constexpr int VUNITS = (BN / 4) * (D / 8);  // (4-key run, 8-wide d chunk)
-  static constexpr int VU = (VUNITS + NT - 1) / NT;
+  static constexpr int CPR = D / 16;                 // chunk pairs per row
+  static constexpr int UNITS = BN * CPR;
+  static constexpr int U = (UNITS + NT - 1) / NT;
+  static constexpr int RPG = 16 / CPR;               // rows per 16-lane group
 
-  uint4 klo[KU], khi[KU];
-  F8 cs[KU], sn[KU];
-  uint4 v[VU][4];
+  __device__ __forceinline__ static int row_of(int unit) {
+    const int jr = unit / CPR;
+    const int jl = jr & 15;
+    return (jr & ~15) | ((jl % RPG) * CPR + jl / RPG);
+  }
 
-  // Keys k0 .. k0+BN-1 (rows past key_end - 1 are clamped to key_end - 1;
-  // they are masked by the caller).
-  __device__ __forceinline__ void load(const AttnParams& p, const __bf16* kb, const __bf16* vb,
-                                       int k0, int key_end, int tid) {
+  uint4 lo[U], hi[U];
+  F8 cs[U], sn[U];
+  int pos[U];
+
+  // Raw K rows k0 .. k0+BN-1 (rows at or past key_end are clamped to key_end - 1).
+  __device__ __forceinline__ void load(const AttnParams& p, const __bf16* kb, int k0, int key_end,
+                                       int tid) {
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int unit = tid + u * NT;
-      if (KUNITS % NT == 0 || unit < KUNITS) {
-        const int j = unit / (D / 16), c = unit % (D / 16);
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int j = row_of(unit), c = unit % CPR;
         const int kj = min(k0 + j, key_end - 1);
         const __bf16* src = kb + (long long)kj * p.ksn + 8 * c;
-        klo[u] = ld16(src);
-        khi[u] = ld16(src + D / 2);
-        if (ROPE) {
-          const long long row = (long long)(p.k_pos0 + kj) * (D / 2) + 8 * c;
-          cs[u] = ld_f8(p.rcos + row);
-          sn[u] = ld_f8(p.rsin + row);
-        }
+        lo[u] = ld16(src);
+        hi[u] = ld16(src + D / 2);
+        pos[u] = p.k_pos0 + kj;
       }
     }
+  }
+  // cos / sin rows for the positions load() recorded.
+  __device__ __forceinline__ void load_tables(const AttnParams& p, int tid) {
+    if (!ROPE) return;
 #pragma unroll
-    for (int u = 0; u < VU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int unit = tid + u * NT;
-      if (VUNITS % NT == 0 || unit < VUNITS) {
-        const int run = unit / (D / 8), dc = unit % (D / 8);
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int c = unit % CPR;
+        const long long row = (long long)pos[u] * (D / 2) + 8 * c;
+        cs[u] = ld_f8(p.rcos + row);
+        sn[u] = ld_f8(p.rsin + row);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* ks, int tid) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int unit = tid + u * NT;
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int j = row_of(unit), c = unit % CPR;
+        uint4 l = lo[u], h = hi[u];
+        if (ROPE) rope_rotate_bf16x8(l, h, cs[u], sn[u]);
+        st16(ks + j * KSTR + 8 * c, l);
+        st16(ks + j * KSTR + D / 2 + 8 * c, h);
+      }
+    }
+  }
+};
+
+// V part: unit = (run of 4 keys, 8-wide d chunk); stored transposed.  Runs
+// vary fastest across lanes, so the 8-byte writes a 16-lane group issues for
+// one d row land side by side in that row (no bank conflicts); each load
+// instruction still reads 64-byte pieces of 16 key rows.
+template <int D, int BN, int NT>
+struct VStage {
+  static constexpr int VSTR = BN + 8;
+  static constexpr int RUNS = BN / 4;
+  static constexpr int UNITS = RUNS * (D / 8);
+  static constexpr int U = (UNITS + NT - 1) / NT;
+
+  uint4 v[U][4];
+
+  __device__ __forceinline__ void load(const AttnParams& p, const __bf16* vb, int k0, int key_end,
+                                       int tid) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int unit = tid + u * NT;
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int run = unit % RUNS, dc = unit / RUNS;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int kj = min(k0 + 4 * run + b, key_end - 1);
@@ -58,29 +108,36 @@ struct TileStage {
       }
     }
   }
-
-  __device__ __forceinline__ void store(__bf16* slot, int tid) {
-    __bf16* ks = slot;
-    __bf16* vs = slot + KBUF;
+  __device__ __forceinline__ void store(__bf16* vs, int tid) {
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int unit = tid + u * NT;
-      if (KUNITS % NT == 0 || unit < KUNITS) {
-        const int j = unit / (D / 16), c = unit % (D / 16);
-        uint4 lo = klo[u], hi = khi[u];
-        if (ROPE) rope_rotate_bf16x8(lo, hi, cs[u], sn[u]);
-        st16(ks + j * KSTR + 8 * c, lo);
-        st16(ks + j * KSTR + D / 2 + 8 * c, hi);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int unit = tid + u * NT;
-      if (VUNITS % NT == 0 || unit < VUNITS) {
-        const int run = unit / (D / 8), dc = unit % (D / 8);
+      if (UNITS % NT == 0 || unit < UNITS) {
+        const int run = unit % RUNS, dc = unit / RUNS;
         store_vt_4x8(vs + (8 * dc) * VSTR + vcol(4 * run), VSTR, v[u]);
       }
     }
+  }
+};
+
+// Both parts for one tile (used where K and V of the same tile move together).
+template <int D, int BN, int NT, bool ROPE>
+struct TileStage {
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = BN + 8;
+  static constexpr int KBUF = BN * KSTR;
+  KStage<D, BN, NT, ROPE> k;
+  VStage<D, BN, NT> v;
+
+  __device__ __forceinline__ void load(const AttnParams& p, const __bf16* kb, const __bf16* vb,
+                                       int k0, int key_end, int tid) {
+    k.load(p, kb, k0, key_end, tid);
+    k.load_tables(p, tid);
+    v.load(p, vb, k0, key_end, tid);
+  }
+  __device__ __forceinline__ void store(__bf16* slot, int tid) {
+    k.store(slot, tid);
+    v.store(slot + KBUF, tid);
   }
 };
 
