@@ -45,8 +45,13 @@ int validate_common(const attnfuse_variant_desc* d) {
   if (d->causal != 0 && d->causal != 1) return ATTNFUSE_ERR_INVALID;
   if (d->window < 0) return ATTNFUSE_ERR_INVALID;
   if (d->rope) {
-    if (!d->rope_cos || !d->rope_sin || !(d->rope_theta > 0.0)) return ATTNFUSE_ERR_INVALID;
-    if (!aligned16(d->rope_cos) || !aligned16(d->rope_sin)) return ATTNFUSE_ERR_INVALID;
+    if (!(d->rope_theta > 0.0)) return ATTNFUSE_ERR_INVALID;
+    if (d->dtype == ATTNFUSE_FP32) {
+      if (!d->rope_cos || !d->rope_sin) return ATTNFUSE_ERR_INVALID;
+      if (!aligned16(d->rope_cos) || !aligned16(d->rope_sin)) return ATTNFUSE_ERR_INVALID;
+    } else {
+      if (!d->rope_cs_f16 || !aligned16(d->rope_cs_f16)) return ATTNFUSE_ERR_INVALID;
+    }
     const int64_t need = (d->q_pos0 + d->Nq > d->k_pos0 + d->Nk) ? d->q_pos0 + d->Nq
                                                                    : d->k_pos0 + d->Nk;
     if (d->rope_table_len < need || d->rope_table_len < 1) return ATTNFUSE_ERR_INVALID;
@@ -86,6 +91,7 @@ AttnParams base_params(const void* q, const void* k, const void* v, void* out,
   p.scale_log2 = (float)(scale * 1.4426950408889634);
   p.rcos = d->rope ? d->rope_cos : nullptr;
   p.rsin = d->rope ? d->rope_sin : nullptr;
+  p.rcs = d->rope ? d->rope_cs_f16 : nullptr;
   p.q_pos0 = (int)d->q_pos0;
   p.k_pos0 = (int)d->k_pos0;
   // Band in position space: lo <= p_k - p_q <= hi; then shifted to index space.
@@ -245,11 +251,11 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
 }
 
 int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, float* sin_out,
-                        void* stream) {
+                        uint32_t* cs_f16_out, void* stream) {
   if (!(theta > 0.0) || !isfinite(theta) || D < 2 || D > 1024 || D % 2 || len < 1 ||
-      len >= kMaxLen || !cos_out || !sin_out)
+      len >= kMaxLen || (!cos_out && !sin_out && !cs_f16_out))
     return ATTNFUSE_ERR_INVALID;
-  return hip_status(attnfuse::launch_rope_table(theta, D, len, cos_out, sin_out,
+  return hip_status(attnfuse::launch_rope_table(theta, D, len, cos_out, sin_out, cs_f16_out,
                                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -267,7 +273,7 @@ int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* 
   const bool vec_ok = aligned16(x) && aligned16(x_rot);
   return hip_status(attnfuse::launch_prerotate(
       x, x_rot, d->dtype == ATTNFUSE_BF16, vec_ok, d->D, d->B, H, N, str[0], str[1], str[2],
-      pos0, d->rope_cos, d->rope_sin, reinterpret_cast<hipStream_t>(stream)));
+      pos0, d->rope_cos, d->rope_sin, d->rope_cs_f16, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -41,8 +41,9 @@ struct AttnParams {
   long long vsb, vsh, vsn;
   long long osb, osh, osn;
   float scale_log2;           // softmax scale times log2(e)
-  const float* rcos;          // RoPE tables [len][D/2] or nullptr
+  const float* rcos;          // fp32 RoPE tables [len][D/2] (fp32 kernels) or nullptr
   const float* rsin;
+  const uint32_t* rcs;        // fp16 (cos, sin) pairs [len][D/2] (bf16 kernels) or nullptr
   int q_pos0, k_pos0;
   // Allowed iff band_lo <= j - i <= band_hi (row/column index space; the
   // position offset k_pos0 - q_pos0 is already folded in).  has_band = 0
@@ -121,6 +122,31 @@ __device__ __forceinline__ void rope_rotate_bf16x8(uint4& lo, uint4& hi, const F
     const float h0 = bf16lo(wh[w]), h1 = bf16hi(wh[w]);
     const float c0 = f8_at(c, 2 * w), c1 = f8_at(c, 2 * w + 1);
     const float s0 = f8_at(s, 2 * w), s1 = f8_at(s, 2 * w + 1);
+    ol[w] = pack_bf16x2(l0 * c0 - h0 * s0, l1 * c1 - h1 * s1);
+    oh[w] = pack_bf16x2(h0 * c0 + l0 * s0, h1 * c1 + l1 * s1);
+  }
+  lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+  hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// NeoX rotation of one (low, high) pair of 8-element bf16 chunks with the
+// angles' (cos, sin) given as fp16 pairs (one 32-bit word per angle, cos in
+// the low half): fp32 math, bf16 result.
+__device__ __forceinline__ void rope_rotate_bf16x8_h(uint4& lo, uint4& hi, const uint4& cs0,
+                                                     const uint4& cs1) {
+  const uint32_t cw[8] = {cs0.x, cs0.y, cs0.z, cs0.w, cs1.x, cs1.y, cs1.z, cs1.w};
+  const uint32_t* wl = reinterpret_cast<const uint32_t*>(&lo);
+  const uint32_t* wh = reinterpret_cast<const uint32_t*>(&hi);
+  uint32_t ol[4], oh[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float l0 = bf16lo(wl[w]), l1 = bf16hi(wl[w]);
+    const float h0 = bf16lo(wh[w]), h1 = bf16hi(wh[w]);
+    const f16x2 a = __builtin_bit_cast(f16x2, cw[2 * w]);
+    const f16x2 b = __builtin_bit_cast(f16x2, cw[2 * w + 1]);
+    const float c0 = (float)a[0], s0 = (float)a[1], c1 = (float)b[0], s1 = (float)b[1];
     ol[w] = pack_bf16x2(l0 * c0 - h0 * s0, l1 * c1 - h1 * s1);
     oh[w] = pack_bf16x2(h0 * c0 + l0 * s0, h1 * c1 + l1 * s1);
   }

@@ -2,15 +2,17 @@
 // online-softmax partial (m, l, acc) per key chunk, phase 2 merges the
 // partials by log-sum-exp.
 //
-// Phase 1: one workgroup (4 waves) per (b, kv-head, group of up to 32 q-heads,
-// chunk).  The q-heads of a kv-head's group are the 32 MFMA columns (GQA:
-// K and V are read once for the whole group; unused columns are padding).
-// The chunk is streamed in 128-key tiles through a double-buffered LDS ring
-// (K rotated once per workgroup on register fragments); wave w takes keys
-// 32w .. 32w+31 of every tile with its own running (m, l, O^T), and the four
-// waves are merged in LDS before the partial is written.  Workgroups are
-// ordered so that the kv-heads of one chunk run on the same XCD, sharing the
-// chunk's RoPE table rows in that XCD's L2.
+// Phase 1 is bound by HBM bandwidth, so it is built to keep many bytes in
+// flight.  One workgroup (4 waves, two workgroups per CU) per (b, kv-head,
+// group of up to 32 q-heads, chunk); the q-heads of the group are the 32 MFMA
+// columns, so K and V are read once for the whole group (GQA).  Each wave
+// streams its own 32-key subtiles of the chunk (subtiles w, w + 4, ...):
+//   global -> registers -> RoPE on the K fragments -> the wave's private LDS
+//   region (K row-major, V transposed) -> MFMA,
+// with the loads of the next subtile in flight while the current one is
+// multiplied, and no workgroup barrier until the four waves' (m, l, O^T) are
+// merged in LDS at the end.  Workgroups are ordered so that the kv-heads of
+// one chunk run on the same XCD and share the chunk's RoPE table rows in L2.
 //
 // Partial layout in the workspace (fp32): for (b, h, chunk), D + 2 floats:
 // acc[0..D-1] (un-normalised), then m (exp2 domain, scaled), then l.
@@ -21,18 +23,19 @@
 namespace attnfuse {
 
 namespace {
-constexpr int kDecTile = 128;  // keys per LDS tile
-constexpr int kDecNT = 256;    // 4 waves
+constexpr int kDecNT = 256;  // 4 waves
+constexpr int kDecSK = 32;   // keys per wave step
 }
 
 template <int D, bool ROPE>
-__global__ void __launch_bounds__(kDecNT) decode_split_kernel(const AttnParams p) {
-  using S = TileStage<D, kDecTile, kDecNT, ROPE>;
-  constexpr int KBUF = S::KBUF;
-  constexpr int VSTR = S::VSTR;
-  constexpr int BUF = KBUF + D * VSTR;
+__global__ void __launch_bounds__(kDecNT, 2) decode_split_kernel(const AttnParams p) {
+  using KS = KStage<D, kDecSK, 64, ROPE>;
+  using VS = VStage<D, kDecSK, 64>;
+  constexpr int KSTR = KS::KSTR;
+  constexpr int VSTR = VS::VSTR;
+  constexpr int WBUF = kDecSK * KSTR + D * VSTR;  // one wave's LDS region (elements)
   constexpr int NKK = D / 16, NDT = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * WBUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 31, lh = lane >> 5;
@@ -46,16 +49,37 @@ __global__ void __launch_bounds__(kDecNT) decode_split_kernel(const AttnParams p
   const int hgrp = u % p.n_hgrp;
   const int kvh = (u / p.n_hgrp) % p.Hkv;
   const int b = u / (p.n_hgrp * p.Hkv);
-  const int g = hgrp * 32 + lq;          // head within the kv group for this column
-  const bool col_valid = g < p.G;
+  const int g = hgrp * 32 + lq;  // head within the kv group for this column
   const int h = kvh * p.G + min(g, p.G - 1);
 
   const int c0 = split * p.chunk;
   const int c1 = min(p.Nk, c0 + p.chunk);
-  const int n_tiles = c1 > c0 ? (c1 - c0 + kDecTile - 1) / kDecTile : 0;
+  const int n_steps = c1 > c0 ? (c1 - c0 + kDecSK - 1) / kDecSK : 0;
 
   const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ksb + kvh * p.ksh;
   const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh;
+  __bf16* const ks = smem + wave * WBUF;
+  __bf16* const vs = ks + kDecSK * KSTR;
+
+  // Wave w takes steps w, w + 4, ... of the chunk, visited from a rotated
+  // starting point: chunk bases are 2^k bytes apart, so without the rotation
+  // every workgroup would address the same HBM channels at the same moment.
+  // (The online softmax does not depend on the key order.)
+  const int rot = n_steps > 0 ? (int)((7u * split + 13u * kvh + 5u * b) % (unsigned)n_steps) : 0;
+  auto step_k0 = [&](int step) {
+    const int s2 = step + rot;
+    return c0 + (s2 >= n_steps ? s2 - n_steps : s2) * kDecSK;
+  };
+
+  // Start streaming before touching the query.
+  KS kst;
+  VS vst;
+  int st = wave;  // this wave's current step
+  if (st < n_steps) {
+    kst.load(p, kb, step_k0(st), c1, lane);
+    kst.load_tables(p, lane);
+    vst.load(p, vb, step_k0(st), c1, lane);
+  }
 
   // Query fragments (one query position; one q-head per column).
   bf16x8 qf[NKK];
@@ -67,8 +91,8 @@ __global__ void __launch_bounds__(kDecNT) decode_split_kernel(const AttnParams p
       uint4 lo = ld16(qrow + d0);
       uint4 hi = ld16(qrow + d0 + D / 2);
       if (ROPE) {
-        const long long row = (long long)p.q_pos0 * (D / 2) + d0;
-        rope_rotate_bf16x8(lo, hi, ld_f8(p.rcos + row), ld_f8(p.rsin + row));
+        const uint32_t* row = p.rcs + (long long)p.q_pos0 * (D / 2) + d0;
+        rope_rotate_bf16x8_h(lo, hi, ld16(row), ld16(row + 4));
       }
       qf[kk] = __builtin_bit_cast(bf16x8, lo);
       qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, hi);
@@ -78,39 +102,40 @@ __global__ void __launch_bounds__(kDecNT) decode_split_kernel(const AttnParams p
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
+  float l_part[2] = {0.f, 0.f};
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const float slope2 = p.alibi ? p.alibi[h] * kLog2e : 0.f;
   const int dpos = p.k_pos0 - p.q_pos0;
 
-  S stage;
-  if (n_tiles > 0) {
-    stage.load(p, kb, vb, c0, c1, tid);
-    stage.store(smem, tid);
-  }
-  __syncthreads();
+  for (; st < n_steps; st += 4) {
+    const int k0 = step_k0(st);
+    // Stage this step into the wave's region, then put the next step in flight.
+    kst.store(ks, lane);
+    vst.store(vs, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (st + 4 < n_steps) {
+      const int kn = step_k0(st + 4);
+      kst.load(p, kb, kn, c1, lane);
+      kst.load_tables(p, lane);
+      vst.load(p, vb, kn, c1, lane);
+    }
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int k0 = c0 + t * kDecTile;
-    const bool more = t + 1 < n_tiles;
-    if (more) stage.load(p, kb, vb, k0 + kDecTile, c1, tid);
-
-    const int kw = k0 + 32 * wave;  // this wave's first key
-    bool skip = kw >= c1;
-    bool need_mask = kw + 32 > c1;
-    if (p.has_band) {  // query row index is 0
-      skip |= (kw + 31 < p.band_lo) || (kw > p.band_hi);
-      need_mask |= (kw < p.band_lo) || (kw + 31 > p.band_hi);
+    bool skip = false, need_mask = k0 + kDecSK > c1;
+    if (p.has_band) {  // the query row index is 0
+      skip = (k0 + kDecSK - 1 < p.band_lo) || (k0 > p.band_hi);
+      need_mask |= (k0 < p.band_lo) || (k0 + kDecSK - 1 > p.band_hi);
     }
     if (!skip) {
-      const __bf16* ks = smem + (t & 1) * BUF;
-      const __bf16* vs = ks + KBUF;
       f32x16 s = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * wave + lq) * S::KSTR + 16 * kk + 8 * lh);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + lq * KSTR + 16 * kk + 8 * lh);
         s = mfma32(a, qf[kk], s);
       }
-      const int jb = kw + 4 * lh;  // key index at register offset 0
+      const int jb = k0 + 4 * lh;  // key index at register offset 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = jb + 8 * (r / 4) + (r % 4);
@@ -123,55 +148,59 @@ __global__ void __launch_bounds__(kDecNT) decode_split_kernel(const AttnParams p
         }
         s[r] = x;
       }
-      float mx = -INFINITY;
+      float t8[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, partner32(mx));
+      for (int r = 0; r < 8; ++r) t8[r] = fmaxf(s[r], s[r + 8]);
+#pragma unroll
+      for (int w = 4; w >= 1; w /= 2)
+#pragma unroll
+        for (int r = 0; r < w; ++r) t8[r] = fmaxf(t8[r], t8[r + w]);
+      const float mx = fmaxf(t8[0], partner32(t8[0]));
       const float m_new = fmaxf(m_run, mx);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f)) {
         const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
         m_run = m_new;
-        l_run *= alpha;
+        l_part[0] *= alpha;
+        l_part[1] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float lsum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = fast_exp2(s[r] - m_use);
-        lsum += s[r];
-      }
-      l_run += lsum;
+      for (int r = 0; r < 16; ++r) s[r] = fast_exp2(s[r] - m_use);
       bf16x8 pf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        uint4 w;
-        w.x = pack_bf16x2(s[8 * c + 0], s[8 * c + 1]);
-        w.y = pack_bf16x2(s[8 * c + 2], s[8 * c + 3]);
-        w.z = pack_bf16x2(s[8 * c + 4], s[8 * c + 5]);
-        w.w = pack_bf16x2(s[8 * c + 6], s[8 * c + 7]);
-        pf[c] = __builtin_bit_cast(bf16x8, w);
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[q] = pack_bf16x2(s[8 * c + 2 * q], s[8 * c + 2 * q + 1]);
+          l_part[q & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]), ones,
+                                                          l_part[q & 1], false);
+        }
+        pf[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (32 * dt + lq) * VSTR + 32 * wave + 16 * c + 8 * lh);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vs + (32 * dt + lq) * VSTR + 16 * c + 8 * lh);
           o[dt] = mfma32(a, pf[c], o[dt]);
         }
     }
-    if (more) stage.store(smem + ((t + 1) & 1) * BUF, tid);
-    __syncthreads();
+    // The next store overwrites this wave's region: every lane is done reading it.
+    __builtin_amdgcn_wave_barrier();
   }
 
-  // Merge the four waves' partials in LDS (the tile ring is free now).
+  // Merge the four waves' partials in LDS.
+  __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
-  float* mw = red;                 // [4][32]
-  float* lw = red + 4 * 32;        // [4][32]
-  float* ow = red + 8 * 32;        // [4][D][32]
+  float* mw = red;           // [4][32]
+  float* lw = red + 4 * 32;  // [4][32]
+  float* ow = red + 8 * 32;  // [4][D][32]
+  const float l_run = l_part[0] + l_part[1];
   const float l_tot = l_run + partner32(l_run);
   if (lh == 0) {
     mw[wave * 32 + lq] = m_run;
@@ -210,33 +239,74 @@ __global__ void __launch_bounds__(kDecNT) decode_split_kernel(const AttnParams p
       dst[D + 1] = L;
     }
   }
-  (void)col_valid;
 }
 
-// Phase 2: one workgroup of D threads per (b, q-head); thread d merges column d.
+// Phase 2: one workgroup of 256 threads per (b, q-head).  Chunks are taken 64
+// at a time; thread (c, g) owns chunk c and the 8-wide d slice g of that group
+// (D / 8 slices), so all of a pass's loads are issued at once.  The merge is a
+// log-sum-exp over the chunk axis: M = max m_c, weights e^(m_c - M), then LDS
+// reductions of the weighted acc and l.
 template <int D>
-__global__ void __launch_bounds__(D) decode_combine_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(256) decode_combine_kernel(const AttnParams p) {
+  constexpr int NG = D / 8;          // 8-wide d slices
+  constexpr int NC = 256 / NG;       // chunks per pass (16 for D = 128, 32 for D = 64)
+  __shared__ float s_l[NC];
+  __shared__ float s_acc[NC][D + 4];
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int c = tid / NG, g = tid % NG;
   const float* base = p.ws + (long long)bh * p.splits * (D + 2);
+
+  // Global maximum of m over all chunks.
   float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, base[s * (D + 2) + D]);
-  float acc = 0.f, L = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < p.splits; ++s) {
-      const float* part = base + s * (D + 2);
+  for (int s = tid; s < p.splits; s += 256) M = fmaxf(M, base[(long long)s * (D + 2) + D]);
+  __shared__ float red[256];
+  red[tid] = M;
+  __syncthreads();
+  for (int w = 128; w >= 1; w /= 2) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  M = red[0];
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int s0 = 0; s0 < p.splits; s0 += NC) {
+    const int s = s0 + c;
+    if (s < p.splits) {
+      const float* part = base + (long long)s * (D + 2);
       const float ms = part[D];
-      if (ms == -INFINITY) continue;
-      const float a = fast_exp2(ms - M);
-      acc += a * part[d];
-      L += a * part[D + 1];
+      const float w = (ms == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(ms - M);
+      // part is 8-byte aligned (D + 2 floats per record): two 8-byte loads per 16 bytes.
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float2 v = *reinterpret_cast<const float2*>(part + 8 * g + e);
+        acc[e] = __builtin_fmaf(w, v.x, acc[e]);
+        acc[e + 1] = __builtin_fmaf(w, v.y, acc[e + 1]);
+      }
+      if (g == 0) L = __builtin_fmaf(w, part[D + 1], L);
     }
   }
+  // Reduce over the NC chunk lanes: acc into s_acc[c][d], L into s_l[c].
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_acc[c][8 * g + e] = acc[e];
+  if (g == 0) s_l[c] = L;
+  __syncthreads();
+  for (int w = NC / 2; w >= 1; w /= 2) {
+    if (c < w) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[c][8 * g + e] += s_acc[c + w][8 * g + e];
+      if (g == 0) s_l[c] += s_l[c + w];
+    }
+    __syncthreads();
+  }
+  const float Lt = s_l[0];
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
   const int b = bh / p.Hq, h = bh % p.Hq;
-  const float val = L > 0.f ? acc / L : 0.f;
   __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh;
-  orow[d] = (__bf16)val;
-  if (p.lse && d == 0) p.lse[bh] = L > 0.f ? (M + __builtin_log2f(L)) * kLn2 : -INFINITY;
+  for (int d = tid; d < D; d += 256) orow[d] = (__bf16)(s_acc[0][d] * inv);
+  if (p.lse && tid == 0) p.lse[bh] = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned grid,
@@ -257,9 +327,9 @@ hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned g
 hipError_t launch_decode_combine(const AttnParams& p, int D, hipStream_t stream) {
   const unsigned grid = (unsigned)(p.B * p.Hq);
   if (D == 64) {
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(grid), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
   } else if (D == 128) {
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(grid), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }

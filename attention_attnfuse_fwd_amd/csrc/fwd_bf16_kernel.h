@@ -131,8 +131,8 @@ fwd_bf16_kernel(const AttnParams p) {
       uint4 lo = ld16(qrow + d0);
       uint4 hi = ld16(qrow + d0 + D / 2);
       if (ROPE) {
-        const long long row = (long long)(p.q_pos0 + iq) * (D / 2) + d0;
-        rope_rotate_bf16x8(lo, hi, ld_f8(p.rcos + row), ld_f8(p.rsin + row));
+        const uint32_t* row = p.rcs + (long long)(p.q_pos0 + iq) * (D / 2) + d0;
+        rope_rotate_bf16x8_h(lo, hi, ld16(row), ld16(row + 4));
       }
       qf[kk] = __builtin_bit_cast(bf16x8, lo);
       qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, hi);

@@ -32,7 +32,7 @@ struct KStage {
   }
 
   uint4 lo[U], hi[U];
-  F8 cs[U], sn[U];
+  uint4 cs[U][2];  // fp16 (cos, sin) pairs for the unit's 8 angles
   int pos[U];
 
   // Raw K rows k0 .. k0+BN-1 (rows at or past key_end are clamped to key_end - 1).
@@ -51,7 +51,7 @@ struct KStage {
       }
     }
   }
-  // cos / sin rows for the positions load() recorded.
+  // (cos, sin) table entries for the positions load() recorded.
   __device__ __forceinline__ void load_tables(const AttnParams& p, int tid) {
     if (!ROPE) return;
 #pragma unroll
@@ -59,9 +59,9 @@ struct KStage {
       const int unit = tid + u * NT;
       if (UNITS % NT == 0 || unit < UNITS) {
         const int c = unit % CPR;
-        const long long row = (long long)pos[u] * (D / 2) + 8 * c;
-        cs[u] = ld_f8(p.rcos + row);
-        sn[u] = ld_f8(p.rsin + row);
+        const uint32_t* row = p.rcs + (long long)pos[u] * (D / 2) + 8 * c;
+        cs[u][0] = ld16(row);
+        cs[u][1] = ld16(row + 4);
       }
     }
   }
@@ -72,7 +72,7 @@ struct KStage {
       if (UNITS % NT == 0 || unit < UNITS) {
         const int j = row_of(unit), c = unit % CPR;
         uint4 l = lo[u], h = hi[u];
-        if (ROPE) rope_rotate_bf16x8(l, h, cs[u], sn[u]);
+        if (ROPE) rope_rotate_bf16x8_h(l, h, cs[u][0], cs[u][1]);
         st16(ks + j * KSTR + 8 * c, l);
         st16(ks + j * KSTR + D / 2 + 8 * c, h);
       }

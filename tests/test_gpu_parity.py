@@ -319,13 +319,20 @@ def test_deterministic_bitwise():
 
 def test_rope_table_matches_fp64():
     D, L, theta = 128, 40000, 5e5
-    cos, sin = af.rope_tables(theta, D, L, "cuda")
+    cos, sin, cs16 = af.rope_tables(theta, D, L, "cuda")
     torch.cuda.synchronize()
     pos = np.array([0, 1, 4095, 32768, 39999])
     r = np.arange(D // 2)
     ang = pos[:, None] * np.power(theta, -2.0 * r / D)[None, :]
     np.testing.assert_allclose(cos.cpu().numpy()[pos], np.cos(ang), rtol=0, atol=1.2e-7)
     np.testing.assert_allclose(sin.cpu().numpy()[pos], np.sin(ang), rtol=0, atol=1.2e-7)
+    # fp16 pairs: cos in the low half, sin in the high half, each within half an fp16 ulp
+    h = cs16.cpu().numpy()[pos].view(np.uint32)
+    c16 = (h & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    s16 = (h >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    np.testing.assert_allclose(c16, np.cos(ang), rtol=0, atol=2.5e-4)
+    np.testing.assert_allclose(s16, np.sin(ang), rtol=0, atol=2.5e-4)
+    assert np.max(np.abs(c16 - np.cos(ang))) > 0  # really fp16-rounded
 
 
 def test_prerotated_path_matches_oracle():
