@@ -46,12 +46,6 @@ int validate_common(const attnfuse_variant_desc* d) {
   if (d->window < 0) return ATTNFUSE_ERR_INVALID;
   if (d->rope) {
     if (!(d->rope_theta > 0.0)) return ATTNFUSE_ERR_INVALID;
-    if (d->dtype == ATTNFUSE_FP32) {
-      if (!d->rope_cos || !d->rope_sin) return ATTNFUSE_ERR_INVALID;
-      if (!aligned16(d->rope_cos) || !aligned16(d->rope_sin)) return ATTNFUSE_ERR_INVALID;
-    } else {
-      if (!d->rope_cs_f16 || !aligned16(d->rope_cs_f16)) return ATTNFUSE_ERR_INVALID;
-    }
     const int64_t need = (d->q_pos0 + d->Nq > d->k_pos0 + d->Nk) ? d->q_pos0 + d->Nq
                                                                    : d->k_pos0 + d->Nk;
     if (d->rope_table_len < need || d->rope_table_len < 1) return ATTNFUSE_ERR_INVALID;
@@ -67,6 +61,15 @@ int validate_common(const attnfuse_variant_desc* d) {
     if (d->bs_head_stride > 0 && d->bs_head_stride < nqb + 1) return ATTNFUSE_ERR_INVALID;
   }
   return ATTNFUSE_OK;
+}
+
+// RoPE tables each entry point reads: fp32 cos / sin for prefill and the
+// pre-rotation pass, fp16 pairs for decode.
+bool fp32_tables_ok(const attnfuse_variant_desc* d) {
+  return !d->rope || (d->rope_cos && d->rope_sin && aligned16(d->rope_cos) && aligned16(d->rope_sin));
+}
+bool f16_table_ok(const attnfuse_variant_desc* d) {
+  return !d->rope || (d->rope_cs_f16 && aligned16(d->rope_cs_f16));
 }
 
 // Fill the kernel parameters that fwd and decode share.
@@ -92,6 +95,7 @@ AttnParams base_params(const void* q, const void* k, const void* v, void* out,
   p.rcos = d->rope ? d->rope_cos : nullptr;
   p.rsin = d->rope ? d->rope_sin : nullptr;
   p.rcs = d->rope ? d->rope_cs_f16 : nullptr;
+  p.rope_len = d->rope ? (int)(d->rope_table_len < kMaxLen ? d->rope_table_len : kMaxLen) : 0;
   p.q_pos0 = (int)d->q_pos0;
   p.k_pos0 = (int)d->k_pos0;
   // Band in position space: lo <= p_k - p_q <= hi; then shifted to index space.
@@ -152,6 +156,7 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   const attnfuse_variant_desc* d = desc;
   // K and V may be NULL only when there are no keys (an empty tensor).
   if (!q || !out || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
+  if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return ATTNFUSE_ERR_UNSUPPORTED;
   const bool sparse = d->bs_row_ptr != nullptr;
@@ -230,6 +235,7 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
   const attnfuse_variant_desc* d = desc;
   if (!q || !k_cache || !v_cache || !out) return ATTNFUSE_ERR_INVALID;
   if (d->Nq != 1 || num_splits < 1 || num_splits > 4096) return ATTNFUSE_ERR_INVALID;
+  if (!f16_table_ok(d)) return ATTNFUSE_ERR_INVALID;
   if (d->dtype != ATTNFUSE_BF16 || d->bias || d->bs_row_ptr) return ATTNFUSE_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return ATTNFUSE_ERR_UNSUPPORTED;
   const size_t need = attnfuse_decode_workspace_size(d, num_splits);
@@ -265,6 +271,7 @@ int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* 
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
   if (!x || !x_rot || !d->rope || (which != 0 && which != 1)) return ATTNFUSE_ERR_INVALID;
+  if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
   const int H = which == 0 ? d->Hq : d->Hkv;
   const int N = which == 0 ? d->Nq : d->Nk;
   const int64_t* str = which == 0 ? d->q_stride : d->k_stride;
@@ -273,7 +280,7 @@ int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* 
   const bool vec_ok = aligned16(x) && aligned16(x_rot);
   return hip_status(attnfuse::launch_prerotate(
       x, x_rot, d->dtype == ATTNFUSE_BF16, vec_ok, d->D, d->B, H, N, str[0], str[1], str[2],
-      pos0, d->rope_cos, d->rope_sin, d->rope_cs_f16, reinterpret_cast<hipStream_t>(stream)));
+      pos0, d->rope_cos, d->rope_sin, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

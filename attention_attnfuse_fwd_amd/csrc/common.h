@@ -43,7 +43,8 @@ struct AttnParams {
   float scale_log2;           // softmax scale times log2(e)
   const float* rcos;          // fp32 RoPE tables [len][D/2] (fp32 kernels) or nullptr
   const float* rsin;
-  const uint32_t* rcs;        // fp16 (cos, sin) pairs [len][D/2] (bf16 kernels) or nullptr
+  const uint32_t* rcs;        // fp16 (cos, sin) pairs [len][D/2] (decode) or nullptr
+  int rope_len;               // rows in the RoPE tables
   int q_pos0, k_pos0;
   // Allowed iff band_lo <= j - i <= band_hi (row/column index space; the
   // position offset k_pos0 - q_pos0 is already folded in).  has_band = 0
@@ -152,6 +153,44 @@ __device__ __forceinline__ void rope_rotate_bf16x8_h(uint4& lo, uint4& hi, const
   }
   lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
   hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+}
+
+// ---- direct global -> LDS staging (gfx950) ----
+
+// Byte offset of a __shared__ object inside the workgroup's LDS allocation.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// Every lane moves 16 bytes from its own global address into LDS at
+// lds_base + 16 * lane (lds_base must be wave-uniform).  The load completes
+// asynchronously and is counted by vmcnt only; the compiler does not track
+// it, so the caller orders it with vmcnt_wait() and barriers.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(g)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Issued through the builtin so
+// the compiler's own wait bookkeeping sees it.
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8-byte blocks that lanes 4e + i / 4 (e = 0..3) address, as
+// its element e.  Pointed at four rows x 32 bytes of a row-major bf16 tile
+// (lane 4a + b at row a, columns 4b .. 4b + 3), lane i gets column i of the
+// four rows.
+__device__ __forceinline__ i16x4 lds_read_tr4(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(size_t)addr);
 }
 
 // Column of key `k` (index within a tile) in the transposed V tile in LDS.

@@ -26,7 +26,6 @@ hipError_t launch_rope_table(double theta, int D, long long len, float* cos_out,
                              uint32_t* cs_out, hipStream_t stream);
 hipError_t launch_prerotate(const void* x, void* x_rot, bool bf16, bool vec_ok, int D, int B,
                             int H, int N, long long sb, long long sh, long long sn, int pos0,
-                            const float* rcos, const float* rsin, const uint32_t* rcs,
-                            hipStream_t stream);
+                            const float* rcos, const float* rsin, hipStream_t stream);
 
 }  // namespace attnfuse

@@ -3,7 +3,7 @@
 //
 //  * rope_table: cos / sin of p * theta^(-2r/D), angle formed in fp64 (an fp32
 //    angle at p ~ 3e4 would carry ~2e-3 rad of error), rounded to fp32 and,
-//    packed as fp16 pairs, for the bf16 kernels.
+//    packed as fp16 pairs, for the decode kernel.
 //  * prerotate: the separate rotation pass that the fused kernel replaces
 //    ("1 Introduction": the pre-rotation workaround costs two extra memory
 //    round trips; "5.3 The Rotation Calculus" weighs the two).  Rotates a
@@ -36,7 +36,7 @@ __global__ void rope_table_kernel(double theta, int D, long long len, float* cos
 template <bool BF16>
 __global__ void prerotate_kernel(const void* x, void* y, int D, int B, int H, int N, long long sb,
                                  long long sh, long long sn, int pos0, const float* rcos,
-                                 const float* rsin, const uint32_t* rcs) {
+                                 const float* rsin) {
   const int h2 = D / 2;
   const long long n = (long long)B * H * N * h2;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
@@ -49,15 +49,7 @@ __global__ void prerotate_kernel(const void* x, void* y, int D, int B, int H, in
     const int bb = (int)(rest / H);
     const long long off = bb * sb + hh * sh + row * sn + r;
     const long long t = (long long)(pos0 + row) * h2 + r;
-    float c, s;
-    if (BF16) {  // bf16 tensors use the fp16 pair table, as the fused bf16 kernels do
-      const f16x2 h = __builtin_bit_cast(f16x2, rcs[t]);
-      c = (float)h[0];
-      s = (float)h[1];
-    } else {
-      c = rcos[t];
-      s = rsin[t];
-    }
+    const float c = rcos[t], s = rsin[t];
     if (BF16) {
       const __bf16* xs = reinterpret_cast<const __bf16*>(x);
       __bf16* ys = reinterpret_cast<__bf16*>(y);
@@ -74,11 +66,11 @@ __global__ void prerotate_kernel(const void* x, void* y, int D, int B, int H, in
   }
 }
 
-// Vectorised bf16 pre-rotation for contiguous rows (16-byte chunks, same fp32
-// math and rounding as the fused kernels' register-fragment rotation).
+// Vectorised bf16 pre-rotation for contiguous rows (16-byte chunks, fp32
+// math, one bf16 rounding per element).
 __global__ void prerotate_bf16x8_kernel(const __bf16* x, __bf16* y, int D, int B, int H, int N,
                                         long long sb, long long sh, long long sn, int pos0,
-                                        const uint32_t* rcs) {
+                                        const float* rcos, const float* rsin) {
   const int chunks = D / 16;  // chunk pairs per row
   const long long n = (long long)B * H * N * chunks;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
@@ -92,7 +84,7 @@ __global__ void prerotate_bf16x8_kernel(const __bf16* x, __bf16* y, int D, int B
     const long long off = bb * sb + hh * sh + row * sn + 8 * c;
     uint4 lo = ld16(x + off), hi = ld16(x + off + D / 2);
     const long long t = (long long)(pos0 + row) * (D / 2) + 8 * c;
-    rope_rotate_bf16x8_h(lo, hi, ld16(rcs + t), ld16(rcs + t + 4));
+    rope_rotate_bf16x8(lo, hi, ld_f8(rcos + t), ld_f8(rsin + t));
     st16(y + off, lo);
     st16(y + off + D / 2, hi);
   }
@@ -109,25 +101,24 @@ hipError_t launch_rope_table(double theta, int D, long long len, float* cos_out,
 
 hipError_t launch_prerotate(const void* x, void* x_rot, bool bf16, bool vec_ok, int D, int B,
                             int H, int N, long long sb, long long sh, long long sn, int pos0,
-                            const float* rcos, const float* rsin, const uint32_t* rcs,
-                            hipStream_t stream) {
+                            const float* rcos, const float* rsin, hipStream_t stream) {
   const long long rows = (long long)B * H * N;
   if (bf16 && vec_ok && D % 16 == 0 && sb % 8 == 0 && sh % 8 == 0 && sn % 8 == 0) {
     const long long n = rows * (D / 16);
     const long long blocks = min((n + 255) / 256, 1LL << 20);
     hipLaunchKernelGGL(prerotate_bf16x8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const __bf16*>(x), reinterpret_cast<__bf16*>(x_rot), D, B,
-                       H, N, sb, sh, sn, pos0, rcs);
+                       H, N, sb, sh, sn, pos0, rcos, rsin);
     return hipGetLastError();
   }
   const long long n = rows * (D / 2);
   const long long blocks = min((n + 255) / 256, 1LL << 20);
   if (bf16)
     hipLaunchKernelGGL(prerotate_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
-                       x_rot, D, B, H, N, sb, sh, sn, pos0, rcos, rsin, rcs);
+                       x_rot, D, B, H, N, sb, sh, sn, pos0, rcos, rsin);
   else
     hipLaunchKernelGGL(prerotate_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x,
-                       x_rot, D, B, H, N, sb, sh, sn, pos0, rcos, rsin, rcs);
+                       x_rot, D, B, H, N, sb, sh, sn, pos0, rcos, rsin);
   return hipGetLastError();
 }
 

@@ -100,14 +100,14 @@ def test_empty_query_is_ok_without_work(lib):
     (dict(window=-3), _abi.ERR_INVALID),
     (dict(q_pos0=-1), _abi.ERR_INVALID),
     (dict(rope=1), _abi.ERR_INVALID),                        # no tables
-    (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=100),
-     _abi.ERR_INVALID),                                      # bf16 needs the fp16 pair table
-    (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_table_len=10),
+    (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_table_len=100),
+     _abi.ERR_INVALID),                                      # prefill reads the fp32 tables
+    (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=10),
      _abi.ERR_INVALID),                                      # table shorter than the positions
-    (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1004, rope_table_len=100),
+    (dict(rope=1, rope_theta=1e4, rope_cos=0x1004, rope_sin=0x2000, rope_table_len=100),
      _abi.ERR_INVALID),                                      # misaligned table
-    (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_table_len=100, dtype=_abi.FP32),
-     _abi.ERR_INVALID),                                      # fp32 needs the fp32 tables
+    (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_table_len=100, dtype=_abi.FP32),
+     _abi.ERR_INVALID),                                      # sin table missing
     (dict(bs_row_ptr=0x1000, bs_block_m=0, bs_block_n=64), _abi.ERR_INVALID),
     (dict(bs_row_ptr=0x1000, bs_block_m=64, bs_block_n=64, bs_nnz=3), _abi.ERR_INVALID),  # no col_idx
     (dict(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=48, bs_block_n=64, bs_nnz=3),
@@ -149,6 +149,9 @@ def test_decode_validation(lib):
     assert call(d, 16, None, ws_need) == _abi.ERR_WORKSPACE
     assert call(_good_desc(Nq=1, bias=0x1000), 16, FAKE, ws_need) == _abi.ERR_UNSUPPORTED
     assert call(_good_desc(Nq=1, dtype=_abi.FP32), 16, FAKE, 10**9) == _abi.ERR_UNSUPPORTED
+    # decode reads the fp16 pair table
+    assert call(_good_desc(Nq=1, rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000,
+                           rope_table_len=100), 16, FAKE, ws_need) == _abi.ERR_INVALID
 
 
 def test_rope_table_and_prerotate_validation(lib):
@@ -158,8 +161,10 @@ def test_rope_table_and_prerotate_validation(lib):
     assert lib.attnfuse_rope_table(1e4, 64, 10, None, None, None, None) == _abi.ERR_INVALID
     d = _good_desc()
     assert lib.attnfuse_prerotate(FAKE, FAKE, ctypes.byref(d), 1, None) == _abi.ERR_INVALID  # rope off
-    d = _good_desc(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_table_len=100)
+    d = _good_desc(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=100)
     assert lib.attnfuse_prerotate(FAKE, FAKE, ctypes.byref(d), 2, None) == _abi.ERR_INVALID
+    d = _good_desc(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_table_len=100)
+    assert lib.attnfuse_prerotate(FAKE, FAKE, ctypes.byref(d), 0, None) == _abi.ERR_INVALID
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
