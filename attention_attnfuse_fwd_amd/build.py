@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -40,12 +41,40 @@ def _sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Kernels that order their direct-to-LDS loads by counting vmcnt: register
+# spills would add scratch stores to that count (stores may retire out of
+# order with loads), so any spill or scratch use in them fails the build.
+NO_SCRATCH_KERNELS = ("fwd_bf16_kernel",)
+
+
+def kernel_resources(remarks: str) -> dict:
+    """Parse clang's kernel-resource-usage remarks: {kernel: {field: int}}."""
+    out, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            out[name] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:]*?): (\d+)", line)
+        if m and name:
+            out[name][m.group(1).strip()] = int(m.group(2))
+    return out
+
+
 def _compile(hipcc: str, src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    for kname, r in kernel_resources(res.stderr).items():
+        if any(k in kname for k in NO_SCRATCH_KERNELS):
+            spill = r.get("VGPRs Spill", 0) + r.get("SGPRs Spill", 0)
+            scratch = r.get("ScratchSize [bytes/lane]", 0)
+            if spill or scratch:
+                raise RuntimeError(f"{kname} in {os.path.basename(src)} spills ({spill} registers, "
+                                   f"{scratch} B scratch per lane); its DMA wait counts assume none")
     return obj
 
 

@@ -16,6 +16,7 @@ using attnfuse::kBandInf;
 namespace {
 
 constexpr long long kMaxLen = 1LL << 30;
+constexpr long long kMaxRowStride = 1LL << 24;  // K / V row stride limit of the bf16 prefill (elements)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -161,6 +162,9 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
     return ATTNFUSE_ERR_UNSUPPORTED;
   const bool sparse = d->bs_row_ptr != nullptr;
   const bool bf16 = d->dtype == ATTNFUSE_BF16;
+  // The bf16 kernel addresses a 64-key tile with 32-bit offsets.
+  if (bf16 && (d->k_stride[2] >= kMaxRowStride || d->v_stride[2] >= kMaxRowStride))
+    return ATTNFUSE_ERR_UNSUPPORTED;
   if (sparse) {
     if (bf16 && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;
     if (!bf16 && (d->bs_block_m % 64 || d->bs_block_n % 32)) return ATTNFUSE_ERR_UNSUPPORTED;
@@ -200,14 +204,18 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
     const int rb_need = (d->Nq + 31) / 32;
     while (NW > 2 && NW > hp && (NW / hp) / 2 >= rb_need) NW /= 2;
   }
+  const bool rope = d->rope != 0;
+  const bool scoremod = d->alibi_slopes != nullptr || d->bias != nullptr;
+  if (!attnfuse::fwd_bf16_supported(d->D, NW, rope, scoremod, use_sparse)) {
+    NW /= 2;  // fewer waves, twice the registers each
+    if (hp > NW) hp = NW;
+  }
   p.hp = hp;
   const int RB = NW / hp;
   p.n_units = d->B * d->Hkv * (p.G / hp);
   p.n_qblk = (d->Nq + 32 * RB - 1) / (32 * RB);
   const long long grid = (long long)p.n_units * p.n_qblk;
   if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
-  const bool rope = d->rope != 0;
-  const bool scoremod = d->alibi_slopes != nullptr || d->bias != nullptr;
   const unsigned g = (unsigned)grid;
   hipError_t e;
   if (d->D == 128) {

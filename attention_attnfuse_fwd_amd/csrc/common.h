@@ -173,6 +173,15 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
                : "memory", "m0");
 }
 
+// Same, with the global address split into a wave-uniform 64-bit base and a
+// per-lane unsigned 32-bit byte offset (one VGPR instead of two).
+__device__ __forceinline__ void dma16_off(uint32_t lds_base, const void* base, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Issued through the builtin so
 // the compiler's own wait bookkeeping sees it.

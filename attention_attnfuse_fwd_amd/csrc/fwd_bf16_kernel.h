@@ -17,10 +17,11 @@
 // Block-Sparse Attention": work proportional to the active blocks).
 //
 // Software pipeline, iteration t (one barrier per iteration):
-//   issue the DMA of K(t+4) and V(t+3), then wait for the group issued two
-//   iterations earlier;  exp / pack / row sums of tile t while the MFMAs of
-//   S(t+1) run;  masks of S(t+1);  score mods and row maximum of S(t+1) and
-//   the RoPE rotation of K(t+2) while the MFMAs of O += V(t) P(t) run.
+//   wait for the DMA group issued two iterations earlier;  the MFMAs of
+//   S(t+1) with the RoPE rotation of K(t+2) between them;  masks of S(t+1);
+//   the MFMAs of O += V(t) P(t) with the exp / pack / row sums of S(t+1)
+//   between them.  The DMA of K(t+4) and V(t+3) is issued one instruction
+//   per step across both phases.
 // The running maximum is only moved when it grows by more than 2^8 (exp2
 // domain); the result is the same exact softmax and the O^T rescale becomes
 // rare.  Row sums are accumulated with bf16 dot products of the very P values
@@ -106,10 +107,10 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr int GRP_HI = (ROPE ? NKW_HI : 0) + 2 * NKW_HI + NVW;
   constexpr int GRP_LO = (ROPE ? NKW_LO : 0) + 2 * NKW_LO + NVW;
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lq = lane & 31, lh = lane >> 5;
 
   // ---- workgroup -> (b, kv-head, head group, query block) ----
@@ -185,6 +186,11 @@ fwd_bf16_kernel(const AttnParams p) {
   const float* const ang_src = ROPE ? ((lane < D / 8 ? rcos : rsin) + 4 * (lane % (D / 8))) : nullptr;
   const int rope_last = p.rope_len - 1, k_pos0 = p.k_pos0;
   const long long ksn = p.ksn, vsn = p.vsn;
+  // Per-lane byte offsets inside a tile (row strides are below 2^24
+  // elements, so 64 rows fit in 32 bits): K low chunk of row r at
+  // r * ksn2 + kcol, V chunk of row r at r * vsn2 + vcol(m).
+  const uint32_t ksn2 = (uint32_t)(2 * ksn), vsn2 = (uint32_t)(2 * vsn);
+  const uint32_t kcol = 16u * (uint32_t)kc;
   // First key of tile u, clamped into the key range.  Tiles past the list
   // reload the last tile, so every wave issues the same number of DMA
   // instructions per iteration (their slots are never read as data).
@@ -194,78 +200,94 @@ fwd_bf16_kernel(const AttnParams p) {
     rmax = Nk - 1 - kc0;
     return kc0;
   };
-  // DMA of K tile u (angle rows first when RoPE) into K / angle slot u % 4.
-  auto issue_k = [&](int u) {
-    int k0, rmax;
-    const int kc0 = tile_base(u, k0, rmax);
-    const __bf16* kt = kb + (long long)kc0 * ksn;
-    const uint32_t slot = lds0 + (uint32_t)(u % RING) * L::KSLOT;
-    if (ROPE) {
-#pragma unroll
-      for (int m = 0; m < NKW_HI; ++m) {
-        const int kp = wave + NW * m;
-        if (m < nkw && lane < D / 4) {
-          // Row of the first key this pair covers; rows past the table only
-          // belong to masked keys.
-          const int pb = min(k_pos0 + k0 + L::KROWS_I * kp, rope_last);
-          dma16(lds0 + L::A_OFF + (uint32_t)((u % RING) * L::NKP + kp) * L::ANG,
-                ang_src + (long long)pb * (D / 2));
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < NKW_HI; ++m) {
-      const int kp = wave + NW * m;
-      if (m < nkw) {
-        const int r = min(L::KROWS_I * kp + kjr, rmax);
-        const __bf16* src = kt + (long long)r * ksn + 8 * kc;
-        dma16(slot + kp * 1024, src);
-        dma16(slot + L::KHI + kp * 1024, src + D / 2);
-      }
-    }
-  };
-  // DMA of V tile u into V slot u % 4.
-  auto issue_v = [&](int u) {
-    int k0, rmax;
-    const int kc0 = tile_base(u, k0, rmax);
-    const __bf16* vt = vb + (long long)kc0 * vsn;
-    const uint32_t slot = lds0 + L::V_OFF + (uint32_t)(u % RING) * L::VSLOT;
-#pragma unroll
-    for (int m = 0; m < NVW; ++m) {
-      const int vi = wave + NW * m;
-      const int key = L::VROWS_I * vi + vrow;
-      const int c = (lane % L::CPR) ^ vswz<D>(key);
-      const int r = min(key, rmax);
-      dma16(slot + vi * 1024, vt + (long long)r * vsn + 8 * c);
-    }
-  };
-  // The group issued at the top of iteration t is {K(t+4), V(t+3)}.  Waiting
-  // until at most two groups are in flight retires the group of iteration
-  // t-2: K(t+2) (rotated this iteration) and V(t+1) (read next iteration).
-  auto wait_groups = [&]() {
+  // Iteration t issues the group {K(t+4) with its angle rows, V(t+3)}, one
+  // instruction at a time between its MFMAs (a burst would stall on the
+  // memory pipe).  At the top of iteration t only the group of t-1 may still
+  // be in flight: waiting for at most one group retires the group of t-2,
+  // i.e. K(t+2) (rotated this iteration) and V(t+1) (read next iteration).
+  const int grp = wave < L::NKP % NW ? GRP_HI : GRP_LO;
+  auto wait_group = [&]() {
     if constexpr (GRP_HI == GRP_LO) {
-      vmcnt_wait<2 * GRP_HI>();
+      vmcnt_wait<GRP_HI>();
     } else {
-      if (nkw == NKW_HI) vmcnt_wait<2 * GRP_HI>();
-      else vmcnt_wait<2 * GRP_LO>();
+      if (nkw == NKW_HI) vmcnt_wait<GRP_HI>();
+      else vmcnt_wait<GRP_LO>();
     }
+  };
+  // Scalar bases of one iteration's group.
+  struct Group {
+    int k0;                  // first key of the K tile (angle rows)
+    const __bf16* kt;        // K tile base (clamped)
+    const __bf16* vt;        // V tile base (clamped)
+    int rmax_k, rmax_v;      // last valid row offsets
+    uint32_t kslot, aslot, vslot;
+  };
+  auto make_group = [&](int uk, int uv) -> Group {
+    Group g;
+    int k0v, rk, rv;
+    const int kck = tile_base(uk, g.k0, rk);
+    const int kcv = tile_base(uv, k0v, rv);
+    g.kt = kb + (long long)kck * ksn;
+    g.vt = vb + (long long)kcv * vsn;
+    g.rmax_k = rk;
+    g.rmax_v = rv;
+    g.kslot = lds0 + (uint32_t)(uk % RING) * L::KSLOT;
+    g.aslot = lds0 + L::A_OFF + (uint32_t)(uk % RING) * L::ASLOT;
+    g.vslot = lds0 + L::V_OFF + (uint32_t)(uv % RING) * L::VSLOT;
+    return g;
+  };
+  // Instruction i of a group, in issue order: angle rows (RoPE, one per K
+  // pair), K low / high per pair, then V.
+  auto dma_item = [&](const Group& g, int i) {
+    const int na = ROPE ? nkw : 0;
+    if (i < na) {
+      const int kp = wave + NW * i;
+      // Row of the first key this pair covers; rows past the table only
+      // belong to masked keys.
+      const int pb = min(k_pos0 + g.k0 + L::KROWS_I * kp, rope_last);
+      if (lane < D / 4) dma16(g.aslot + (uint32_t)kp * L::ANG, ang_src + (long long)pb * (D / 2));
+    } else if (i < na + 2 * nkw) {
+      const int m = (i - na) / 2, hi = (i - na) % 2;
+      const int kp = wave + NW * m;
+      const uint32_t off = (uint32_t)min(L::KROWS_I * kp + kjr, g.rmax_k) * ksn2 + kcol;
+      dma16_off(g.kslot + (hi ? L::KHI : 0) + kp * 1024, hi ? g.kt + D / 2 : g.kt, off);
+    } else {
+      const int vi = wave + NW * (i - na - 2 * nkw);
+      const int key = L::VROWS_I * vi + vrow;
+      const uint32_t c = (uint32_t)((lane % L::CPR) ^ vswz<D>(key));
+      dma16_off(g.vslot + vi * 1024, g.vt, (uint32_t)min(key, g.rmax_v) * vsn2 + 16u * c);
+    }
+  };
+  // A whole group at once (prologue); with_v = false stops after the K part.
+  auto issue_group = [&](int uk, int uv, bool with_v) {
+    const Group g = make_group(uk, uv);
+    const int nk = (ROPE ? nkw : 0) + 2 * nkw;
+#pragma unroll
+    for (int i = 0; i < GRP_HI; ++i)
+      if (i < grp && (with_v || i < nk)) dma_item(g, i);
   };
 
   // ---- RoPE: local angles of this thread's K rows, then in-place rotation ----
   // A K instruction pair covers KROWS_I consecutive keys starting at a row
   // whose angles arrive with the tile; the lane's key sits kjr rows further,
   // so its angle is that row's angle plus kjr * theta_i (angle addition).
-  float lcos[8], lsin[8];
-  if (ROPE) {
+  // The local angles (at most 15 * theta_i) are kept as fp16 (cos, sin)
+  // pairs: their 2^-12 rounding stays well below the bf16 rounding of the
+  // rotated keys, and they cost 8 registers instead of 16.
+  uint32_t lcs[8];
+  auto load_local_angles = [&]() {
+    if (!ROPE) return;
     const int jr = min(kjr, rope_last);
     const F8 c = ld_f8(rcos + (long long)jr * (D / 2) + 8 * kc);
     const F8 s = ld_f8(rsin + (long long)jr * (D / 2) + 8 * kc);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      lcos[e] = f8_at(c, e);
-      lsin[e] = f8_at(s, e);
+      const f16x2 h = {(_Float16)f8_at(c, e), (_Float16)f8_at(s, e)};
+      lcs[e] = __builtin_bit_cast(uint32_t, h);
     }
-  }
+  };
+  auto lcos = [&](int e) -> float { return (float)__builtin_bit_cast(f16x2, lcs[e])[0]; };
+  auto lsin = [&](int e) -> float { return (float)__builtin_bit_cast(f16x2, lcs[e])[1]; };
   auto rotate = [&](int u) {
     char* slot = smem + (u % RING) * L::KSLOT;
 #pragma unroll
@@ -290,8 +312,8 @@ fwd_bf16_kernel(const AttnParams p) {
           for (int x = 0; x < 2; ++x) {
             const int e = 2 * w + x;
             const float cB = f8_at(cb, e), sB = f8_at(sb, e);
-            const float c = cB * lcos[e] - sB * lsin[e];
-            const float s = sB * lcos[e] + cB * lsin[e];
+            const float c = cB * lcos(e) - sB * lsin(e);
+            const float s = sB * lcos(e) + cB * lsin(e);
             rl[x] = l2[x] * c - h2[x] * s;
             rh[x] = h2[x] * c + l2[x] * s;
           }
@@ -333,7 +355,7 @@ fwd_bf16_kernel(const AttnParams p) {
 
   // ---- Q fragments: load, rotate once, keep as bf16 B operands ----
   bf16x8 qf[NKK];
-  {
+  auto load_q = [&]() {
     const __bf16* qrow = qb + (long long)iq * p.qsn;
 #pragma unroll
     for (int kk = 0; kk < NKK / 2; ++kk) {
@@ -347,33 +369,28 @@ fwd_bf16_kernel(const AttnParams p) {
       qf[kk] = __builtin_bit_cast(bf16x8, lo);
       qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, hi);
     }
-  }
+  };
 
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY;                 // running max, exp2 domain
-  float l_part[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums
+  float m_run = -INFINITY;  // running max, exp2 domain
+  float l_run = 0.f;        // this lane's share of the row sum (its half of each tile's keys)
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  const float slope2 = (SCOREMOD && p.alibi) ? p.alibi[h] * kLog2e : 0.f;
+  float slope2 = 0.f;  // ALiBi slope times log2(e), loaded in the prologue
   const int dpos = p.k_pos0 - p.q_pos0;
-
-  // S^T of tile u (raw dot products).
-  auto s_tile = [&](int u, f32x16 (&s)[2]) {
-    const char* ks = smem + (u % RING) * L::KSLOT;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) s[st] = mfma32(k_frag(ks, st, kk), qf[kk], s[st]);
-  };
-  // Masks of tile u in place (only where the tile needs them: the key tail,
-  // or the band edge crossing this wave's rows).
   const float scale_log2 = p.scale_log2;
+  const float* const brow =
+      (SCOREMOD && p.bias) ? p.bias + b * p.bsb + h * p.bsh + (long long)iq * p.bsi : nullptr;
+  const long long bsj = p.bsj;
+
+  // Masks of S^T tile u in place (only where the tile needs them: the key
+  // tail, or the band edge crossing this wave's rows).  A tile past the list
+  // (the last iteration's look-ahead) is masked out entirely.
   auto mask_scores = [&](int u, f32x16 (&s)[2]) {
+    const bool beyond = u >= n_tiles;
     const int k0 = tile_k0(min(u, n_tiles - 1));
-    bool need_mask = k0 + 64 > Nk;
+    bool need_mask = beyond || k0 + 64 > Nk;
     if (has_band) {
       const int dmin = k0 - w_last, dmax = k0 + 63 - w0;
       need_mask |= (dmin < band_lo) | (dmax > band_hi);
@@ -386,6 +403,7 @@ fwd_bf16_kernel(const AttnParams p) {
         lo_off = band_lo - jd;
         hi_off = min(hi_off, band_hi - jd);
       }
+      if (beyond) hi_off = lo_off - 1;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -395,136 +413,263 @@ fwd_bf16_kernel(const AttnParams p) {
         }
     }
   };
-  // Score mods of tile u in place (scaled, exp2 domain), then the row maximum
-  // of this lane's query column over both halves.  Without score mods the
-  // scores stay raw and the maximum is scaled instead.
-  auto mods_max = [&](int u, f32x16 (&s)[2]) -> float {
+
+  // ---- online softmax ("2 Background / FlashAttention and online softmax") ----
+  // A tile is exponentiated against the running maximum it arrives with:
+  // p = 2^(score - m_run).  Its partial row sum (needed anyway) bounds every
+  // p, so one compare tells whether any exceeded 2^15 (or was inf / NaN); only
+  // then, and for the first tile with live keys, the exact path takes the
+  // tile maximum, rescales O and l, and exponentiates again.  Every p is then
+  // at most 2^15 and the result is the same exact softmax.
+  constexpr float kTrig = 32768.f;
+  // Per-lane, per-tile part of the exp2 argument: score mods' lane offset.
+  auto mod_base = [&](int k0) -> float { return SCOREMOD ? slope2 * (float)(k0 + 4 * lh - i + dpos) : 0.f; };
+  // exp2 argument of register r of subtile st: scaled score, score mods,
+  // minus the running maximum (folded into `base`).
+  auto arg = [&](const f32x16 (&s)[2], int st, int r, int k0, float base) -> float {
+    float x = __builtin_fmaf(s[st][r], scale_log2, base);
     if (SCOREMOD) {
-      const int k0 = tile_k0(min(u, n_tiles - 1));
-      const float tb = (float)(k0 + 4 * lh - i + dpos);
-      const float* brow = nullptr;
-      if (p.bias) brow = p.bias + b * p.bsb + h * p.bsh + (long long)iq * p.bsi;
+      x = __builtin_fmaf(slope2, (float)kOff(st, r), x);
+      if (brow) {
+        const int j = min(k0 + 4 * lh + kOff(st, r), Nk - 1);
+        x = __builtin_fmaf(brow[(long long)j * bsj], kLog2e, x);
+      }
+    }
+    return x;
+  };
+  // P pair x: registers r, r+1 of subtile st -> word q of P^T fragment c;
+  // the partial row sum takes the same bf16 values.  The exp2 arguments are
+  // left in s for the exact path.
+  auto exp_pair = [&](f32x16 (&s)[2], int x, int k0, float base, float (&ts)[4]) -> uint32_t {
+    const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
+    s[st][r] = arg(s, st, r, k0, base);
+    s[st][r + 1] = arg(s, st, r + 1, k0, base);
+    const uint32_t w = pack_bf16x2(fast_exp2(s[st][r]), fast_exp2(s[st][r + 1]));
+    ts[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ts[q], false);
+    asm volatile("" ::"v"(w));  // anchor it to this step (no sinking towards its use)
+    return w;
+  };
+  // Check the tile's sums; on the rare exact path re-exponentiate against the
+  // tile maximum (O^T must already hold every earlier tile's product).  s
+  // holds the exp2 arguments relative to m_use.  Adds the tile to l_run.
+  auto finish_tile = [&](f32x16 (&s)[2], float m_use, uint32_t (&pw)[16], float (&ts)[4]) {
+    float tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
+    const bool trig = !(tsum <= kTrig) || (m_run == -INFINITY && tsum > 0.f);
+    if (__builtin_amdgcn_ballot_w64(trig)) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[st][r] * scale_log2;
-          x = __builtin_fmaf(slope2, tb + (float)kOff(st, r), x);
-          if (brow) {
-            const int j = min(k0 + 4 * lh + kOff(st, r), Nk - 1);
-            x = __builtin_fmaf(brow[(long long)j * p.bsj], kLog2e, x);
-          }
-          s[st][r] = x;
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
+      mx = fmaxf(mx, partner32(mx)) + m_use;
+      const float m_new = fmaxf(m_run, mx);
+      float shift = 0.f;
+      if (m_new != -INFINITY) {
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        shift = m_use - m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      tsum = 0.f;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
+        pw[x] = pack_bf16x2(fast_exp2(s[st][r] + shift), fast_exp2(s[st][r + 1] + shift));
+        tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x]), ones, tsum, false);
+      }
     }
-    float mx = tree_max32(s[0], s[1]);
-    mx = fmaxf(mx, partner32(mx));
-    return SCOREMOD ? mx : mx * scale_log2;
+    l_run += tsum;
+  };
+  auto neg_m = [&]() -> float { return (m_run == -INFINITY) ? 0.f : -m_run; };
+  auto to_frags = [](const uint32_t (&pw)[16], bf16x8 (&pf)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      pf[c] = __builtin_bit_cast(bf16x8, make_uint4(pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]));
   };
 
   const int n = n_tiles;
-  f32x16 sc[2];
-  float mx_cur = -INFINITY;
+  bf16x8 pfa[4], pfb[4];  // P^T of the tile the next iteration multiplies with V (ping-pong)
   // Prologue: K(0), K(1) loaded and rotated, V(0) loaded; the groups of
-  // iterations -2 and -1 ({K(2), V(1)}, {K(3), V(2)}) in flight; S(0).
+  // iterations -2 and -1 ({K(2), V(1)}, {K(3), V(2)}) in flight; P(0).
   if (n > 0) {
-    issue_k(0);
-    issue_k(1);
-    issue_v(0);
+    issue_group(0, 0, true);
+    issue_group(1, 1, false);
   }
-  vmcnt_wait<0>();  // also retires the Q / angle / slope loads above
+  // Q, the local angles and the slope load while the first tiles arrive.
+  load_q();
+  load_local_angles();
+  if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
+  vmcnt_wait<0>();
   if (n > 0) {
     if (ROPE) {
       rotate(0);
       rotate(1);
     }
-    issue_k(2);
-    issue_v(1);
-    issue_k(3);
-    issue_v(2);
+    issue_group(2, 1, true);
+    issue_group(3, 2, true);
   }
   __syncthreads();
   if (n > 0) {
-    s_tile(0, sc);
-    mask_scores(0, sc);
-    mx_cur = mods_max(0, sc);
+    f32x16 s0[2];
+    s0[0] = f32x16{};
+    s0[1] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < 2 * NKK; ++k) s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], s0[k & 1]);
+    mask_scores(0, s0);
+    const int k00 = tile_k0(0);
+    uint32_t pw[16];
+    float ts[4] = {0.f, 0.f, 0.f, 0.f};
+    const float base = mod_base(k00) + neg_m();
+#pragma unroll
+    for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00, base, ts);
+    finish_tile(s0, -neg_m(), pw, ts);
+    to_frags(pw, pfa);
   }
   // Iteration 0 refills K slot 0, which every wave has just read for S(0).
   __syncthreads();
 
-  for (int t = 0; t < n; ++t) {
-    issue_k(t + 4);
-    issue_v(t + 3);
-    wait_groups();
+  // ---- main loop: hand-scheduled phases, one MFMA per step ----
+  // Phase A: the MFMAs of S(t+1); between them the RoPE rotation of K(t+2).
+  // Phase B: the MFMAs of O^T += V^T P^T for tile t; between them the
+  // exp / pack / row sums that turn S(t+1) into P(t+1).  Fragments are read
+  // PF steps ahead; sched_barrier keeps each step's instructions together so
+  // the vector work fills the MFMA shadow.
+  constexpr int NSA = 2 * NKK;                     // phase A steps
+  constexpr int NSB = 4 * NDT;                     // phase B steps
+  constexpr int NROT = ROPE ? 8 * NKW_HI : 0;      // rotation items, one angle each
+  constexpr int AIPS = (NROT + NSA - 3) / (NSA - 2);  // per step from step 2 on
+  constexpr int XPB = 16 / NSB;                    // exp pairs per phase B step
+  constexpr int PF = 2;                            // fragment prefetch distance
 
-    // Online softmax of tile t with a lazily moved maximum.
-    const float m_new = fmaxf(m_run, mx_cur);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + 8.0f)) {
-      const float alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
+  // Group instruction slots: every other step of phase A, then of phase B,
+  // IPD instructions per slot.
+  constexpr int DSLOTS = NSA / 2 + NSB / 2;
+  constexpr int IPD = (GRP_HI + DSLOTS - 1) / DSLOTS;
+  auto dma_slot = [&](const Group& g, int slot) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) l_part[q] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    for (int i = slot * IPD; i < (slot + 1) * IPD; ++i)
+      if (i < GRP_HI && i < grp) dma_item(g, i);
+  };
+  auto iteration = [&](int t, const bf16x8 (&pf)[4], bf16x8 (&pf_next)[4]) {
+    wait_group();
+    const Group g = make_group(t + 4, t + 3);
 
-    // S(t+1) on the matrix cores while tile t is exponentiated.
+    // ---- phase A ----
+    const char* ks = smem + ((t + 1) % RING) * L::KSLOT;
     f32x16 sn[2];
-    s_tile(t + 1, sn);
-    bf16x8 pf[4];
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    bf16x8 afr[PF + 1];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int st = c / 2, r0 = 8 * (c % 2);
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float x0 = sc[st][r0 + 2 * q], x1 = sc[st][r0 + 2 * q + 1];
-        const float e0 = SCOREMOD ? (x0 - m_use) : __builtin_fmaf(x0, scale_log2, -m_use);
-        const float e1 = SCOREMOD ? (x1 - m_use) : __builtin_fmaf(x1, scale_log2, -m_use);
-        w[q] = pack_bf16x2(fast_exp2(e0), fast_exp2(e1));
-        l_part[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]), ones, l_part[q], false);
+    for (int k = 0; k < PF; ++k) afr[k] = k_frag(ks, k & 1, k >> 1);
+    // Rotation of K(t+2): pair m, angles e = 0..7 of this lane's chunk, in two
+    // halves of four.  A half's operands (two words of the low chunk, two of
+    // the high chunk, four cos and four sin of the angle row) are read from
+    // LDS two steps before its first item, so at most one and a half halves
+    // are held at a time.
+    char* kslot2 = smem + ((t + 2) % RING) * L::KSLOT;
+    const float* ang2 = reinterpret_cast<const float*>(smem + L::A_OFF + ((t + 2) % RING) * L::NKP * L::ANG);
+    uint2 rlo[NKW_HI][2], rhi[NKW_HI][2];
+    float4 rcb[NKW_HI][2], rsb[NKW_HI][2];
+    uint32_t olw[NKW_HI][4], ohw[NKW_HI][4];
+    float rl_even[NKW_HI], rh_even[NKW_HI];
+    auto rot_load = [&](int m, int hf) {
+      const int kp = wave + NW * m;
+      if (m < nkw) {
+        const float* ang = ang2 + kp * (L::ANG / 4);
+        rcb[m][hf] = *reinterpret_cast<const float4*>(ang + 8 * kc + 4 * hf);
+        rsb[m][hf] = *reinterpret_cast<const float4*>(ang + D / 2 + 8 * kc + 4 * hf);
+        rlo[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + kp * 1024 + lane * 16 + 8 * hf);
+        rhi[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + L::KHI + kp * 1024 + lane * 16 + 8 * hf);
       }
-      pf[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-    }
-    // One K fragment read, one MFMA and six vector instructions at a time.
+    };
+    auto rot_item = [&](int ri) {
+      const int m = ri / 8, e = ri % 8, hf = e / 4, e4 = e % 4;
+      if (m < nkw) {
+        const uint32_t wl = (e4 < 2) ? rlo[m][hf].x : rlo[m][hf].y;
+        const uint32_t wh = (e4 < 2) ? rhi[m][hf].x : rhi[m][hf].y;
+        const float l = (e & 1) ? bf16hi(wl) : bf16lo(wl);
+        const float hv = (e & 1) ? bf16hi(wh) : bf16lo(wh);
+        const float cB = e4 == 0 ? rcb[m][hf].x : e4 == 1 ? rcb[m][hf].y : e4 == 2 ? rcb[m][hf].z : rcb[m][hf].w;
+        const float sB = e4 == 0 ? rsb[m][hf].x : e4 == 1 ? rsb[m][hf].y : e4 == 2 ? rsb[m][hf].z : rsb[m][hf].w;
+        const float cs = cB * lcos(e) - sB * lsin(e);
+        const float sv = sB * lcos(e) + cB * lsin(e);
+        const float rl = l * cs - hv * sv;
+        const float rh = hv * cs + l * sv;
+        if (e & 1) {
+          olw[m][e / 2] = pack_bf16x2(rl_even[m], rl);
+          ohw[m][e / 2] = pack_bf16x2(rh_even[m], rh);
+        } else {
+          rl_even[m] = rl;
+          rh_even[m] = rh;
+        }
+      }
+    };
 #pragma unroll
-    for (int k = 0; k < 2 * NKK; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-    // Keep P(t) formed here, next to the S(t+1) MFMAs, rather than sunk past
-    // the mask branch.
+    for (int k = 0; k < NSA; ++k) {
+      if (k + PF < NSA) afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
+      sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], sn[k & 1]);
+      if (k & 1) dma_slot(g, k / 2);
+      if (ROPE) {
+        // Item ri runs at step 2 + ri / AIPS; its half's operands two steps earlier.
 #pragma unroll
-    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(pf[c]));
+        for (int hh = 0; hh < 2 * NKW_HI; ++hh)
+          if ((4 * hh) / AIPS == k) rot_load(hh / 2, hh % 2);
+        if (k >= 2) {
+#pragma unroll
+          for (int ri = (k - 2) * AIPS; ri < (k - 1) * AIPS; ++ri)
+            if (ri < NROT) rot_item(ri);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ROPE) {
+#pragma unroll
+      for (int m = 0; m < NKW_HI; ++m) {
+        const int kp = wave + NW * m;
+        if (m < nkw) {
+          st16(kslot2 + kp * 1024 + lane * 16, make_uint4(olw[m][0], olw[m][1], olw[m][2], olw[m][3]));
+          st16(kslot2 + L::KHI + kp * 1024 + lane * 16, make_uint4(ohw[m][0], ohw[m][1], ohw[m][2], ohw[m][3]));
+        }
+      }
+    }
     mask_scores(t + 1, sn);
 
-    // O^T += V^T P^T for tile t while the score mods and maximum of S(t+1)
-    // are formed and K(t+2) is rotated.
+    // ---- phase B ----
     const uint32_t vs = lds0 + L::V_OFF + (uint32_t)(t % RING) * L::VSLOT;
+    bf16x8 vfr[PF + 1];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int k = 0; k < PF; ++k) vfr[k] = v_frag(vs, k / NDT, k % NDT);
+    const int k0n = tile_k0(min(t + 1, n - 1));
+    const float base = mod_base(k0n) + neg_m();
+    uint32_t pw[16];
+    float ts[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma32(v_frag(vs, c, dt), pf[c], o[dt]);
-    mx_cur = mods_max(t + 1, sn);
-    if (ROPE) rotate(t + 2);
-    // Two LDS reads, one MFMA and eight vector instructions at a time.
+    for (int k = 0; k < NSB; ++k) {
+      if (k + PF < NSB) vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
+      o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
+      if (k & 1) dma_slot(g, NSA / 2 + k / 2);
 #pragma unroll
-    for (int k = 0; k < 4 * NDT; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      for (int x = k * XPB; x < (k + 1) * XPB; ++x) pw[x] = exp_pair(sn, x, k0n, base, ts);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    finish_tile(sn, -neg_m(), pw, ts);
+    to_frags(pw, pf_next);
     __syncthreads();
-    sc[0] = sn[0];
-    sc[1] = sn[1];
+  };
+  // Unrolled by two so that the P tiles swap roles without copies.
+  int t = 0;
+  for (; t + 1 < n; t += 2) {
+    iteration(t, pfa, pfb);
+    iteration(t + 1, pfb, pfa);
   }
+  if (t < n) iteration(t, pfa, pfb);
 
   // ---- epilogue: O = O^T / l, optional lse ----
-  const float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
   const float l_tot = l_run + partner32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (i < p.Nq) {

@@ -9,11 +9,14 @@ namespace attnfuse {
 template <int D, int NW>
 hipError_t launch_fwd_bf16(const AttnParams& p, bool rope, bool scoremod, bool sparse,
                            unsigned grid, hipStream_t stream) {
-#define ATTNFUSE_CASE(R, S, SP)                                                          \
-  if (rope == R && scoremod == S && sparse == SP) {                                      \
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, R, S, SP>), dim3(grid), dim3(NW * 64), 0, \
-                       stream, p);                                                       \
-    return hipGetLastError();                                                            \
+#define ATTNFUSE_CASE(R, S, SP)                                                            \
+  if (rope == R && scoremod == S && sparse == SP) {                                        \
+    if constexpr (fwd_bf16_supported(D, NW, R, S, SP)) {                                   \
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, R, S, SP>), dim3(grid), dim3(NW * 64), 0, \
+                         stream, p);                                                       \
+      return hipGetLastError();                                                            \
+    }                                                                                      \
+    return hipErrorInvalidValue;                                                           \
   }
   ATTNFUSE_CASE(false, false, false)
   ATTNFUSE_CASE(false, false, true)

@@ -17,6 +17,12 @@ hipError_t launch_fwd_bf16(const AttnParams& p, bool rope, bool scoremod, bool s
 hipError_t launch_fwd_fp32(const AttnParams& p, int D, unsigned grid, hipStream_t stream);
 
 // Split-KV decode phase 1 (partials into p.ws) and phase 2 (LSE merge).
+// Head dim 128 with both RoPE and score mods does not fit two waves per SIMD
+// without spilling; the dispatcher runs it with at most 4 waves.
+constexpr bool fwd_bf16_supported(int D, int NW, bool rope, bool scoremod, bool /*sparse*/) {
+  return !(D == 128 && NW == 8 && rope && scoremod);
+}
+
 hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned grid,
                                hipStream_t stream);
 hipError_t launch_decode_combine(const AttnParams& p, int D, hipStream_t stream);
