@@ -449,6 +449,27 @@ fwd_bf16_kernel(const AttnParams p) {
     asm volatile("" ::"v"(w));  // anchor it to this step (no sinking towards its use)
     return w;
   };
+  // The same work in three stages, so that a pipelined loop can give each
+  // step independent instructions: (1) the exp2 arguments, left in s;
+  // (2) the two exponentials; (3) pack to bf16 and add to the row sum.
+  auto exp_stage1 = [&](f32x16 (&s)[2], int x, int k0, float base) {
+    const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
+    (void)q;
+    s[st][r] = arg(s, st, r, k0, base);
+    s[st][r + 1] = arg(s, st, r + 1, k0, base);
+  };
+  auto exp_stage2 = [&](const f32x16 (&s)[2], int x, float (&e)[2]) {
+    const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
+    (void)q;
+    e[0] = fast_exp2(s[st][r]);
+    e[1] = fast_exp2(s[st][r + 1]);
+  };
+  auto exp_stage3 = [&](int x, const float (&e)[2], float (&ts)[4]) -> uint32_t {
+    const uint32_t w = pack_bf16x2(e[0], e[1]);
+    ts[x % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ts[x % 4], false);
+    asm volatile("" ::"v"(w));  // anchor it to this step (no sinking towards its use)
+    return w;
+  };
   // Check the tile's sums; on the rare exact path re-exponentiate against the
   // tile maximum (O^T must already hold every earlier tile's product).  s
   // holds the exp2 arguments relative to m_use.  Adds the tile to l_run.
@@ -647,16 +668,29 @@ fwd_bf16_kernel(const AttnParams p) {
     const int k0n = tile_k0(min(t + 1, n - 1));
     const float base = mod_base(k0n) + neg_m();
     uint32_t pw[16];
+    float ex[16][2];
     float ts[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
       if (k + PF < NSB) vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
       o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
       if (k & 1) dma_slot(g, NSA / 2 + k / 2);
+      // Pairs of step k: arguments now, exponentials one step later, pack
+      // and row sum two steps later.
 #pragma unroll
-      for (int x = k * XPB; x < (k + 1) * XPB; ++x) pw[x] = exp_pair(sn, x, k0n, base, ts);
+      for (int x = k * XPB; x < (k + 1) * XPB; ++x) exp_stage1(sn, x, k0n, base);
+#pragma unroll
+      for (int x = (k - 1) * XPB; x < k * XPB; ++x)
+        if (x >= 0) exp_stage2(sn, x, ex[x]);
+#pragma unroll
+      for (int x = (k - 2) * XPB; x < (k - 1) * XPB; ++x)
+        if (x >= 0) pw[x] = exp_stage3(x, ex[x], ts);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int x = (NSB - 1) * XPB; x < NSB * XPB; ++x) exp_stage2(sn, x, ex[x]);
+#pragma unroll
+    for (int x = (NSB - 2) * XPB; x < NSB * XPB; ++x) pw[x] = exp_stage3(x, ex[x], ts);
     finish_tile(sn, -neg_m(), pw, ts);
     to_frags(pw, pf_next);
     __syncthreads();
