@@ -241,15 +241,17 @@ __global__ void __launch_bounds__(kDecNT, 2) decode_split_kernel(const AttnParam
   }
 }
 
-// Phase 2: one workgroup of 256 threads per (b, q-head).  Chunks are taken 64
-// at a time; thread (c, g) owns chunk c and the 8-wide d slice g of that group
-// (D / 8 slices), so all of a pass's loads are issued at once.  The merge is a
-// log-sum-exp over the chunk axis: M = max m_c, weights e^(m_c - M), then LDS
-// reductions of the weighted acc and l.
+// Phase 2: one workgroup of 256 threads per (b, q-head), one memory round
+// trip.  Thread (c, g) owns chunks c, c + NC, ... and the 8-wide d slice g
+// (D / 8 slices); it loads all of its (m, l, acc-slice) records at once, then
+// the log-sum-exp merge runs from registers: M = max m_c (LDS max over the
+// chunk lanes), weights 2^(m_c - M), LDS sums of the weighted acc and l.
 template <int D>
 __global__ void __launch_bounds__(256) decode_combine_kernel(const AttnParams p) {
   constexpr int NG = D / 8;          // 8-wide d slices
-  constexpr int NC = 256 / NG;       // chunks per pass (16 for D = 128, 32 for D = 64)
+  constexpr int NC = 256 / NG;       // chunk lanes (16 for D = 128, 32 for D = 64)
+  constexpr int MAXR = 8;            // records per thread held at once (splits <= NC * MAXR)
+  __shared__ float s_m[256];
   __shared__ float s_l[NC];
   __shared__ float s_acc[NC][D + 4];
   const int bh = blockIdx.x;
@@ -257,38 +259,55 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const AttnParams p)
   const int c = tid / NG, g = tid % NG;
   const float* base = p.ws + (long long)bh * p.splits * (D + 2);
 
-  // Global maximum of m over all chunks.
-  float M = -INFINITY;
-  for (int s = tid; s < p.splits; s += 256) M = fmaxf(M, base[(long long)s * (D + 2) + D]);
-  __shared__ float red[256];
-  red[tid] = M;
-  __syncthreads();
-  for (int w = 128; w >= 1; w /= 2) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  M = red[0];
-
+  float M = -INFINITY, L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int s0 = 0; s0 < p.splits; s0 += NC) {
-    const int s = s0 + c;
-    if (s < p.splits) {
-      const float* part = base + (long long)s * (D + 2);
-      const float ms = part[D];
-      const float w = (ms == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(ms - M);
-      // part is 8-byte aligned (D + 2 floats per record): two 8-byte loads per 16 bytes.
+  for (int s0 = 0; s0 < p.splits; s0 += NC * MAXR) {
+    // Load a batch of records (independent loads, one round trip).
+    float mr[MAXR], lr[MAXR];
+    float2 vr[MAXR][4];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float2 v = *reinterpret_cast<const float2*>(part + 8 * g + e);
-        acc[e] = __builtin_fmaf(w, v.x, acc[e]);
-        acc[e + 1] = __builtin_fmaf(w, v.y, acc[e + 1]);
+    for (int k = 0; k < MAXR; ++k) {
+      const int s = s0 + c + NC * k;
+      mr[k] = -INFINITY;
+      lr[k] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vr[k][e] = make_float2(0.f, 0.f);
+      if (s < p.splits) {
+        const float* part = base + (long long)s * (D + 2);
+        mr[k] = part[D];
+        lr[k] = part[D + 1];
+        // part is 8-byte aligned (D + 2 floats per record).
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[k][e] = *reinterpret_cast<const float2*>(part + 8 * g + 2 * e);
       }
-      if (g == 0) L = __builtin_fmaf(w, part[D + 1], L);
+    }
+    // Maximum over this batch and everything before it (all chunk lanes).
+    float mloc = M;
+#pragma unroll
+    for (int k = 0; k < MAXR; ++k) mloc = fmaxf(mloc, mr[k]);
+    s_m[tid] = mloc;
+    __syncthreads();
+    float Mn = -INFINITY;
+    for (int cc = 0; cc < NC; ++cc) Mn = fmaxf(Mn, s_m[cc * NG + g]);
+    __syncthreads();
+    // Rescale what was accumulated against the old maximum, then add the batch.
+    const float a0 = (M == -INFINITY || Mn == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    L *= a0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= a0;
+    M = Mn;
+#pragma unroll
+    for (int k = 0; k < MAXR; ++k) {
+      const float w = (mr[k] == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(mr[k] - M);
+      L = __builtin_fmaf(w, lr[k], L);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = __builtin_fmaf(w, vr[k][e].x, acc[2 * e]);
+        acc[2 * e + 1] = __builtin_fmaf(w, vr[k][e].y, acc[2 * e + 1]);
+      }
     }
   }
-  // Reduce over the NC chunk lanes: acc into s_acc[c][d], L into s_l[c].
-  __syncthreads();
+  // Sum over the NC chunk lanes (every lane holds the same M).
 #pragma unroll
   for (int e = 0; e < 8; ++e) s_acc[c][8 * g + e] = acc[e];
   if (g == 0) s_l[c] = L;
