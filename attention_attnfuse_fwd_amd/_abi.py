@@ -61,6 +61,7 @@ class VariantDesc(ctypes.Structure):
         ("rope_cos", ctypes.c_void_p),
         ("rope_sin", ctypes.c_void_p),
         ("rope_cs_f16", ctypes.c_void_p),
+        ("rope_cs_bf16", ctypes.c_void_p),
         ("rope_table_len", ctypes.c_int64),
         ("q_pos0", ctypes.c_int64),
         ("k_pos0", ctypes.c_int64),
@@ -106,7 +107,7 @@ def load() -> ctypes.CDLL:
     lib.attnfuse_decode_workspace_size.restype = ctypes.c_size_t
     lib.attnfuse_decode.argtypes = [P, P, P, P, D, ctypes.c_int32, P, ctypes.c_size_t, P]
     lib.attnfuse_decode.restype = ctypes.c_int
-    lib.attnfuse_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int64, P, P, P, P]
+    lib.attnfuse_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int64, P, P, P, P, P]
     lib.attnfuse_rope_table.restype = ctypes.c_int
     lib.attnfuse_prerotate.argtypes = [P, P, D, ctypes.c_int32, P]
     lib.attnfuse_prerotate.restype = ctypes.c_int

@@ -64,10 +64,14 @@ int validate_common(const attnfuse_variant_desc* d) {
   return ATTNFUSE_OK;
 }
 
-// RoPE tables each entry point reads: fp32 cos / sin for prefill and the
-// pre-rotation pass, fp16 pairs for decode.
+// RoPE tables each entry point reads: fp32 cos / sin for prefill (Q) and the
+// pre-rotation pass, bf16 pairs for the bf16 prefill (K), fp16 pairs for
+// decode.
 bool fp32_tables_ok(const attnfuse_variant_desc* d) {
   return !d->rope || (d->rope_cos && d->rope_sin && aligned16(d->rope_cos) && aligned16(d->rope_sin));
+}
+bool bf16_table_ok(const attnfuse_variant_desc* d) {
+  return !d->rope || (d->rope_cs_bf16 && aligned16(d->rope_cs_bf16));
 }
 bool f16_table_ok(const attnfuse_variant_desc* d) {
   return !d->rope || (d->rope_cs_f16 && aligned16(d->rope_cs_f16));
@@ -96,6 +100,7 @@ AttnParams base_params(const void* q, const void* k, const void* v, void* out,
   p.rcos = d->rope ? d->rope_cos : nullptr;
   p.rsin = d->rope ? d->rope_sin : nullptr;
   p.rcs = d->rope ? d->rope_cs_f16 : nullptr;
+  p.rcsb = d->rope ? d->rope_cs_bf16 : nullptr;
   p.rope_len = d->rope ? (int)(d->rope_table_len < kMaxLen ? d->rope_table_len : kMaxLen) : 0;
   p.q_pos0 = (int)d->q_pos0;
   p.k_pos0 = (int)d->k_pos0;
@@ -158,6 +163,7 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   // K and V may be NULL only when there are no keys (an empty tensor).
   if (!q || !out || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
   if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
+  if (d->dtype == ATTNFUSE_BF16 && !bf16_table_ok(d)) return ATTNFUSE_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return ATTNFUSE_ERR_UNSUPPORTED;
   const bool sparse = d->bs_row_ptr != nullptr;
@@ -265,12 +271,12 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
 }
 
 int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, float* sin_out,
-                        uint32_t* cs_f16_out, void* stream) {
+                        uint32_t* cs_f16_out, uint32_t* cs_bf16_out, void* stream) {
   if (!(theta > 0.0) || !isfinite(theta) || D < 2 || D > 1024 || D % 2 || len < 1 ||
-      len >= kMaxLen || (!cos_out && !sin_out && !cs_f16_out))
+      len >= kMaxLen || (!cos_out && !sin_out && !cs_f16_out && !cs_bf16_out))
     return ATTNFUSE_ERR_INVALID;
   return hip_status(attnfuse::launch_rope_table(theta, D, len, cos_out, sin_out, cs_f16_out,
-                                                reinterpret_cast<hipStream_t>(stream)));
+                                                cs_bf16_out, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* desc,

@@ -44,6 +44,7 @@ struct AttnParams {
   const float* rcos;          // fp32 RoPE tables [len][D/2] (fp32 kernels) or nullptr
   const float* rsin;
   const uint32_t* rcs;        // fp16 (cos, sin) pairs [len][D/2] (decode) or nullptr
+  const uint32_t* rcsb;       // bf16 (cos, sin) pairs [len][D/2] (bf16 prefill K) or nullptr
   int rope_len;               // rows in the RoPE tables
   int q_pos0, k_pos0;
   // Allowed iff band_lo <= j - i <= band_hi (row/column index space; the
@@ -111,9 +112,11 @@ __device__ __forceinline__ float f8_at(const F8& f, int e) {
   }
 }
 
-// NeoX rotation of one (low, high) pair of 8-element bf16 chunks:
-//   lo' = lo * c - hi * s,  hi' = hi * c + lo * s   (fp32 math, bf16 result)
-__device__ __forceinline__ void rope_rotate_bf16x8(uint4& lo, uint4& hi, const F8& c, const F8& s) {
+// NeoX rotation of one (low, high) pair of 8-element bf16 chunks, times k:
+//   lo' = k (lo * c - hi * s),  hi' = k (hi * c + lo * s)
+// (fp32 math, one bf16 rounding of the result).
+__device__ __forceinline__ void rope_rotate_bf16x8(uint4& lo, uint4& hi, const F8& c, const F8& s,
+                                                   float k = 1.f) {
   const uint32_t* wl = reinterpret_cast<const uint32_t*>(&lo);
   const uint32_t* wh = reinterpret_cast<const uint32_t*>(&hi);
   uint32_t ol[4], oh[4];
@@ -121,10 +124,56 @@ __device__ __forceinline__ void rope_rotate_bf16x8(uint4& lo, uint4& hi, const F
   for (int w = 0; w < 4; ++w) {
     const float l0 = bf16lo(wl[w]), l1 = bf16hi(wl[w]);
     const float h0 = bf16lo(wh[w]), h1 = bf16hi(wh[w]);
-    const float c0 = f8_at(c, 2 * w), c1 = f8_at(c, 2 * w + 1);
-    const float s0 = f8_at(s, 2 * w), s1 = f8_at(s, 2 * w + 1);
+    const float c0 = f8_at(c, 2 * w) * k, c1 = f8_at(c, 2 * w + 1) * k;
+    const float s0 = f8_at(s, 2 * w) * k, s1 = f8_at(s, 2 * w + 1) * k;
     ol[w] = pack_bf16x2(l0 * c0 - h0 * s0, l1 * c1 - h1 * s1);
     oh[w] = pack_bf16x2(h0 * c0 + l0 * s0, h1 * c1 + l1 * s1);
+  }
+  lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+  hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+}
+
+// Eight bf16 values times k (fp32 product, one bf16 rounding).
+__device__ __forceinline__ uint4 scale_bf16x8(const uint4& x, float k) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&x);
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16lo(w[i]) * k, bf16hi(w[i]) * k);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// NeoX rotation of element e (0 or 1) of a bf16 word pair, with the angle
+// given as a bf16 (cos, sin) word t (cos in the low half):
+//   rl = l c - h s,  rh = h c + l s,
+// one bf16 dot product each (exact products, fp32 sum).  wl / wh hold
+// elements (2w, 2w+1) of the low / high half; whn is wh with both sign bits
+// flipped.
+__device__ __forceinline__ void rope_dot2(uint32_t wl, uint32_t wh, uint32_t whn, int e, uint32_t t,
+                                          float& rl, float& rh) {
+  const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+  const uint32_t a = __builtin_amdgcn_perm(whn, wl, sel);  // (l, -h)
+  const uint32_t b = __builtin_amdgcn_perm(wl, wh, sel);   // (h, l)
+  const bf16x2 tb = __builtin_bit_cast(bf16x2, t);
+  rl = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), tb, 0.f, false);
+  rh = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, b), tb, 0.f, false);
+}
+
+// Rotation of one (low, high) pair of 8-element bf16 chunks with bf16
+// (cos, sin) words t0 (elements 0-3) and t1 (elements 4-7).
+__device__ __forceinline__ void rope_rotate_bf16x8_t(uint4& lo, uint4& hi, const uint4& t0,
+                                                     const uint4& t1) {
+  const uint32_t tw[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+  const uint32_t* wl = reinterpret_cast<const uint32_t*>(&lo);
+  const uint32_t* wh = reinterpret_cast<const uint32_t*>(&hi);
+  uint32_t ol[4], oh[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t whn = wh[w] ^ 0x80008000u;
+    float l0, h0, l1, h1;
+    rope_dot2(wl[w], wh[w], whn, 0, tw[2 * w], l0, h0);
+    rope_dot2(wl[w], wh[w], whn, 1, tw[2 * w + 1], l1, h1);
+    ol[w] = pack_bf16x2(l0, l1);
+    oh[w] = pack_bf16x2(h0, h1);
   }
   lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
   hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);

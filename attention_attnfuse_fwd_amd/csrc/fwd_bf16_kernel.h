@@ -7,7 +7,9 @@
 //   global -> LDS by direct DMA, K four and V three tiles ahead (no
 //   registers held) ->
 //   K rotated in place in LDS two tiles ahead ("4.1 Fused RoPE": each key is
-//   rotated once per workgroup, in fp32, by the thread that loaded it) ->
+//   rotated once per workgroup by the thread that loaded it, with two bf16
+//   dot products per element against a precomputed bf16 (cos, sin) table
+//   whose entries the thread fetched into a private LDS slot) ->
 //   MFMA operands (K row fragments; V read transposed by ds_read_b64_tr_b16).
 // Per tile and wave:  S^T = K' Q'^T (bf16 MFMA, fp32 acc), score mods and
 // masks only where the tile needs them, online softmax ("2 Background /
@@ -17,11 +19,12 @@
 // Block-Sparse Attention": work proportional to the active blocks).
 //
 // Software pipeline, iteration t (one barrier per iteration):
-//   wait for the DMA group issued two iterations earlier;  the MFMAs of
-//   S(t+1) with the RoPE rotation of K(t+2) between them;  masks of S(t+1);
-//   the MFMAs of O += V(t) P(t) with the exp / pack / row sums of S(t+1)
-//   between them.  The DMA of K(t+4) and V(t+3) is issued one instruction
-//   per step across both phases.
+//   wait for the DMA group issued two iterations earlier (and the table
+//   entries of the previous one);  the MFMAs of S(t+1) with the RoPE
+//   rotation of K(t+2) between them;  masks of S(t+1);  the MFMAs of
+//   O += V(t) P(t) with the exp / pack / row sums of S(t+1) between them.
+//   The DMA of K(t+4) is issued one instruction per step in the first phase,
+//   the table entries of K(t+3) and V(t+3) in the second.
 // The running maximum is only moved when it grows by more than 2^8 (exp2
 // domain); the result is the same exact softmax and the O^T rescale becomes
 // rare.  Row sums are accumulated with bf16 dot products of the very P values
@@ -33,8 +36,10 @@
 namespace attnfuse {
 
 // LDS layout for head dim D (bytes): a ring of 4 K slots, a ring of 4 V
-// slots and (RoPE) a ring of 4 angle slots.  A K slot holds the tile's RoPE
-// halves, each [64 rows][D/2]; a V slot is [64 rows][D].  Every 16-byte chunk
+// slots and (RoPE) one table slot.  A K slot holds the tile's RoPE halves,
+// each [64 rows][D/2]; a V slot is [64 rows][D]; the table slot holds, per K
+// instruction pair, 2 KiB of bf16 (cos, sin) words: 32 bytes per thread, the
+// 8 angles of the 8-element chunk it rotates, read back only by that thread.  Every 16-byte chunk
 // sits at an XOR-swizzled position inside its row so that the MFMA operand
 // reads are free of bank conflicts; a DMA instruction fills 1 KiB of
 // consecutive LDS, which the swizzle turns into a permutation of the chunks
@@ -52,9 +57,10 @@ struct TileLds {
   static constexpr int CPR = D / 8;         // 16-byte chunks per V row
   static constexpr int VROWS_I = 512 / D;   // V rows per DMA instruction
   static constexpr int NVI = D / 8;         // V instructions per tile
-  static constexpr int ANG = 4 * D;         // one angle row: cos[D/2], sin[D/2] in fp32
-  static constexpr int A_OFF = V_OFF + RING * VSLOT;
-  static constexpr int ASLOT = NKP * ANG;
+  static constexpr int T_OFF = V_OFF + RING * VSLOT;
+  static constexpr int TPAIR = 2048;        // table bytes per K instruction pair
+  static constexpr int TSLOT = NKP * TPAIR;
+  static constexpr int ROWB = 2 * D;        // bytes per table row (D/2 words)
 };
 
 // Swizzle of K half row j: rows that a 16-lane MFMA operand read touches
@@ -96,7 +102,7 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NDT = D / 32;  // 32-row tiles of O^T
   constexpr int RING = L::RING;
-  constexpr int LDS_BYTES = L::A_OFF + (ROPE ? RING * L::ASLOT : 0);
+  constexpr int LDS_BYTES = L::T_OFF + (ROPE ? L::TSLOT : 0);
   // DMA instructions per wave and tile.  V is spread evenly; K pairs may not
   // be (D = 64 with 8 waves: waves 0..3 take one pair each).
   static_assert(L::NVI % NW == 0, "V instructions must spread evenly over the waves");
@@ -104,8 +110,7 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr int NVW = L::NVI / NW;
   constexpr int NKW_HI = (L::NKP + NW - 1) / NW;
   constexpr int NKW_LO = L::NKP / NW;
-  constexpr int GRP_HI = (ROPE ? NKW_HI : 0) + 2 * NKW_HI + NVW;
-  constexpr int GRP_LO = (ROPE ? NKW_LO : 0) + 2 * NKW_LO + NVW;
+  constexpr int TPK = ROPE ? 2 : 0;  // table instructions per K pair
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -180,11 +185,11 @@ fwd_bf16_kernel(const AttnParams p) {
   const int kc = (lane % L::CPH) ^ kswz<D>(L::KROWS_I * wave + kjr);
   const int vrow = lane / L::CPR;
 
-  // Angle-row source of this lane: lanes 0 .. D/8-1 fetch cos, the next D/8 sin.
   const float* const rcos = p.rcos;
   const float* const rsin = p.rsin;
-  const float* const ang_src = ROPE ? ((lane < D / 8 ? rcos : rsin) + 4 * (lane % (D / 8))) : nullptr;
   const int rope_last = p.rope_len - 1, k_pos0 = p.k_pos0;
+  // Byte offset of this lane's first table word inside its row.
+  const uint32_t tcol = 32u * (uint32_t)kc;
   const long long ksn = p.ksn, vsn = p.vsn;
   // Per-lane byte offsets inside a tile (row strides are below 2^24
   // elements, so 64 rows fit in 32 bits): K low chunk of row r at
@@ -200,128 +205,105 @@ fwd_bf16_kernel(const AttnParams p) {
     rmax = Nk - 1 - kc0;
     return kc0;
   };
-  // Iteration t issues the group {K(t+4) with its angle rows, V(t+3)}, one
-  // instruction at a time between its MFMAs (a burst would stall on the
-  // memory pipe).  At the top of iteration t only the group of t-1 may still
-  // be in flight: waiting for at most one group retires the group of t-2,
-  // i.e. K(t+2) (rotated this iteration) and V(t+1) (read next iteration).
-  const int grp = wave < L::NKP % NW ? GRP_HI : GRP_LO;
+  // Iteration t issues the group {K(t+4); table entries of K(t+3), V(t+3)},
+  // one instruction at a time between its MFMAs (a burst would stall on the
+  // memory pipe): K in the first phase, the rest in the second, after the
+  // rotation of that iteration has read the table slot.  At the top of
+  // iteration t only the V part of the group of t-1 may still be in flight
+  // (vmcnt retires in issue order): that retires the group of t-2, i.e.
+  // K(t+2) (rotated this iteration) and V(t+1) (read next iteration), and
+  // the table entries of K(t+2).  Without RoPE the whole group of t-1 may be
+  // in flight.
+  const int grp = (2 + TPK) * nkw + NVW;  // instructions per group (this wave)
   auto wait_group = [&]() {
-    if constexpr (GRP_HI == GRP_LO) {
-      vmcnt_wait<GRP_HI>();
+    if constexpr (ROPE) {
+      vmcnt_wait<NVW>();
+    } else if constexpr (NKW_HI == NKW_LO) {
+      vmcnt_wait<2 * NKW_HI + NVW>();
     } else {
-      if (nkw == NKW_HI) vmcnt_wait<GRP_HI>();
-      else vmcnt_wait<GRP_LO>();
+      if (nkw == NKW_HI) vmcnt_wait<2 * NKW_HI + NVW>();
+      else vmcnt_wait<2 * NKW_LO + NVW>();
     }
   };
   // Scalar bases of one iteration's group.
   struct Group {
-    int k0;                  // first key of the K tile (angle rows)
+    int k0t;                 // first key of the tile whose table entries are fetched
     const __bf16* kt;        // K tile base (clamped)
     const __bf16* vt;        // V tile base (clamped)
     int rmax_k, rmax_v;      // last valid row offsets
-    uint32_t kslot, aslot, vslot;
+    uint32_t kslot, vslot;
   };
   auto make_group = [&](int uk, int uv) -> Group {
     Group g;
-    int k0v, rk, rv;
-    const int kck = tile_base(uk, g.k0, rk);
-    const int kcv = tile_base(uv, k0v, rv);
+    int k0k, rk, rv;
+    const int kck = tile_base(uk, k0k, rk);
+    const int kcv = tile_base(uv, g.k0t, rv);
     g.kt = kb + (long long)kck * ksn;
     g.vt = vb + (long long)kcv * vsn;
     g.rmax_k = rk;
     g.rmax_v = rv;
     g.kslot = lds0 + (uint32_t)(uk % RING) * L::KSLOT;
-    g.aslot = lds0 + L::A_OFF + (uint32_t)(uk % RING) * L::ASLOT;
     g.vslot = lds0 + L::V_OFF + (uint32_t)(uv % RING) * L::VSLOT;
     return g;
   };
-  // Instruction i of a group, in issue order: angle rows (RoPE, one per K
-  // pair), K low / high per pair, then V.
+  // Instruction i of a group, in issue order: K low / high per pair, then
+  // (RoPE) two table instructions per pair, then V.
+  const uint32_t tslot = lds0 + L::T_OFF;
   auto dma_item = [&](const Group& g, int i) {
-    const int na = ROPE ? nkw : 0;
-    if (i < na) {
-      const int kp = wave + NW * i;
-      // Row of the first key this pair covers; rows past the table only
-      // belong to masked keys.
-      const int pb = min(k_pos0 + g.k0 + L::KROWS_I * kp, rope_last);
-      if (lane < D / 4) dma16(g.aslot + (uint32_t)kp * L::ANG, ang_src + (long long)pb * (D / 2));
-    } else if (i < na + 2 * nkw) {
-      const int m = (i - na) / 2, hi = (i - na) % 2;
+    if (i < 2 * nkw) {
+      const int m = i / 2, hi = i % 2;
       const int kp = wave + NW * m;
       const uint32_t off = (uint32_t)min(L::KROWS_I * kp + kjr, g.rmax_k) * ksn2 + kcol;
       dma16_off(g.kslot + (hi ? L::KHI : 0) + kp * 1024, hi ? g.kt + D / 2 : g.kt, off);
+    } else if (i < (2 + TPK) * nkw) {
+      const int m = (i - 2 * nkw) / 2, x = (i - 2 * nkw) % 2;
+      const int kp = wave + NW * m;
+      // The pair covers KROWS_I keys from position prow; rows past the
+      // table only belong to masked keys and re-read its last row.
+      const int prow = k_pos0 + g.k0t + L::KROWS_I * kp;
+      const int row0 = min(prow, rope_last);
+      const uint32_t r = (uint32_t)min(kjr, rope_last - row0);
+      dma16_off(tslot + (uint32_t)kp * L::TPAIR + 1024u * x, p.rcsb + (long long)row0 * (D / 2),
+                r * (uint32_t)L::ROWB + tcol + 16u * x);
     } else {
-      const int vi = wave + NW * (i - na - 2 * nkw);
+      const int vi = wave + NW * (i - (2 + TPK) * nkw);
       const int key = L::VROWS_I * vi + vrow;
       const uint32_t c = (uint32_t)((lane % L::CPR) ^ vswz<D>(key));
       dma16_off(g.vslot + vi * 1024, g.vt, (uint32_t)min(key, g.rmax_v) * vsn2 + 16u * c);
     }
   };
-  // A whole group at once (prologue); with_v = false stops after the K part.
-  auto issue_group = [&](int uk, int uv, bool with_v) {
+  // A whole group at once (prologue); with_v = false issues the K part only,
+  // with_t = false skips the table part.
+  constexpr int GRP_MAX = (2 + TPK) * NKW_HI + NVW;
+  auto issue_group = [&](int uk, int uv, bool with_t, bool with_v) {
     const Group g = make_group(uk, uv);
-    const int nk = (ROPE ? nkw : 0) + 2 * nkw;
 #pragma unroll
-    for (int i = 0; i < GRP_HI; ++i)
-      if (i < grp && (with_v || i < nk)) dma_item(g, i);
-  };
-
-  // ---- RoPE: local angles of this thread's K rows, then in-place rotation ----
-  // A K instruction pair covers KROWS_I consecutive keys starting at a row
-  // whose angles arrive with the tile; the lane's key sits kjr rows further,
-  // so its angle is that row's angle plus kjr * theta_i (angle addition).
-  // The local angles (at most 15 * theta_i) are kept as fp16 (cos, sin)
-  // pairs: their 2^-12 rounding stays well below the bf16 rounding of the
-  // rotated keys, and they cost 8 registers instead of 16.
-  uint32_t lcs[8];
-  auto load_local_angles = [&]() {
-    if (!ROPE) return;
-    const int jr = min(kjr, rope_last);
-    const F8 c = ld_f8(rcos + (long long)jr * (D / 2) + 8 * kc);
-    const F8 s = ld_f8(rsin + (long long)jr * (D / 2) + 8 * kc);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const f16x2 h = {(_Float16)f8_at(c, e), (_Float16)f8_at(s, e)};
-      lcs[e] = __builtin_bit_cast(uint32_t, h);
+    for (int i = 0; i < GRP_MAX; ++i) {
+      const bool is_t = i >= 2 * nkw && i < (2 + TPK) * nkw;
+      const bool is_v = i >= (2 + TPK) * nkw;
+      if (i < grp && (with_t || !is_t) && (with_v || !is_v)) dma_item(g, i);
     }
   };
-  auto lcos = [&](int e) -> float { return (float)__builtin_bit_cast(f16x2, lcs[e])[0]; };
-  auto lsin = [&](int e) -> float { return (float)__builtin_bit_cast(f16x2, lcs[e])[1]; };
-  auto rotate = [&](int u) {
+
+  // ---- RoPE of K in place: prologue tiles ----
+  // Tiles 0 and 1 are rotated before the loop with table words read straight
+  // from global memory; the loop rotates later tiles from the table slot.
+  auto rotate_direct = [&](int u) {
     char* slot = smem + (u % RING) * L::KSLOT;
+    const int k0u = tile_k0(min(u, n_tiles - 1));
 #pragma unroll
     for (int m = 0; m < NKW_HI; ++m) {
       const int kp = wave + NW * m;
       if (m < nkw) {
-        const float* ang = reinterpret_cast<const float*>(smem + L::A_OFF + ((u % RING) * L::NKP + kp) * L::ANG);
-        const F8 cb = ld_f8(ang + 8 * kc);
-        const F8 sb = ld_f8(ang + D / 2 + 8 * kc);
+        const int row = min(k_pos0 + k0u + L::KROWS_I * kp + kjr, rope_last);
+        const uint32_t* tr = p.rcsb + (long long)row * (D / 2) + 8 * kc;
+        const uint4 t0 = ld16(tr), t1 = ld16(tr + 4);
         char* lo_p = slot + kp * 1024 + lane * 16;
         char* hi_p = lo_p + L::KHI;
-        const uint4 lo = ld16(lo_p), hi = ld16(hi_p);
-        const uint32_t* wl = reinterpret_cast<const uint32_t*>(&lo);
-        const uint32_t* wh = reinterpret_cast<const uint32_t*>(&hi);
-        uint32_t ol[4], oh[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float l2[2] = {bf16lo(wl[w]), bf16hi(wl[w])};
-          float h2[2] = {bf16lo(wh[w]), bf16hi(wh[w])};
-          float rl[2], rh[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int e = 2 * w + x;
-            const float cB = f8_at(cb, e), sB = f8_at(sb, e);
-            const float c = cB * lcos(e) - sB * lsin(e);
-            const float s = sB * lcos(e) + cB * lsin(e);
-            rl[x] = l2[x] * c - h2[x] * s;
-            rh[x] = h2[x] * c + l2[x] * s;
-          }
-          ol[w] = pack_bf16x2(rl[0], rl[1]);
-          oh[w] = pack_bf16x2(rh[0], rh[1]);
-        }
-        st16(lo_p, make_uint4(ol[0], ol[1], ol[2], ol[3]));
-        st16(hi_p, make_uint4(oh[0], oh[1], oh[2], oh[3]));
+        uint4 lo = ld16(lo_p), hi = ld16(hi_p);
+        rope_rotate_bf16x8_t(lo, hi, t0, t1);
+        st16(lo_p, lo);
+        st16(hi_p, hi);
       }
     }
   };
@@ -354,9 +336,13 @@ fwd_bf16_kernel(const AttnParams p) {
   };
 
   // ---- Q fragments: load, rotate once, keep as bf16 B operands ----
+  // The softmax scale (times log2 e, for exp2) is applied here, in fp32,
+  // before the single bf16 rounding of the rotated row, so the score MFMAs
+  // produce exp2-domain scores directly.
   bf16x8 qf[NKK];
   auto load_q = [&]() {
     const __bf16* qrow = qb + (long long)iq * p.qsn;
+    const float qscale = p.scale_log2;
 #pragma unroll
     for (int kk = 0; kk < NKK / 2; ++kk) {
       const int d0 = 16 * kk + 8 * lh;
@@ -364,7 +350,10 @@ fwd_bf16_kernel(const AttnParams p) {
       uint4 hi = ld16(qrow + d0 + D / 2);
       if (ROPE) {
         const long long row = (long long)(p.q_pos0 + iq) * (D / 2) + d0;
-        rope_rotate_bf16x8(lo, hi, ld_f8(rcos + row), ld_f8(rsin + row));
+        rope_rotate_bf16x8(lo, hi, ld_f8(rcos + row), ld_f8(rsin + row), qscale);
+      } else {
+        lo = scale_bf16x8(lo, qscale);
+        hi = scale_bf16x8(hi, qscale);
       }
       qf[kk] = __builtin_bit_cast(bf16x8, lo);
       qf[kk + NKK / 2] = __builtin_bit_cast(bf16x8, hi);
@@ -379,7 +368,6 @@ fwd_bf16_kernel(const AttnParams p) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float slope2 = 0.f;  // ALiBi slope times log2(e), loaded in the prologue
   const int dpos = p.k_pos0 - p.q_pos0;
-  const float scale_log2 = p.scale_log2;
   const float* const brow =
       (SCOREMOD && p.bias) ? p.bias + b * p.bsb + h * p.bsh + (long long)iq * p.bsi : nullptr;
   const long long bsj = p.bsj;
@@ -422,14 +410,20 @@ fwd_bf16_kernel(const AttnParams p) {
   // tile maximum, rescales O and l, and exponentiates again.  Every p is then
   // at most 2^15 and the result is the same exact softmax.
   constexpr float kTrig = 32768.f;
+  auto neg_m = [&]() -> float { return (m_run == -INFINITY) ? 0.f : -m_run; };
   // Per-lane, per-tile part of the exp2 argument: score mods' lane offset.
   auto mod_base = [&](int k0) -> float { return SCOREMOD ? slope2 * (float)(k0 + 4 * lh - i + dpos) : 0.f; };
-  // exp2 argument of register r of subtile st: scaled score, score mods,
-  // minus the running maximum (folded into `base`).
-  auto arg = [&](const f32x16 (&s)[2], int st, int r, int k0, float base) -> float {
-    float x = __builtin_fmaf(s[st][r], scale_log2, base);
+  // The first score MFMA of every tile takes its C operand from minit, a
+  // splat of minus the running maximum (updated only when the maximum
+  // moves), so the MFMAs leave the exp2 argument itself: the scale is folded
+  // into Q and no per-tile initialisation is needed.
+  f32x16 minit = f32x16{};
+  // exp2 argument of register r of subtile st: the accumulator plus, with
+  // score mods, the lane's offset, the register's ALiBi step and the bias.
+  auto arg = [&](const f32x16 (&s)[2], int st, int r, int k0) -> float {
+    float x = s[st][r];
     if (SCOREMOD) {
-      x = __builtin_fmaf(slope2, (float)kOff(st, r), x);
+      x += __builtin_fmaf(slope2, (float)kOff(st, r), mod_base(k0));
       if (brow) {
         const int j = min(k0 + 4 * lh + kOff(st, r), Nk - 1);
         x = __builtin_fmaf(brow[(long long)j * bsj], kLog2e, x);
@@ -440,10 +434,10 @@ fwd_bf16_kernel(const AttnParams p) {
   // P pair x: registers r, r+1 of subtile st -> word q of P^T fragment c;
   // the partial row sum takes the same bf16 values.  The exp2 arguments are
   // left in s for the exact path.
-  auto exp_pair = [&](f32x16 (&s)[2], int x, int k0, float base, float (&ts)[4]) -> uint32_t {
+  auto exp_pair = [&](f32x16 (&s)[2], int x, int k0, float (&ts)[4]) -> uint32_t {
     const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
-    s[st][r] = arg(s, st, r, k0, base);
-    s[st][r + 1] = arg(s, st, r + 1, k0, base);
+    s[st][r] = arg(s, st, r, k0);
+    s[st][r + 1] = arg(s, st, r + 1, k0);
     const uint32_t w = pack_bf16x2(fast_exp2(s[st][r]), fast_exp2(s[st][r + 1]));
     ts[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ts[q], false);
     asm volatile("" ::"v"(w));  // anchor it to this step (no sinking towards its use)
@@ -452,11 +446,12 @@ fwd_bf16_kernel(const AttnParams p) {
   // The same work in three stages, so that a pipelined loop can give each
   // step independent instructions: (1) the exp2 arguments, left in s;
   // (2) the two exponentials; (3) pack to bf16 and add to the row sum.
-  auto exp_stage1 = [&](f32x16 (&s)[2], int x, int k0, float base) {
+  auto exp_stage1 = [&](f32x16 (&s)[2], int x, int k0) {
+    if (!SCOREMOD) return;
     const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
     (void)q;
-    s[st][r] = arg(s, st, r, k0, base);
-    s[st][r + 1] = arg(s, st, r + 1, k0, base);
+    s[st][r] = arg(s, st, r, k0);
+    s[st][r + 1] = arg(s, st, r + 1, k0);
   };
   auto exp_stage2 = [&](const f32x16 (&s)[2], int x, float (&e)[2]) {
     const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
@@ -488,6 +483,7 @@ fwd_bf16_kernel(const AttnParams p) {
       if (m_new != -INFINITY) {
         const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
         m_run = m_new;
+        minit = f32x16{} - m_new;
         shift = m_use - m_new;
         l_run *= alpha;
 #pragma unroll
@@ -505,7 +501,6 @@ fwd_bf16_kernel(const AttnParams p) {
     }
     l_run += tsum;
   };
-  auto neg_m = [&]() -> float { return (m_run == -INFINITY) ? 0.f : -m_run; };
   auto to_frags = [](const uint32_t (&pw)[16], bf16x8 (&pf)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -517,36 +512,34 @@ fwd_bf16_kernel(const AttnParams p) {
   // Prologue: K(0), K(1) loaded and rotated, V(0) loaded; the groups of
   // iterations -2 and -1 ({K(2), V(1)}, {K(3), V(2)}) in flight; P(0).
   if (n > 0) {
-    issue_group(0, 0, true);
-    issue_group(1, 1, false);
+    issue_group(0, 0, false, true);
+    issue_group(1, 1, false, false);
   }
-  // Q, the local angles and the slope load while the first tiles arrive.
+  // Q and the slope load while the first tiles arrive.
   load_q();
-  load_local_angles();
   if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
   vmcnt_wait<0>();
   if (n > 0) {
     if (ROPE) {
-      rotate(0);
-      rotate(1);
+      rotate_direct(0);
+      rotate_direct(1);
     }
-    issue_group(2, 1, true);
-    issue_group(3, 2, true);
+    // Groups of iterations -2 and -1: {K(2), V(1)}, {K(3), table of K(2), V(2)}.
+    issue_group(2, 1, false, true);
+    issue_group(3, 2, true, true);
   }
   __syncthreads();
   if (n > 0) {
-    f32x16 s0[2];
-    s0[0] = f32x16{};
-    s0[1] = f32x16{};
-#pragma unroll
-    for (int k = 0; k < 2 * NKK; ++k) s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], s0[k & 1]);
-    mask_scores(0, s0);
     const int k00 = tile_k0(0);
+    f32x16 s0[2];
+#pragma unroll
+    for (int k = 0; k < 2 * NKK; ++k)
+      s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], k < 2 ? minit : s0[k & 1]);
+    mask_scores(0, s0);
     uint32_t pw[16];
     float ts[4] = {0.f, 0.f, 0.f, 0.f};
-    const float base = mod_base(k00) + neg_m();
 #pragma unroll
-    for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00, base, ts);
+    for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00, ts);
     finish_tile(s0, -neg_m(), pw, ts);
     to_frags(pw, pfa);
   }
@@ -561,19 +554,25 @@ fwd_bf16_kernel(const AttnParams p) {
   // the vector work fills the MFMA shadow.
   constexpr int NSA = 2 * NKK;                     // phase A steps
   constexpr int NSB = 4 * NDT;                     // phase B steps
-  constexpr int NROT = ROPE ? 8 * NKW_HI : 0;      // rotation items, one angle each
+  constexpr int NROT = ROPE ? 8 * NKW_HI : 0;      // rotation items, one element pair each
   constexpr int AIPS = (NROT + NSA - 3) / (NSA - 2);  // per step from step 2 on
   constexpr int XPB = 16 / NSB;                    // exp pairs per phase B step
   constexpr int PF = 2;                            // fragment prefetch distance
 
-  // Group instruction slots: every other step of phase A, then of phase B,
-  // IPD instructions per slot.
-  constexpr int DSLOTS = NSA / 2 + NSB / 2;
-  constexpr int IPD = (GRP_HI + DSLOTS - 1) / DSLOTS;
-  auto dma_slot = [&](const Group& g, int slot) {
+  // Group instruction slots: every other step of phase A carries the K part
+  // (IPDA instructions per slot), every other step of phase B the table and
+  // V parts (IPDB per slot).
+  constexpr int IPDA = (2 * NKW_HI + NSA / 2 - 1) / (NSA / 2);
+  constexpr int IPDB = (TPK * NKW_HI + NVW + NSB / 2 - 1) / (NSB / 2);
+  auto dma_slot_a = [&](const Group& g, int slot) {
 #pragma unroll
-    for (int i = slot * IPD; i < (slot + 1) * IPD; ++i)
-      if (i < GRP_HI && i < grp) dma_item(g, i);
+    for (int j = slot * IPDA; j < (slot + 1) * IPDA; ++j)
+      if (j < 2 * NKW_HI && j < 2 * nkw) dma_item(g, j);
+  };
+  auto dma_slot_b = [&](const Group& g, int slot) {
+#pragma unroll
+    for (int j = slot * IPDB; j < (slot + 1) * IPDB; ++j)
+      if (j < TPK * NKW_HI + NVW && 2 * nkw + j < grp) dma_item(g, 2 * nkw + j);
   };
   auto iteration = [&](int t, const bf16x8 (&pf)[4], bf16x8 (&pf_next)[4]) {
     wait_group();
@@ -581,29 +580,26 @@ fwd_bf16_kernel(const AttnParams p) {
 
     // ---- phase A ----
     const char* ks = smem + ((t + 1) % RING) * L::KSLOT;
+    const int k0n = tile_k0(min(t + 1, n - 1));
     f32x16 sn[2];
-    sn[0] = f32x16{};
-    sn[1] = f32x16{};
     bf16x8 afr[PF + 1];
 #pragma unroll
     for (int k = 0; k < PF; ++k) afr[k] = k_frag(ks, k & 1, k >> 1);
-    // Rotation of K(t+2): pair m, angles e = 0..7 of this lane's chunk, in two
-    // halves of four.  A half's operands (two words of the low chunk, two of
-    // the high chunk, four cos and four sin of the angle row) are read from
-    // LDS two steps before its first item, so at most one and a half halves
-    // are held at a time.
+    // Rotation of K(t+2): pair m, elements e = 0..7 of this lane's chunk, in
+    // two halves of four.  A half's operands (two words of the low chunk, two
+    // of the high chunk, four table words) are read from LDS two steps before
+    // its first item, so at most one and a half halves are held at a time.
     char* kslot2 = smem + ((t + 2) % RING) * L::KSLOT;
-    const float* ang2 = reinterpret_cast<const float*>(smem + L::A_OFF + ((t + 2) % RING) * L::NKP * L::ANG);
+    const char* tsl = smem + L::T_OFF + lane * 16;
     uint2 rlo[NKW_HI][2], rhi[NKW_HI][2];
-    float4 rcb[NKW_HI][2], rsb[NKW_HI][2];
+    uint4 rtb[NKW_HI][2];
     uint32_t olw[NKW_HI][4], ohw[NKW_HI][4];
+    uint32_t whn[NKW_HI];
     float rl_even[NKW_HI], rh_even[NKW_HI];
     auto rot_load = [&](int m, int hf) {
       const int kp = wave + NW * m;
       if (m < nkw) {
-        const float* ang = ang2 + kp * (L::ANG / 4);
-        rcb[m][hf] = *reinterpret_cast<const float4*>(ang + 8 * kc + 4 * hf);
-        rsb[m][hf] = *reinterpret_cast<const float4*>(ang + D / 2 + 8 * kc + 4 * hf);
+        rtb[m][hf] = ld16(tsl + kp * L::TPAIR + 1024 * hf);
         rlo[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + kp * 1024 + lane * 16 + 8 * hf);
         rhi[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + L::KHI + kp * 1024 + lane * 16 + 8 * hf);
       }
@@ -613,14 +609,10 @@ fwd_bf16_kernel(const AttnParams p) {
       if (m < nkw) {
         const uint32_t wl = (e4 < 2) ? rlo[m][hf].x : rlo[m][hf].y;
         const uint32_t wh = (e4 < 2) ? rhi[m][hf].x : rhi[m][hf].y;
-        const float l = (e & 1) ? bf16hi(wl) : bf16lo(wl);
-        const float hv = (e & 1) ? bf16hi(wh) : bf16lo(wh);
-        const float cB = e4 == 0 ? rcb[m][hf].x : e4 == 1 ? rcb[m][hf].y : e4 == 2 ? rcb[m][hf].z : rcb[m][hf].w;
-        const float sB = e4 == 0 ? rsb[m][hf].x : e4 == 1 ? rsb[m][hf].y : e4 == 2 ? rsb[m][hf].z : rsb[m][hf].w;
-        const float cs = cB * lcos(e) - sB * lsin(e);
-        const float sv = sB * lcos(e) + cB * lsin(e);
-        const float rl = l * cs - hv * sv;
-        const float rh = hv * cs + l * sv;
+        if (!(e & 1)) whn[m] = wh ^ 0x80008000u;
+        const uint32_t tw = e4 == 0 ? rtb[m][hf].x : e4 == 1 ? rtb[m][hf].y : e4 == 2 ? rtb[m][hf].z : rtb[m][hf].w;
+        float rl, rh;
+        rope_dot2(wl, wh, whn[m], e & 1, tw, rl, rh);
         if (e & 1) {
           olw[m][e / 2] = pack_bf16x2(rl_even[m], rl);
           ohw[m][e / 2] = pack_bf16x2(rh_even[m], rh);
@@ -633,8 +625,8 @@ fwd_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int k = 0; k < NSA; ++k) {
       if (k + PF < NSA) afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
-      sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], sn[k & 1]);
-      if (k & 1) dma_slot(g, k / 2);
+      sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? minit : sn[k & 1]);
+      if (k & 1) dma_slot_a(g, k / 2);
       if (ROPE) {
         // Item ri runs at step 2 + ri / AIPS; its half's operands two steps earlier.
 #pragma unroll
@@ -665,8 +657,6 @@ fwd_bf16_kernel(const AttnParams p) {
     bf16x8 vfr[PF + 1];
 #pragma unroll
     for (int k = 0; k < PF; ++k) vfr[k] = v_frag(vs, k / NDT, k % NDT);
-    const int k0n = tile_k0(min(t + 1, n - 1));
-    const float base = mod_base(k0n) + neg_m();
     uint32_t pw[16];
     float ex[16][2];
     float ts[4] = {0.f, 0.f, 0.f, 0.f};
@@ -674,11 +664,11 @@ fwd_bf16_kernel(const AttnParams p) {
     for (int k = 0; k < NSB; ++k) {
       if (k + PF < NSB) vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
       o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
-      if (k & 1) dma_slot(g, NSA / 2 + k / 2);
+      if (k & 1) dma_slot_b(g, k / 2);
       // Pairs of step k: arguments now, exponentials one step later, pack
       // and row sum two steps later.
 #pragma unroll
-      for (int x = k * XPB; x < (k + 1) * XPB; ++x) exp_stage1(sn, x, k0n, base);
+      for (int x = k * XPB; x < (k + 1) * XPB; ++x) exp_stage1(sn, x, k0n);
 #pragma unroll
       for (int x = (k - 1) * XPB; x < k * XPB; ++x)
         if (x >= 0) exp_stage2(sn, x, ex[x]);

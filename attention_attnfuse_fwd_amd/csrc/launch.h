@@ -29,7 +29,7 @@ hipError_t launch_decode_combine(const AttnParams& p, int D, hipStream_t stream)
 
 // RoPE cos / sin tables and the stand-alone pre-rotation pass.
 hipError_t launch_rope_table(double theta, int D, long long len, float* cos_out, float* sin_out,
-                             uint32_t* cs_out, hipStream_t stream);
+                             uint32_t* cs_out, uint32_t* csb_out, hipStream_t stream);
 hipError_t launch_prerotate(const void* x, void* x_rot, bool bf16, bool vec_ok, int D, int B,
                             int H, int N, long long sb, long long sh, long long sn, int pos0,
                             const float* rcos, const float* rsin, hipStream_t stream);

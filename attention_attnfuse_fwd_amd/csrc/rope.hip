@@ -2,8 +2,9 @@
 // cos / sin table; NeoX half-split pairs (r, r + D/2)).
 //
 //  * rope_table: cos / sin of p * theta^(-2r/D), angle formed in fp64 (an fp32
-//    angle at p ~ 3e4 would carry ~2e-3 rad of error), rounded to fp32 and,
-//    packed as fp16 pairs, for the decode kernel.
+//    angle at p ~ 3e4 would carry ~2e-3 rad of error), rounded to fp32, and
+//    packed as fp16 pairs (decode kernel) and bf16 pairs (the bf16 prefill
+//    kernel rotates K with bf16 dot products).
 //  * prerotate: the separate rotation pass that the fused kernel replaces
 //    ("1 Introduction": the pre-rotation workaround costs two extra memory
 //    round trips; "5.3 The Rotation Calculus" weighs the two).  Rotates a
@@ -14,7 +15,7 @@
 namespace attnfuse {
 
 __global__ void rope_table_kernel(double theta, int D, long long len, float* cos_out,
-                                  float* sin_out, uint32_t* cs_out) {
+                                  float* sin_out, uint32_t* cs_out, uint32_t* csb_out) {
   const int h2 = D / 2;
   const long long n = len * h2;
   for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
@@ -30,6 +31,7 @@ __global__ void rope_table_kernel(double theta, int D, long long len, float* cos
       const f16x2 h = {(_Float16)c, (_Float16)s};
       cs_out[idx] = __builtin_bit_cast(uint32_t, h);
     }
+    if (csb_out) csb_out[idx] = pack_bf16x2((float)c, (float)s);
   }
 }
 
@@ -91,11 +93,11 @@ __global__ void prerotate_bf16x8_kernel(const __bf16* x, __bf16* y, int D, int B
 }
 
 hipError_t launch_rope_table(double theta, int D, long long len, float* cos_out, float* sin_out,
-                             uint32_t* cs_out, hipStream_t stream) {
+                             uint32_t* cs_out, uint32_t* csb_out, hipStream_t stream) {
   const long long n = len * (D / 2);
   const long long blocks = min((n + 255) / 256, 65536LL);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, theta, D,
-                     len, cos_out, sin_out, cs_out);
+                     len, cos_out, sin_out, cs_out, csb_out);
   return hipGetLastError();
 }
 

@@ -57,8 +57,8 @@ _ROPE_CACHE: dict = {}
 
 
 def rope_tables(theta: float, D: int, length: int, device) -> tuple:
-    """(cos, sin, cs_f16) tables [L][D/2] with L >= length, built on the device and cached:
-    fp32 cos and sin, and the packed fp16 (cos, sin) pairs the bf16 kernels read."""
+    """(cos, sin, cs_f16, cs_bf16) tables [L][D/2] with L >= length, built on the device
+    and cached: fp32 cos and sin, and the packed fp16 and bf16 (cos, sin) pairs."""
     device = torch.device(device)
     key = (float(theta), int(D), device.index if device.index is not None else torch.cuda.current_device())
     hit = _ROPE_CACHE.get(key)
@@ -70,10 +70,11 @@ def rope_tables(theta: float, D: int, length: int, device) -> tuple:
     cos = torch.empty((L, D // 2), dtype=torch.float32, device=device)
     sin = torch.empty_like(cos)
     cs16 = torch.empty((L, D // 2), dtype=torch.int32, device=device)
+    csb16 = torch.empty((L, D // 2), dtype=torch.int32, device=device)
     _check(_abi.load().attnfuse_rope_table(float(theta), int(D), int(L), _ptr(cos), _ptr(sin),
-                                           _ptr(cs16), _stream(device)), "rope_table")
-    _ROPE_CACHE[key] = (cos, sin, cs16)
-    return cos, sin, cs16
+                                           _ptr(cs16), _ptr(csb16), _stream(device)), "rope_table")
+    _ROPE_CACHE[key] = (cos, sin, cs16, csb16)
+    return cos, sin, cs16, csb16
 
 
 # ----------------------------------------------------------------------------
@@ -155,12 +156,13 @@ def _make_desc(q, k, v, out, *, scale, causal, window, rope_theta, q_pos0, k_pos
     d.window = int(window or 0)
     if rope_theta is not None:
         need = max(int(q_pos0) + Nq, int(k_pos0) + Nk)
-        cos, sin, cs16 = rope_tables(rope_theta, D, need, q.device)
-        keep.extend([cos, sin, cs16])
+        cos, sin, cs16, csb16 = rope_tables(rope_theta, D, need, q.device)
+        keep.extend([cos, sin, cs16, csb16])
         d.rope = 1
         d.rope_theta = float(rope_theta)
         d.rope_cos, d.rope_sin = cos.data_ptr(), sin.data_ptr()
         d.rope_cs_f16 = cs16.data_ptr()
+        d.rope_cs_bf16 = csb16.data_ptr()
         d.rope_table_len = cos.shape[0]
     if alibi_slopes is not None:
         a = torch.as_tensor(alibi_slopes, dtype=torch.float32).to(q.device).contiguous()

@@ -85,20 +85,27 @@ typedef struct attnfuse_variant_desc {
   /* rope ("4.1 Fused RoPE", NeoX half-split pairs (r, r + D/2)).  rope != 0
    * applies the rotation in-kernel to Q (once) and to every K tile.  The
    * tables hold cos / sin of position * theta^(-2r/D), row-major
-   * [rope_table_len][D/2]: rope_cos / rope_sin as fp32 (read by the fp32
-   * kernels), rope_cs_f16 as one 32-bit word per entry holding the fp16 pair
-   * (cos in the low half, sin in the high half; read by the bf16 kernels,
-   * where the fp16 rounding, at most 2^-12, is well below the bf16 rounding
-   * of the rotated vectors).  Build them with attnfuse_rope_table.  Every
-   * position used (q_pos0 + Nq - 1, k_pos0 + Nk - 1) must be below
-   * rope_table_len.  rope_theta records the base the tables were built with.
-   * With dtype ATTNFUSE_FP32 the fp32 tables are required, with
-   * ATTNFUSE_BF16 the fp16 table; the other may be NULL. */
+   * [rope_table_len][D/2], 16-byte aligned:
+   *   rope_cos / rope_sin: fp32.  Read by attnfuse_fwd (both dtypes: Q is
+   *     rotated in fp32 before its single bf16 rounding) and
+   *     attnfuse_prerotate.
+   *   rope_cs_bf16: one 32-bit word per entry holding the bf16 pair (cos in
+   *     bits 0-15, sin in bits 16-31).  Read by attnfuse_fwd with dtype
+   *     ATTNFUSE_BF16, which rotates each K tile with two bf16 dot products
+   *     per element (the table rounding, at most 2^-9 relative, is of the
+   *     order of the bf16 rounding of the rotated keys themselves).
+   *   rope_cs_f16: the same pairs in fp16 (rounding at most 2^-12).  Read by
+   *     attnfuse_decode.
+   * Build them with attnfuse_rope_table.  Every position used
+   * (q_pos0 + Nq - 1, k_pos0 + Nk - 1) must be below rope_table_len.
+   * rope_theta records the base the tables were built with.  A table an
+   * entry point does not read may be NULL. */
   int32_t rope;
   double rope_theta;
   const float* rope_cos;
   const float* rope_sin;
   const uint32_t* rope_cs_f16;
+  const uint32_t* rope_cs_bf16;
   int64_t rope_table_len;
 
   int64_t q_pos0, k_pos0; /* positions of query row 0 and key row 0 (>= 0)          */
@@ -171,12 +178,13 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
  * cos_out[p][r] = cos(p * theta^(-2r/D)), sin_out likewise, for
  * 0 <= p < len and 0 <= r < D/2, with the angle formed in fp64 and the results
  * rounded to fp32; cs_f16_out[p][r] packs the same two values rounded to
- * fp16 (cos in bits 0-15, sin in bits 16-31).  cos_out, sin_out: device
- * buffers of len * D/2 floats; cs_f16_out: len * D/2 uint32.  Any output may
- * be NULL (at least one must be given).  D even, 2 <= D <= 1024, len >= 1,
- * theta > 0. */
+ * fp16 (cos in bits 0-15, sin in bits 16-31), cs_bf16_out[p][r] packs them
+ * rounded (from fp32, to nearest even) to bf16.  cos_out, sin_out: device
+ * buffers of len * D/2 floats; cs_f16_out, cs_bf16_out: len * D/2 uint32.
+ * Any output may be NULL (at least one must be given).  D even,
+ * 2 <= D <= 1024, 1 <= len < 2^30, theta > 0 and finite. */
 int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, float* sin_out,
-                        uint32_t* cs_f16_out, void* stream);
+                        uint32_t* cs_f16_out, uint32_t* cs_bf16_out, void* stream);
 
 /* Pre-rotation pass (the "apply RoPE in a separate kernel" baseline of
  * "1 Introduction" and "5.3 The Rotation Calculus"): writes RoPE(x) to x_rot.

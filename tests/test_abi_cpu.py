@@ -108,6 +108,10 @@ def test_empty_query_is_ok_without_work(lib):
      _abi.ERR_INVALID),                                      # misaligned table
     (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_table_len=100, dtype=_abi.FP32),
      _abi.ERR_INVALID),                                      # sin table missing
+    (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=100),
+     _abi.ERR_INVALID),                                      # bf16 prefill reads the bf16 pairs (K)
+    (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_cs_bf16=0x3008,
+          rope_table_len=100), _abi.ERR_INVALID),            # misaligned bf16 pair table
     (dict(bs_row_ptr=0x1000, bs_block_m=0, bs_block_n=64), _abi.ERR_INVALID),
     (dict(bs_row_ptr=0x1000, bs_block_m=64, bs_block_n=64, bs_nnz=3), _abi.ERR_INVALID),  # no col_idx
     (dict(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=48, bs_block_n=64, bs_nnz=3),
@@ -155,10 +159,10 @@ def test_decode_validation(lib):
 
 
 def test_rope_table_and_prerotate_validation(lib):
-    assert lib.attnfuse_rope_table(0.0, 64, 10, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID
-    assert lib.attnfuse_rope_table(1e4, 63, 10, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID
-    assert lib.attnfuse_rope_table(1e4, 64, 0, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID
-    assert lib.attnfuse_rope_table(1e4, 64, 10, None, None, None, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_rope_table(0.0, 64, 10, FAKE, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_rope_table(1e4, 63, 10, FAKE, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_rope_table(1e4, 64, 0, FAKE, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_rope_table(1e4, 64, 10, None, None, None, None, None) == _abi.ERR_INVALID
     d = _good_desc()
     assert lib.attnfuse_prerotate(FAKE, FAKE, ctypes.byref(d), 1, None) == _abi.ERR_INVALID  # rope off
     d = _good_desc(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=100)

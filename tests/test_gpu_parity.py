@@ -319,7 +319,7 @@ def test_deterministic_bitwise():
 
 def test_rope_table_matches_fp64():
     D, L, theta = 128, 40000, 5e5
-    cos, sin, cs16 = af.rope_tables(theta, D, L, "cuda")
+    cos, sin, cs16, csb16 = af.rope_tables(theta, D, L, "cuda")
     torch.cuda.synchronize()
     pos = np.array([0, 1, 4095, 32768, 39999])
     r = np.arange(D // 2)
@@ -333,6 +333,14 @@ def test_rope_table_matches_fp64():
     np.testing.assert_allclose(c16, np.cos(ang), rtol=0, atol=2.5e-4)
     np.testing.assert_allclose(s16, np.sin(ang), rtol=0, atol=2.5e-4)
     assert np.max(np.abs(c16 - np.cos(ang))) > 0  # really fp16-rounded
+    # bf16 pairs: the fp32 values rounded to nearest even bf16, bit for bit
+    hb = csb16.cpu().numpy()[pos].view(np.uint32)
+
+    def bf16_rne(x):
+        u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
+    np.testing.assert_array_equal(hb & 0xFFFF, bf16_rne(cos.cpu().numpy()[pos]))
+    np.testing.assert_array_equal(hb >> 16, bf16_rne(sin.cpu().numpy()[pos]))
 
 
 def test_prerotated_path_matches_oracle():
