@@ -144,18 +144,17 @@ __device__ __forceinline__ uint4 scale_bf16x8(const uint4& x, float k) {
 
 // NeoX rotation of element e (0 or 1) of a bf16 word pair, with the angle
 // given as a bf16 (cos, sin) word t (cos in the low half):
-//   rl = l c - h s,  rh = h c + l s,
-// one bf16 dot product each (exact products, fp32 sum).  wl / wh hold
-// elements (2w, 2w+1) of the low / high half; whn is wh with both sign bits
-// flipped.
-__device__ __forceinline__ void rope_dot2(uint32_t wl, uint32_t wh, uint32_t whn, int e, uint32_t t,
-                                          float& rl, float& rh) {
-  const uint32_t sel = e ? 0x07060302u : 0x05040100u;
-  const uint32_t a = __builtin_amdgcn_perm(whn, wl, sel);  // (l, -h)
-  const uint32_t b = __builtin_amdgcn_perm(wl, wh, sel);   // (h, l)
-  const bf16x2 tb = __builtin_bit_cast(bf16x2, t);
-  rl = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), tb, 0.f, false);
-  rh = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, b), tb, 0.f, false);
+//   rl = l c - h s,  rh = h c + l s   (fp32 arithmetic on the exact bf16
+// values).  wl / wh hold elements (2w, 2w+1) of the low / high half.  Plain
+// VALU arithmetic: the bf16 dot-product instructions would queue behind the
+// matrix core, which the partner wave keeps busy.
+__device__ __forceinline__ void rope_elem(uint32_t wl, uint32_t wh, int e, uint32_t t, float& rl,
+                                          float& rh) {
+  const float l = e ? bf16hi(wl) : bf16lo(wl);
+  const float h = e ? bf16hi(wh) : bf16lo(wh);
+  const float c = bf16lo(t), s = bf16hi(t);
+  rl = __builtin_fmaf(l, c, -h * s);
+  rh = __builtin_fmaf(h, c, l * s);
 }
 
 // Rotation of one (low, high) pair of 8-element bf16 chunks with bf16
@@ -168,10 +167,9 @@ __device__ __forceinline__ void rope_rotate_bf16x8_t(uint4& lo, uint4& hi, const
   uint32_t ol[4], oh[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const uint32_t whn = wh[w] ^ 0x80008000u;
     float l0, h0, l1, h1;
-    rope_dot2(wl[w], wh[w], whn, 0, tw[2 * w], l0, h0);
-    rope_dot2(wl[w], wh[w], whn, 1, tw[2 * w + 1], l1, h1);
+    rope_elem(wl[w], wh[w], 0, tw[2 * w], l0, h0);
+    rope_elem(wl[w], wh[w], 1, tw[2 * w + 1], l1, h1);
     ol[w] = pack_bf16x2(l0, l1);
     oh[w] = pack_bf16x2(h0, h1);
   }
@@ -238,6 +236,14 @@ template <int N>
 __device__ __forceinline__ void vmcnt_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt is six bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(N) (LDS / scalar-memory counter), vmcnt and expcnt
+// untouched.
+template <int N>
+__device__ __forceinline__ void lgkmcnt_wait() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));

@@ -25,10 +25,12 @@
 //   O += V(t) P(t) with the exp / pack / row sums of S(t+1) between them.
 //   The DMA of K(t+4) is issued one instruction per step in the first phase,
 //   the table entries of K(t+3) and V(t+3) in the second.
-// The running maximum is only moved when it grows by more than 2^8 (exp2
-// domain); the result is the same exact softmax and the O^T rescale becomes
-// rare.  Row sums are accumulated with bf16 dot products of the very P values
-// that feed the P V product, so the normalisation matches the weights used.
+// The running maximum is only moved when a tile's scores exceed it by more
+// than 15 (exp2 domain); the result is the same exact softmax and the O^T
+// rescale becomes rare.  Row sums come out of the matrix core: one more
+// P V-shaped MFMA per 16 keys with an all-ones A operand sums the very bf16
+// P values that feed the P V product, so the normalisation matches the
+// weights used (and no vector dot product has to queue behind the MFMAs).
 #pragma once
 
 #include "common.h"
@@ -79,6 +81,23 @@ __device__ __forceinline__ constexpr int vswz(int key) {
                   : ((4 * ((key >> 1) & 1)) ^ (2 * ((key >> 2) & 1)));
 }
 
+// Largest bit pattern, read as a signed integer, of 32 floats: for a
+// non-negative threshold T, the result exceeds bits(T) exactly when some
+// value exceeds T or is a positive NaN (negative values compare below).
+// Integer max3 needs no NaN canonicalisation, unlike fmaxf.
+__device__ __forceinline__ int tree_max32_bits(const f32x16& a, const f32x16& b) {
+  int t[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    t[i] = max(max(__float_as_int(a[3 * i]), __float_as_int(a[3 * i + 1])), __float_as_int(a[3 * i + 2]));
+    t[5 + i] = max(max(__float_as_int(b[3 * i]), __float_as_int(b[3 * i + 1])), __float_as_int(b[3 * i + 2]));
+  }
+  t[10] = max(__float_as_int(a[15]), __float_as_int(b[15]));
+  const int u0 = max(max(t[0], t[1]), t[2]), u1 = max(max(t[3], t[4]), t[5]);
+  const int u2 = max(max(t[6], t[7]), t[8]), u3 = max(t[9], t[10]);
+  return max(max(u0, u1), max(u2, u3));
+}
+
 // Maximum of 32 values as a balanced tree (exposes ILP; pairs fold into v_max3).
 __device__ __forceinline__ float tree_max32(const f32x16& a, const f32x16& b) {
   float t[16];
@@ -111,6 +130,7 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr int NKW_HI = (L::NKP + NW - 1) / NW;
   constexpr int NKW_LO = L::NKP / NW;
   constexpr int TPK = ROPE ? 2 : 0;  // table instructions per K pair
+  constexpr bool PP = NW == 8;       // ping-pong schedule (two waves per SIMD)
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -233,11 +253,12 @@ fwd_bf16_kernel(const AttnParams p) {
     int rmax_k, rmax_v;      // last valid row offsets
     uint32_t kslot, vslot;
   };
-  auto make_group = [&](int uk, int uv) -> Group {
+  auto make_group = [&](int uk, int ut, int uv) -> Group {
     Group g;
-    int k0k, rk, rv;
+    int k0k, k0v, rk, rt, rv;
     const int kck = tile_base(uk, k0k, rk);
-    const int kcv = tile_base(uv, g.k0t, rv);
+    const int kcv = tile_base(uv, k0v, rv);
+    tile_base(ut, g.k0t, rt);
     g.kt = kb + (long long)kck * ksn;
     g.vt = vb + (long long)kcv * vsn;
     g.rmax_k = rk;
@@ -275,8 +296,8 @@ fwd_bf16_kernel(const AttnParams p) {
   // A whole group at once (prologue); with_v = false issues the K part only,
   // with_t = false skips the table part.
   constexpr int GRP_MAX = (2 + TPK) * NKW_HI + NVW;
-  auto issue_group = [&](int uk, int uv, bool with_t, bool with_v) {
-    const Group g = make_group(uk, uv);
+  auto issue_group = [&](int uk, int ut, int uv, bool with_t, bool with_v) {
+    const Group g = make_group(uk, ut, uv);
 #pragma unroll
     for (int i = 0; i < GRP_MAX; ++i) {
       const bool is_t = i >= 2 * nkw && i < (2 + TPK) * nkw;
@@ -363,9 +384,12 @@ fwd_bf16_kernel(const AttnParams p) {
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+  // Row sums: ol = ones . P^T, so every register of a lane holds the sum of
+  // its query column.
+  f32x16 ol = f32x16{};
+  const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   float m_run = -INFINITY;  // running max, exp2 domain
-  float l_run = 0.f;        // this lane's share of the row sum (its half of each tile's keys)
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float slope2 = 0.f;  // ALiBi slope times log2(e), loaded in the prologue
   const int dpos = p.k_pos0 - p.q_pos0;
   const float* const brow =
@@ -404,12 +428,11 @@ fwd_bf16_kernel(const AttnParams p) {
 
   // ---- online softmax ("2 Background / FlashAttention and online softmax") ----
   // A tile is exponentiated against the running maximum it arrives with:
-  // p = 2^(score - m_run).  Its partial row sum (needed anyway) bounds every
-  // p, so one compare tells whether any exceeded 2^15 (or was inf / NaN); only
-  // then, and for the first tile with live keys, the exact path takes the
-  // tile maximum, rescales O and l, and exponentiates again.  Every p is then
-  // at most 2^15 and the result is the same exact softmax.
-  constexpr float kTrig = 32768.f;
+  // p = 2^(score - m_run).  Only when some exponent exceeds 15 (or is NaN),
+  // and for the first tile with live keys, the exact path takes the tile
+  // maximum, rescales O and the row sums, and exponentiates again.  Every p
+  // is then at most 2^15 and the result is the same exact softmax.
+  constexpr float kTrig = 15.f;  // largest exp2 argument taken without the exact path
   auto neg_m = [&]() -> float { return (m_run == -INFINITY) ? 0.f : -m_run; };
   // Per-lane, per-tile part of the exp2 argument: score mods' lane offset.
   auto mod_base = [&](int k0) -> float { return SCOREMOD ? slope2 * (float)(k0 + 4 * lh - i + dpos) : 0.f; };
@@ -431,21 +454,18 @@ fwd_bf16_kernel(const AttnParams p) {
     }
     return x;
   };
-  // P pair x: registers r, r+1 of subtile st -> word q of P^T fragment c;
-  // the partial row sum takes the same bf16 values.  The exp2 arguments are
-  // left in s for the exact path.
-  auto exp_pair = [&](f32x16 (&s)[2], int x, int k0, float (&ts)[4]) -> uint32_t {
+  // P pair x: registers r, r+1 of subtile st -> word q of P^T fragment c.
+  // The exp2 arguments are left in s for the overflow check and the exact
+  // path.
+  auto exp_pair = [&](f32x16 (&s)[2], int x, int k0) -> uint32_t {
     const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
     s[st][r] = arg(s, st, r, k0);
     s[st][r + 1] = arg(s, st, r + 1, k0);
-    const uint32_t w = pack_bf16x2(fast_exp2(s[st][r]), fast_exp2(s[st][r + 1]));
-    ts[q] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ts[q], false);
-    asm volatile("" ::"v"(w));  // anchor it to this step (no sinking towards its use)
-    return w;
+    return pack_bf16x2(fast_exp2(s[st][r]), fast_exp2(s[st][r + 1]));
   };
   // The same work in three stages, so that a pipelined loop can give each
   // step independent instructions: (1) the exp2 arguments, left in s;
-  // (2) the two exponentials; (3) pack to bf16 and add to the row sum.
+  // (2) the two exponentials; (3) pack to bf16.
   auto exp_stage1 = [&](f32x16 (&s)[2], int x, int k0) {
     if (!SCOREMOD) return;
     const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
@@ -459,25 +479,21 @@ fwd_bf16_kernel(const AttnParams p) {
     e[0] = fast_exp2(s[st][r]);
     e[1] = fast_exp2(s[st][r + 1]);
   };
-  auto exp_stage3 = [&](int x, const float (&e)[2], float (&ts)[4]) -> uint32_t {
+  auto exp_stage3 = [&](int x, const float (&e)[2]) -> uint32_t {
     const uint32_t w = pack_bf16x2(e[0], e[1]);
-    ts[x % 4] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, ts[x % 4], false);
     asm volatile("" ::"v"(w));  // anchor it to this step (no sinking towards its use)
     return w;
   };
-  // Check the tile's sums; on the rare exact path re-exponentiate against the
-  // tile maximum (O^T must already hold every earlier tile's product).  s
-  // holds the exp2 arguments relative to m_use.  Adds the tile to l_run.
-  auto finish_tile = [&](f32x16 (&s)[2], float m_use, uint32_t (&pw)[16], float (&ts)[4]) {
-    float tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
-    const bool trig = !(tsum <= kTrig) || (m_run == -INFINITY && tsum > 0.f);
+  // Check the tile's exponents; on the rare exact path re-exponentiate
+  // against the tile maximum (O^T and the row sums must already hold every
+  // earlier tile's product).  s holds the exp2 arguments relative to m_use.
+  // While no key has been seen (m_run = -inf) every tile takes the exact
+  // path, which then establishes the maximum.
+  auto finish_tile = [&](f32x16 (&s)[2], float m_use, uint32_t (&pw)[16]) {
+    const bool trig = tree_max32_bits(s[0], s[1]) > __float_as_int(kTrig) || m_run == -INFINITY;
     if (__builtin_amdgcn_ballot_w64(trig)) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-      mx = fmaxf(mx, partner32(mx)) + m_use;
+      const float mx_l = tree_max32(s[0], s[1]);
+      const float mx = fmaxf(mx_l, partner32(mx_l)) + m_use;
       const float m_new = fmaxf(m_run, mx);
       float shift = 0.f;
       if (m_new != -INFINITY) {
@@ -485,21 +501,19 @@ fwd_bf16_kernel(const AttnParams p) {
         m_run = m_new;
         minit = f32x16{} - m_new;
         shift = m_use - m_new;
-        l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ol[r] *= alpha;
       }
-      tsum = 0.f;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int c = x / 4, q = x % 4, st = c / 2, r = 8 * (c % 2) + 2 * q;
         pw[x] = pack_bf16x2(fast_exp2(s[st][r] + shift), fast_exp2(s[st][r + 1] + shift));
-        tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[x]), ones, tsum, false);
       }
     }
-    l_run += tsum;
   };
   auto to_frags = [](const uint32_t (&pw)[16], bf16x8 (&pf)[4]) {
 #pragma unroll
@@ -509,27 +523,8 @@ fwd_bf16_kernel(const AttnParams p) {
 
   const int n = n_tiles;
   bf16x8 pfa[4], pfb[4];  // P^T of the tile the next iteration multiplies with V (ping-pong)
-  // Prologue: K(0), K(1) loaded and rotated, V(0) loaded; the groups of
-  // iterations -2 and -1 ({K(2), V(1)}, {K(3), V(2)}) in flight; P(0).
-  if (n > 0) {
-    issue_group(0, 0, false, true);
-    issue_group(1, 1, false, false);
-  }
-  // Q and the slope load while the first tiles arrive.
-  load_q();
-  if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
-  vmcnt_wait<0>();
-  if (n > 0) {
-    if (ROPE) {
-      rotate_direct(0);
-      rotate_direct(1);
-    }
-    // Groups of iterations -2 and -1: {K(2), V(1)}, {K(3), table of K(2), V(2)}.
-    issue_group(2, 1, false, true);
-    issue_group(3, 2, true, true);
-  }
-  __syncthreads();
-  if (n > 0) {
+  // S(0) -> P(0) in the prologue, shared by both schedules.
+  auto first_tile = [&]() {
     const int k00 = tile_k0(0);
     f32x16 s0[2];
 #pragma unroll
@@ -537,164 +532,325 @@ fwd_bf16_kernel(const AttnParams p) {
       s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], k < 2 ? minit : s0[k & 1]);
     mask_scores(0, s0);
     uint32_t pw[16];
-    float ts[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00, ts);
-    finish_tile(s0, -neg_m(), pw, ts);
+    for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00);
+    finish_tile(s0, -neg_m(), pw);
     to_frags(pw, pfa);
-  }
-  // Iteration 0 refills K slot 0, which every wave has just read for S(0).
-  __syncthreads();
-
-  // ---- main loop: hand-scheduled phases, one MFMA per step ----
-  // Phase A: the MFMAs of S(t+1); between them the RoPE rotation of K(t+2).
-  // Phase B: the MFMAs of O^T += V^T P^T for tile t; between them the
-  // exp / pack / row sums that turn S(t+1) into P(t+1).  Fragments are read
-  // PF steps ahead; sched_barrier keeps each step's instructions together so
-  // the vector work fills the MFMA shadow.
-  constexpr int NSA = 2 * NKK;                     // phase A steps
-  constexpr int NSB = 4 * NDT;                     // phase B steps
-  constexpr int NROT = ROPE ? 8 * NKW_HI : 0;      // rotation items, one element pair each
-  constexpr int AIPS = (NROT + NSA - 3) / (NSA - 2);  // per step from step 2 on
-  constexpr int XPB = 16 / NSB;                    // exp pairs per phase B step
-  constexpr int PF = 2;                            // fragment prefetch distance
-
-  // Group instruction slots: every other step of phase A carries the K part
-  // (IPDA instructions per slot), every other step of phase B the table and
-  // V parts (IPDB per slot).
-  constexpr int IPDA = (2 * NKW_HI + NSA / 2 - 1) / (NSA / 2);
-  constexpr int IPDB = (TPK * NKW_HI + NVW + NSB / 2 - 1) / (NSB / 2);
-  auto dma_slot_a = [&](const Group& g, int slot) {
-#pragma unroll
-    for (int j = slot * IPDA; j < (slot + 1) * IPDA; ++j)
-      if (j < 2 * NKW_HI && j < 2 * nkw) dma_item(g, j);
   };
-  auto dma_slot_b = [&](const Group& g, int slot) {
-#pragma unroll
-    for (int j = slot * IPDB; j < (slot + 1) * IPDB; ++j)
-      if (j < TPK * NKW_HI + NVW && 2 * nkw + j < grp) dma_item(g, 2 * nkw + j);
-  };
-  auto iteration = [&](int t, const bf16x8 (&pf)[4], bf16x8 (&pf_next)[4]) {
-    wait_group();
-    const Group g = make_group(t + 4, t + 3);
-
-    // ---- phase A ----
-    const char* ks = smem + ((t + 1) % RING) * L::KSLOT;
-    const int k0n = tile_k0(min(t + 1, n - 1));
-    f32x16 sn[2];
-    bf16x8 afr[PF + 1];
-#pragma unroll
-    for (int k = 0; k < PF; ++k) afr[k] = k_frag(ks, k & 1, k >> 1);
-    // Rotation of K(t+2): pair m, elements e = 0..7 of this lane's chunk, in
-    // two halves of four.  A half's operands (two words of the low chunk, two
-    // of the high chunk, four table words) are read from LDS two steps before
-    // its first item, so at most one and a half halves are held at a time.
-    char* kslot2 = smem + ((t + 2) % RING) * L::KSLOT;
-    const char* tsl = smem + L::T_OFF + lane * 16;
-    uint2 rlo[NKW_HI][2], rhi[NKW_HI][2];
-    uint4 rtb[NKW_HI][2];
-    uint32_t olw[NKW_HI][4], ohw[NKW_HI][4];
-    uint32_t whn[NKW_HI];
-    float rl_even[NKW_HI], rh_even[NKW_HI];
-    auto rot_load = [&](int m, int hf) {
-      const int kp = wave + NW * m;
-      if (m < nkw) {
-        rtb[m][hf] = ld16(tsl + kp * L::TPAIR + 1024 * hf);
-        rlo[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + kp * 1024 + lane * 16 + 8 * hf);
-        rhi[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + L::KHI + kp * 1024 + lane * 16 + 8 * hf);
-      }
-    };
-    auto rot_item = [&](int ri) {
-      const int m = ri / 8, e = ri % 8, hf = e / 4, e4 = e % 4;
-      if (m < nkw) {
-        const uint32_t wl = (e4 < 2) ? rlo[m][hf].x : rlo[m][hf].y;
-        const uint32_t wh = (e4 < 2) ? rhi[m][hf].x : rhi[m][hf].y;
-        if (!(e & 1)) whn[m] = wh ^ 0x80008000u;
-        const uint32_t tw = e4 == 0 ? rtb[m][hf].x : e4 == 1 ? rtb[m][hf].y : e4 == 2 ? rtb[m][hf].z : rtb[m][hf].w;
-        float rl, rh;
-        rope_dot2(wl, wh, whn[m], e & 1, tw, rl, rh);
-        if (e & 1) {
-          olw[m][e / 2] = pack_bf16x2(rl_even[m], rl);
-          ohw[m][e / 2] = pack_bf16x2(rh_even[m], rh);
-        } else {
-          rl_even[m] = rl;
-          rh_even[m] = rh;
-        }
-      }
-    };
-#pragma unroll
-    for (int k = 0; k < NSA; ++k) {
-      if (k + PF < NSA) afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
-      sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? minit : sn[k & 1]);
-      if (k & 1) dma_slot_a(g, k / 2);
-      if (ROPE) {
-        // Item ri runs at step 2 + ri / AIPS; its half's operands two steps earlier.
-#pragma unroll
-        for (int hh = 0; hh < 2 * NKW_HI; ++hh)
-          if ((4 * hh) / AIPS == k) rot_load(hh / 2, hh % 2);
-        if (k >= 2) {
-#pragma unroll
-          for (int ri = (k - 2) * AIPS; ri < (k - 1) * AIPS; ++ri)
-            if (ri < NROT) rot_item(ri);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PP) {
+    // ---- ping-pong schedule (two waves per SIMD) ----
+    // Waves w and w + NW/2 share a SIMD.  Each wave alternates an MFMA
+    // cluster M(t) (S(t+1) = K'(t+1) Q'^T and O^T += V(t)^T P(t)^T, 32 MFMAs,
+    // operands from LDS) with a vector cluster (softmax of the S tile just
+    // computed, in-place RoPE of one K tile, DMA issue); a barrier closes
+    // every cluster.  The second half of the workgroup starts with one extra
+    // vector cluster, so on every SIMD one wave keeps the matrix core busy
+    // while its partner does the vector work.
+    // Half-step timing (slot 2t: first half runs M(t), second half a vector
+    // cluster; slot 2t+1: the other way round): in slots 2t and 2t+1 both
+    // halves rotate their pairs of K(t+2) and issue the DMA of K(t+3), its
+    // table entries and V(t+2).  A vector cluster first waits for every DMA
+    // its wave issued in its previous vector cluster; with four-slot rings
+    // every slot is refilled only after both halves have read it.
+    const bool m_first = wave < NW / 2;
+    if (n > 0) {
+      issue_group(0, 0, 0, false, true);  // K(0), V(0)
+      issue_group(1, 1, 1, false, true);  // K(1), V(1)
+      issue_group(2, 2, 2, true, false);  // K(2) and its table entries
     }
-    if (ROPE) {
+    load_q();
+    if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
+    vmcnt_wait<0>();
+    if (n > 0 && ROPE) {
+      rotate_direct(0);
+      rotate_direct(1);
+    }
+    __syncthreads();
+    if (n > 0) first_tile();
+
+    constexpr int NST = 2 * NKK;  // MFMA pairs per cluster (S step + PV step)
+    static_assert(NST == 4 * NDT, "one S and one PV MFMA per step");
+    constexpr int PF = 2;         // fragment prefetch distance
+    f32x16 sn[2];                 // S(t+1) from an MFMA cluster to the next vector cluster
+    // The MFMA cluster runs at raised wave priority: when both waves of a SIMD
+    // can issue, the matrix core is fed first (otherwise the older wave wins
+    // and the second half's MFMA clusters stretch).
+    auto mcluster = [&](int t, const bf16x8 (&pf)[4]) {
+      __builtin_amdgcn_s_setprio(1);
+      const char* ks = smem + ((t + 1) % RING) * L::KSLOT;
+      const uint32_t vs = lds0 + L::V_OFF + (uint32_t)(t % RING) * L::VSLOT;
+      bf16x8 afr[PF + 1], vfr[PF + 1];
 #pragma unroll
-      for (int m = 0; m < NKW_HI; ++m) {
+      for (int k = 0; k < PF; ++k) {
+        afr[k] = k_frag(ks, k & 1, k >> 1);
+        vfr[k] = v_frag(vs, k / NDT, k % NDT);
+      }
+#pragma unroll
+      for (int k = 0; k < NST; ++k) {
+        if (k + PF < NST) {
+          afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
+          vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
+        }
+        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? minit : sn[k & 1]);
+        o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
+        if (k % NDT == NDT - 1) ol = mfma32(ones8, pf[k / NDT], ol);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // Vector cluster of step t; st = index of the S tile to turn into P
+    // (absent for the second half's first step).
+    auto vcluster = [&](int t, int st, bool has_s, bf16x8 (&pf_next)[4]) {
+      vmcnt_wait<0>();
+      const Group g = make_group(t + 3, t + 3, t + 2);
+      // K(t+3) and V(t+2) first: their slots were last read two steps ago.
+#pragma unroll
+      for (int i = 0; i < 2 * NKW_HI; ++i)
+        if (i < 2 * nkw) dma_item(g, i);
+#pragma unroll
+      for (int j = 0; j < NVW; ++j) dma_item(g, (2 + TPK) * nkw + j);
+      // Operands of the rotation of K(t+2).
+      char* kslot2 = smem + ((t + 2) % RING) * L::KSLOT;
+      const char* tsl = smem + L::T_OFF + lane * 16;
+      uint4 rl[NKW_HI], rh[NKW_HI], rt0[NKW_HI], rt1[NKW_HI];
+      if (ROPE) {
+#pragma unroll
+        for (int m = 0; m < NKW_HI; ++m) {
+          const int kp = wave + NW * m;
+          if (m < nkw) {
+            rl[m] = ld16(kslot2 + kp * 1024 + lane * 16);
+            rh[m] = ld16(kslot2 + L::KHI + kp * 1024 + lane * 16);
+            rt0[m] = ld16(tsl + kp * L::TPAIR);
+            rt1[m] = ld16(tsl + kp * L::TPAIR + 1024);
+          }
+        }
+      }
+      if (ROPE) {
+        // Table entries of K(t+3) go into the slot just read: wait for those
+        // reads, then issue (the exponentials below cover the latency).
+        lgkmcnt_wait<0>();
+#pragma unroll
+        for (int i = 2 * NKW_HI; i < (2 + TPK) * NKW_HI; ++i)
+          if (i - 2 * NKW_HI < TPK * nkw) dma_item(g, i - 2 * NKW_HI + 2 * nkw);
+      }
+      if (has_s) {
+        const int k0s = tile_k0(min(st, n - 1));
+        mask_scores(st, sn);
+        uint32_t pw[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) pw[x] = exp_pair(sn, x, k0s);
+        finish_tile(sn, -neg_m(), pw);
+        to_frags(pw, pf_next);
+      }
+      if (ROPE) {
+#pragma unroll
+        for (int m = 0; m < NKW_HI; ++m) {
+          const int kp = wave + NW * m;
+          if (m < nkw) {
+            rope_rotate_bf16x8_t(rl[m], rh[m], rt0[m], rt1[m]);
+            st16(kslot2 + kp * 1024 + lane * 16, rl[m]);
+            st16(kslot2 + L::KHI + kp * 1024 + lane * 16, rh[m]);
+          }
+        }
+      }
+    };
+    // Both halves run the same loop; the second half's vector clusters work
+    // one step ahead on K and V (their slot 2t+2 belongs to step t+1).
+    const int dstep = m_first ? 0 : 1;
+    if (n > 0 && !m_first) {
+      vcluster(0, 0, false, pfb);
+      __syncthreads();
+    }
+    auto step = [&](int t, const bf16x8 (&pf_cur)[4], bf16x8 (&pf_nxt)[4]) {
+      mcluster(t, pf_cur);
+      __syncthreads();
+      vcluster(t + dstep, t + 1, true, pf_nxt);
+      __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < n; t += 2) {
+      step(t, pfa, pfb);
+      step(t + 1, pfb, pfa);
+    }
+    if (t < n) step(t, pfa, pfb);
+    // Same barrier count in both halves: the first half's closing barrier
+    // matches the second half's extra vector cluster.
+    if (n > 0 && m_first) __syncthreads();
+  } else {
+    // Prologue: K(0), K(1) loaded and rotated, V(0) loaded; the groups of
+    // iterations -2 and -1 ({K(2), V(1)}, {K(3), V(2)}) in flight; P(0).
+    if (n > 0) {
+      issue_group(0, 0, 0, false, true);
+      issue_group(1, 1, 1, false, false);
+    }
+    // Q and the slope load while the first tiles arrive.
+    load_q();
+    if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
+    vmcnt_wait<0>();
+    if (n > 0) {
+      if (ROPE) {
+        rotate_direct(0);
+        rotate_direct(1);
+      }
+      // Groups of iterations -2 and -1: {K(2), V(1)}, {K(3), table of K(2), V(2)}.
+      issue_group(2, 2, 1, false, true);
+      issue_group(3, 2, 2, true, true);
+    }
+    __syncthreads();
+    if (n > 0) first_tile();
+    // Iteration 0 refills K slot 0, which every wave has just read for S(0).
+    __syncthreads();
+
+    // ---- main loop: hand-scheduled phases, one MFMA per step ----
+    // Phase A: the MFMAs of S(t+1); between them the RoPE rotation of K(t+2).
+    // Phase B: the MFMAs of O^T += V^T P^T for tile t; between them the
+    // exp / pack / row sums that turn S(t+1) into P(t+1).  Fragments are read
+    // PF steps ahead; sched_barrier keeps each step's instructions together so
+    // the vector work fills the MFMA shadow.
+    constexpr int NSA = 2 * NKK;                     // phase A steps
+    constexpr int NSB = 4 * NDT;                     // phase B steps
+    constexpr int NROT = ROPE ? 8 * NKW_HI : 0;      // rotation items, one element pair each
+    constexpr int AIPS = (NROT + NSA - 3) / (NSA - 2);  // per step from step 2 on
+    constexpr int XPB = 16 / NSB;                    // exp pairs per phase B step
+    constexpr int PF = 2;                            // fragment prefetch distance
+
+    // Group instruction slots: every other step of phase A carries the K part
+    // (IPDA instructions per slot), every other step of phase B the table and
+    // V parts (IPDB per slot).
+    constexpr int IPDA = (2 * NKW_HI + NSA / 2 - 1) / (NSA / 2);
+    constexpr int IPDB = (TPK * NKW_HI + NVW + NSB / 2 - 1) / (NSB / 2);
+    auto dma_slot_a = [&](const Group& g, int slot) {
+  #pragma unroll
+      for (int j = slot * IPDA; j < (slot + 1) * IPDA; ++j)
+        if (j < 2 * NKW_HI && j < 2 * nkw) dma_item(g, j);
+    };
+    auto dma_slot_b = [&](const Group& g, int slot) {
+  #pragma unroll
+      for (int j = slot * IPDB; j < (slot + 1) * IPDB; ++j)
+        if (j < TPK * NKW_HI + NVW && 2 * nkw + j < grp) dma_item(g, 2 * nkw + j);
+    };
+    auto iteration = [&](int t, const bf16x8 (&pf)[4], bf16x8 (&pf_next)[4]) {
+      wait_group();
+      const Group g = make_group(t + 4, t + 3, t + 3);
+
+      // ---- phase A ----
+      const char* ks = smem + ((t + 1) % RING) * L::KSLOT;
+      const int k0n = tile_k0(min(t + 1, n - 1));
+      f32x16 sn[2];
+      bf16x8 afr[PF + 1];
+  #pragma unroll
+      for (int k = 0; k < PF; ++k) afr[k] = k_frag(ks, k & 1, k >> 1);
+      // Rotation of K(t+2): pair m, elements e = 0..7 of this lane's chunk, in
+      // two halves of four.  A half's operands (two words of the low chunk, two
+      // of the high chunk, four table words) are read from LDS two steps before
+      // its first item, so at most one and a half halves are held at a time.
+      char* kslot2 = smem + ((t + 2) % RING) * L::KSLOT;
+      const char* tsl = smem + L::T_OFF + lane * 16;
+      uint2 rlo[NKW_HI][2], rhi[NKW_HI][2];
+      uint4 rtb[NKW_HI][2];
+      uint32_t olw[NKW_HI][4], ohw[NKW_HI][4];
+      float rl_even[NKW_HI], rh_even[NKW_HI];
+      auto rot_load = [&](int m, int hf) {
         const int kp = wave + NW * m;
         if (m < nkw) {
-          st16(kslot2 + kp * 1024 + lane * 16, make_uint4(olw[m][0], olw[m][1], olw[m][2], olw[m][3]));
-          st16(kslot2 + L::KHI + kp * 1024 + lane * 16, make_uint4(ohw[m][0], ohw[m][1], ohw[m][2], ohw[m][3]));
+          rtb[m][hf] = ld16(tsl + kp * L::TPAIR + 1024 * hf);
+          rlo[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + kp * 1024 + lane * 16 + 8 * hf);
+          rhi[m][hf] = *reinterpret_cast<const uint2*>(kslot2 + L::KHI + kp * 1024 + lane * 16 + 8 * hf);
+        }
+      };
+      auto rot_item = [&](int ri) {
+        const int m = ri / 8, e = ri % 8, hf = e / 4, e4 = e % 4;
+        if (m < nkw) {
+          const uint32_t wl = (e4 < 2) ? rlo[m][hf].x : rlo[m][hf].y;
+          const uint32_t wh = (e4 < 2) ? rhi[m][hf].x : rhi[m][hf].y;
+          const uint32_t tw = e4 == 0 ? rtb[m][hf].x : e4 == 1 ? rtb[m][hf].y : e4 == 2 ? rtb[m][hf].z : rtb[m][hf].w;
+          float rl, rh;
+          rope_elem(wl, wh, e & 1, tw, rl, rh);
+          if (e & 1) {
+            olw[m][e / 2] = pack_bf16x2(rl_even[m], rl);
+            ohw[m][e / 2] = pack_bf16x2(rh_even[m], rh);
+          } else {
+            rl_even[m] = rl;
+            rh_even[m] = rh;
+          }
+        }
+      };
+  #pragma unroll
+      for (int k = 0; k < NSA; ++k) {
+        if (k + PF < NSA) afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
+        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? minit : sn[k & 1]);
+        if (k & 1) dma_slot_a(g, k / 2);
+        if (ROPE) {
+          // Item ri runs at step 2 + ri / AIPS; its half's operands two steps earlier.
+  #pragma unroll
+          for (int hh = 0; hh < 2 * NKW_HI; ++hh)
+            if ((4 * hh) / AIPS == k) rot_load(hh / 2, hh % 2);
+          if (k >= 2) {
+  #pragma unroll
+            for (int ri = (k - 2) * AIPS; ri < (k - 1) * AIPS; ++ri)
+              if (ri < NROT) rot_item(ri);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ROPE) {
+  #pragma unroll
+        for (int m = 0; m < NKW_HI; ++m) {
+          const int kp = wave + NW * m;
+          if (m < nkw) {
+            st16(kslot2 + kp * 1024 + lane * 16, make_uint4(olw[m][0], olw[m][1], olw[m][2], olw[m][3]));
+            st16(kslot2 + L::KHI + kp * 1024 + lane * 16, make_uint4(ohw[m][0], ohw[m][1], ohw[m][2], ohw[m][3]));
+          }
         }
       }
-    }
-    mask_scores(t + 1, sn);
+      mask_scores(t + 1, sn);
 
-    // ---- phase B ----
-    const uint32_t vs = lds0 + L::V_OFF + (uint32_t)(t % RING) * L::VSLOT;
-    bf16x8 vfr[PF + 1];
-#pragma unroll
-    for (int k = 0; k < PF; ++k) vfr[k] = v_frag(vs, k / NDT, k % NDT);
-    uint32_t pw[16];
-    float ex[16][2];
-    float ts[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-      if (k + PF < NSB) vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
-      o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
-      if (k & 1) dma_slot_b(g, k / 2);
-      // Pairs of step k: arguments now, exponentials one step later, pack
-      // and row sum two steps later.
-#pragma unroll
-      for (int x = k * XPB; x < (k + 1) * XPB; ++x) exp_stage1(sn, x, k0n);
-#pragma unroll
-      for (int x = (k - 1) * XPB; x < k * XPB; ++x)
-        if (x >= 0) exp_stage2(sn, x, ex[x]);
-#pragma unroll
-      for (int x = (k - 2) * XPB; x < (k - 1) * XPB; ++x)
-        if (x >= 0) pw[x] = exp_stage3(x, ex[x], ts);
-      __builtin_amdgcn_sched_barrier(0);
+      // ---- phase B ----
+      const uint32_t vs = lds0 + L::V_OFF + (uint32_t)(t % RING) * L::VSLOT;
+      bf16x8 vfr[PF + 1];
+  #pragma unroll
+      for (int k = 0; k < PF; ++k) vfr[k] = v_frag(vs, k / NDT, k % NDT);
+      uint32_t pw[16];
+      float ex[16][2];
+  #pragma unroll
+      for (int k = 0; k < NSB; ++k) {
+        if (k + PF < NSB) vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
+        o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
+        if (k % NDT == NDT - 1) ol = mfma32(ones8, pf[k / NDT], ol);
+        if (k & 1) dma_slot_b(g, k / 2);
+        // Pairs of step k: arguments now, exponentials one step later, pack
+        // and row sum two steps later.
+  #pragma unroll
+        for (int x = k * XPB; x < (k + 1) * XPB; ++x) exp_stage1(sn, x, k0n);
+  #pragma unroll
+        for (int x = (k - 1) * XPB; x < k * XPB; ++x)
+          if (x >= 0) exp_stage2(sn, x, ex[x]);
+  #pragma unroll
+        for (int x = (k - 2) * XPB; x < (k - 1) * XPB; ++x)
+          if (x >= 0) pw[x] = exp_stage3(x, ex[x]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  #pragma unroll
+      for (int x = (NSB - 1) * XPB; x < NSB * XPB; ++x) exp_stage2(sn, x, ex[x]);
+  #pragma unroll
+      for (int x = (NSB - 2) * XPB; x < NSB * XPB; ++x) pw[x] = exp_stage3(x, ex[x]);
+      finish_tile(sn, -neg_m(), pw);
+      to_frags(pw, pf_next);
+      __syncthreads();
+    };
+    // Unrolled by two so that the P tiles swap roles without copies.
+    int t = 0;
+    for (; t + 1 < n; t += 2) {
+      iteration(t, pfa, pfb);
+      iteration(t + 1, pfb, pfa);
     }
-#pragma unroll
-    for (int x = (NSB - 1) * XPB; x < NSB * XPB; ++x) exp_stage2(sn, x, ex[x]);
-#pragma unroll
-    for (int x = (NSB - 2) * XPB; x < NSB * XPB; ++x) pw[x] = exp_stage3(x, ex[x], ts);
-    finish_tile(sn, -neg_m(), pw, ts);
-    to_frags(pw, pf_next);
-    __syncthreads();
-  };
-  // Unrolled by two so that the P tiles swap roles without copies.
-  int t = 0;
-  for (; t + 1 < n; t += 2) {
-    iteration(t, pfa, pfb);
-    iteration(t + 1, pfb, pfa);
+    if (t < n) iteration(t, pfa, pfb);
   }
-  if (t < n) iteration(t, pfa, pfb);
+  // No DMA may land in LDS after the workgroup ends.
+  vmcnt_wait<0>();
 
   // ---- epilogue: O = O^T / l, optional lse ----
-  const float l_tot = l_run + partner32(l_run);
+  const float l_tot = ol[0];
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (i < p.Nq) {
     __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh + (long long)i * p.osn;

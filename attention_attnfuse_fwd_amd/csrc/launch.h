@@ -17,10 +17,10 @@ hipError_t launch_fwd_bf16(const AttnParams& p, bool rope, bool scoremod, bool s
 hipError_t launch_fwd_fp32(const AttnParams& p, int D, unsigned grid, hipStream_t stream);
 
 // Split-KV decode phase 1 (partials into p.ws) and phase 2 (LSE merge).
-// Head dim 128 with both RoPE and score mods does not fit two waves per SIMD
-// without spilling; the dispatcher runs it with at most 4 waves.
-constexpr bool fwd_bf16_supported(int D, int NW, bool rope, bool scoremod, bool /*sparse*/) {
-  return !(D == 128 && NW == 8 && rope && scoremod);
+// Head dim 128 with score mods and either RoPE or a block mask does not fit
+// two waves per SIMD without spilling; the dispatcher runs it with 4 waves.
+constexpr bool fwd_bf16_supported(int D, int NW, bool rope, bool scoremod, bool sparse) {
+  return !(D == 128 && NW == 8 && scoremod && (rope || sparse));
 }
 
 hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned grid,
