@@ -64,9 +64,9 @@ int validate_common(const attnfuse_variant_desc* d) {
   return ATTNFUSE_OK;
 }
 
-// RoPE tables each entry point reads: fp32 cos / sin for prefill (Q) and the
-// pre-rotation pass, bf16 pairs for the bf16 prefill (K), fp16 pairs for
-// decode.
+// RoPE tables each entry point reads: fp32 cos / sin for the fp32 prefill
+// and the pre-rotation pass; fp16 pairs for the bf16 prefill's Q and for
+// decode; bf16 pairs for the bf16 prefill's K.
 bool fp32_tables_ok(const attnfuse_variant_desc* d) {
   return !d->rope || (d->rope_cos && d->rope_sin && aligned16(d->rope_cos) && aligned16(d->rope_sin));
 }
@@ -162,8 +162,10 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   const attnfuse_variant_desc* d = desc;
   // K and V may be NULL only when there are no keys (an empty tensor).
   if (!q || !out || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
-  if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
-  if (d->dtype == ATTNFUSE_BF16 && !bf16_table_ok(d)) return ATTNFUSE_ERR_INVALID;
+  // fp32 kernels read the fp32 tables; bf16 kernels rotate Q with the fp16
+  // pairs and K with the bf16 pairs.
+  if (d->dtype == ATTNFUSE_FP32 && !fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
+  if (d->dtype == ATTNFUSE_BF16 && (!bf16_table_ok(d) || !f16_table_ok(d))) return ATTNFUSE_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return ATTNFUSE_ERR_UNSUPPORTED;
   const bool sparse = d->bs_row_ptr != nullptr;

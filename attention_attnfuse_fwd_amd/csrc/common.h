@@ -179,11 +179,11 @@ __device__ __forceinline__ void rope_rotate_bf16x8_t(uint4& lo, uint4& hi, const
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// NeoX rotation of one (low, high) pair of 8-element bf16 chunks with the
-// angles' (cos, sin) given as fp16 pairs (one 32-bit word per angle, cos in
-// the low half): fp32 math, bf16 result.
+// NeoX rotation of one (low, high) pair of 8-element bf16 chunks, times k,
+// with the angles' (cos, sin) given as fp16 pairs (one 32-bit word per angle,
+// cos in the low half): fp32 math, bf16 result.
 __device__ __forceinline__ void rope_rotate_bf16x8_h(uint4& lo, uint4& hi, const uint4& cs0,
-                                                     const uint4& cs1) {
+                                                     const uint4& cs1, float k = 1.f) {
   const uint32_t cw[8] = {cs0.x, cs0.y, cs0.z, cs0.w, cs1.x, cs1.y, cs1.z, cs1.w};
   const uint32_t* wl = reinterpret_cast<const uint32_t*>(&lo);
   const uint32_t* wh = reinterpret_cast<const uint32_t*>(&hi);
@@ -194,7 +194,7 @@ __device__ __forceinline__ void rope_rotate_bf16x8_h(uint4& lo, uint4& hi, const
     const float h0 = bf16lo(wh[w]), h1 = bf16hi(wh[w]);
     const f16x2 a = __builtin_bit_cast(f16x2, cw[2 * w]);
     const f16x2 b = __builtin_bit_cast(f16x2, cw[2 * w + 1]);
-    const float c0 = (float)a[0], s0 = (float)a[1], c1 = (float)b[0], s1 = (float)b[1];
+    const float c0 = (float)a[0] * k, s0 = (float)a[1] * k, c1 = (float)b[0] * k, s1 = (float)b[1] * k;
     ol[w] = pack_bf16x2(l0 * c0 - h0 * s0, l1 * c1 - h1 * s1);
     oh[w] = pack_bf16x2(h0 * c0 + l0 * s0, h1 * c1 + l1 * s1);
   }

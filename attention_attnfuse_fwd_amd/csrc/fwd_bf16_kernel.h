@@ -308,17 +308,29 @@ fwd_bf16_kernel(const AttnParams p) {
 
   // ---- RoPE of K in place: prologue tiles ----
   // Tiles 0 and 1 are rotated before the loop with table words read straight
-  // from global memory; the loop rotates later tiles from the table slot.
+  // from global memory, fetched together with the first tiles and Q (one
+  // memory round trip); the loop rotates later tiles from the table slot.
+  uint4 ptab[2][NKW_HI][2];
+  auto fetch_direct = [&](int u) {
+    const int k0u = tile_k0(min(u, n_tiles - 1));
+#pragma unroll
+    for (int m = 0; m < NKW_HI; ++m) {
+      if (m < nkw) {
+        const int kp = wave + NW * m;
+        const int row = min(k_pos0 + k0u + L::KROWS_I * kp + kjr, rope_last);
+        const uint32_t* tr = p.rcsb + (long long)row * (D / 2) + 8 * kc;
+        ptab[u][m][0] = ld16(tr);
+        ptab[u][m][1] = ld16(tr + 4);
+      }
+    }
+  };
   auto rotate_direct = [&](int u) {
     char* slot = smem + (u % RING) * L::KSLOT;
-    const int k0u = tile_k0(min(u, n_tiles - 1));
 #pragma unroll
     for (int m = 0; m < NKW_HI; ++m) {
       const int kp = wave + NW * m;
       if (m < nkw) {
-        const int row = min(k_pos0 + k0u + L::KROWS_I * kp + kjr, rope_last);
-        const uint32_t* tr = p.rcsb + (long long)row * (D / 2) + 8 * kc;
-        const uint4 t0 = ld16(tr), t1 = ld16(tr + 4);
+        const uint4 t0 = ptab[u][m][0], t1 = ptab[u][m][1];
         char* lo_p = slot + kp * 1024 + lane * 16;
         char* hi_p = lo_p + L::KHI;
         uint4 lo = ld16(lo_p), hi = ld16(hi_p);
@@ -360,18 +372,35 @@ fwd_bf16_kernel(const AttnParams p) {
   // The softmax scale (times log2 e, for exp2) is applied here, in fp32,
   // before the single bf16 rounding of the rotated row, so the score MFMAs
   // produce exp2-domain scores directly.
+  // Issued in two parts so that the loads share the prologue's single wait
+  // with the first tiles: load_q_issue() fetches the row chunks and their
+  // angles (packed fp16 (cos, sin) words: their 2^-12 rounding is far below
+  // the bf16 rounding of the rotated row, at half the bytes of fp32 cos and
+  // sin), load_q_finish() rotates and scales them in fp32.
   bf16x8 qf[NKK];
-  auto load_q = [&]() {
+  uint4 qlo[NKK / 2], qhi[NKK / 2];
+  uint4 qa[ROPE ? NKK / 2 : 1], qb2[ROPE ? NKK / 2 : 1];
+  auto load_q_issue = [&]() {
     const __bf16* qrow = qb + (long long)iq * p.qsn;
-    const float qscale = p.scale_log2;
 #pragma unroll
     for (int kk = 0; kk < NKK / 2; ++kk) {
       const int d0 = 16 * kk + 8 * lh;
-      uint4 lo = ld16(qrow + d0);
-      uint4 hi = ld16(qrow + d0 + D / 2);
+      qlo[kk] = ld16(qrow + d0);
+      qhi[kk] = ld16(qrow + d0 + D / 2);
       if (ROPE) {
-        const long long row = (long long)(p.q_pos0 + iq) * (D / 2) + d0;
-        rope_rotate_bf16x8(lo, hi, ld_f8(rcos + row), ld_f8(rsin + row), qscale);
+        const uint32_t* row = p.rcs + (long long)(p.q_pos0 + iq) * (D / 2) + d0;
+        qa[kk] = ld16(row);
+        qb2[kk] = ld16(row + 4);
+      }
+    }
+  };
+  auto load_q_finish = [&]() {
+    const float qscale = p.scale_log2;
+#pragma unroll
+    for (int kk = 0; kk < NKK / 2; ++kk) {
+      uint4 lo = qlo[kk], hi = qhi[kk];
+      if (ROPE) {
+        rope_rotate_bf16x8_h(lo, hi, qa[kk], qb2[kk], qscale);
       } else {
         lo = scale_bf16x8(lo, qscale);
         hi = scale_bf16x8(hi, qscale);
@@ -553,19 +582,29 @@ fwd_bf16_kernel(const AttnParams p) {
     // its wave issued in its previous vector cluster; with four-slot rings
     // every slot is refilled only after both halves have read it.
     const bool m_first = wave < NW / 2;
+    // Tiles past the list are never loaded here (every vector cluster waits
+    // for all of its wave's loads, so no fixed instruction count is needed):
+    // their scores are masked out entirely and they never meet V.
     if (n > 0) {
-      issue_group(0, 0, 0, false, true);  // K(0), V(0)
-      issue_group(1, 1, 1, false, true);  // K(1), V(1)
-      issue_group(2, 2, 2, true, false);  // K(2) and its table entries
+      issue_group(0, 0, 0, false, true);                  // K(0), V(0)
+      if (n > 1) issue_group(1, 1, 1, false, true);       // K(1), V(1)
+      if (n > 2) issue_group(2, 2, 2, true, false);       // K(2) and its table entries
+      if (ROPE) {
+        fetch_direct(0);
+        fetch_direct(1);
+      }
     }
-    load_q();
+    load_q_issue();
     if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
     vmcnt_wait<0>();
+    // K(0) and K(1), which every wave reads, are rotated before the barrier;
+    // the private Q rotation and the first tile follow it.
     if (n > 0 && ROPE) {
       rotate_direct(0);
       rotate_direct(1);
     }
     __syncthreads();
+    load_q_finish();
     if (n > 0) first_tile();
 
     constexpr int NST = 2 * NKK;  // MFMA pairs per cluster (S step + PV step)
@@ -603,12 +642,17 @@ fwd_bf16_kernel(const AttnParams p) {
     auto vcluster = [&](int t, int st, bool has_s, bf16x8 (&pf_next)[4]) {
       vmcnt_wait<0>();
       const Group g = make_group(t + 3, t + 3, t + 2);
+      const bool k_live = t + 3 < n, v_live = t + 2 < n;
       // K(t+3) and V(t+2) first: their slots were last read two steps ago.
+      if (k_live) {
 #pragma unroll
-      for (int i = 0; i < 2 * NKW_HI; ++i)
-        if (i < 2 * nkw) dma_item(g, i);
+        for (int i = 0; i < 2 * NKW_HI; ++i)
+          if (i < 2 * nkw) dma_item(g, i);
+      }
+      if (v_live) {
 #pragma unroll
-      for (int j = 0; j < NVW; ++j) dma_item(g, (2 + TPK) * nkw + j);
+        for (int j = 0; j < NVW; ++j) dma_item(g, (2 + TPK) * nkw + j);
+      }
       // Operands of the rotation of K(t+2).
       char* kslot2 = smem + ((t + 2) % RING) * L::KSLOT;
       const char* tsl = smem + L::T_OFF + lane * 16;
@@ -625,14 +669,6 @@ fwd_bf16_kernel(const AttnParams p) {
           }
         }
       }
-      if (ROPE) {
-        // Table entries of K(t+3) go into the slot just read: wait for those
-        // reads, then issue (the exponentials below cover the latency).
-        lgkmcnt_wait<0>();
-#pragma unroll
-        for (int i = 2 * NKW_HI; i < (2 + TPK) * NKW_HI; ++i)
-          if (i - 2 * NKW_HI < TPK * nkw) dma_item(g, i - 2 * NKW_HI + 2 * nkw);
-      }
       if (has_s) {
         const int k0s = tile_k0(min(st, n - 1));
         mask_scores(st, sn);
@@ -643,6 +679,14 @@ fwd_bf16_kernel(const AttnParams p) {
         to_frags(pw, pf_next);
       }
       if (ROPE) {
+        // Table entries of K(t+3) go into the slot read above: those reads
+        // completed during the softmax; wait for them, then issue.
+        lgkmcnt_wait<0>();
+        if (k_live) {
+#pragma unroll
+          for (int i = 2 * NKW_HI; i < (2 + TPK) * NKW_HI; ++i)
+            if (i - 2 * NKW_HI < TPK * nkw) dma_item(g, i - 2 * NKW_HI + 2 * nkw);
+        }
 #pragma unroll
         for (int m = 0; m < NKW_HI; ++m) {
           const int kp = wave + NW * m;
@@ -682,9 +726,13 @@ fwd_bf16_kernel(const AttnParams p) {
     if (n > 0) {
       issue_group(0, 0, 0, false, true);
       issue_group(1, 1, 1, false, false);
+      if (ROPE) {
+        fetch_direct(0);
+        fetch_direct(1);
+      }
     }
     // Q and the slope load while the first tiles arrive.
-    load_q();
+    load_q_issue();
     if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
     vmcnt_wait<0>();
     if (n > 0) {
@@ -697,6 +745,7 @@ fwd_bf16_kernel(const AttnParams p) {
       issue_group(3, 2, 2, true, true);
     }
     __syncthreads();
+    load_q_finish();
     if (n > 0) first_tile();
     // Iteration 0 refills K slot 0, which every wave has just read for S(0).
     __syncthreads();

@@ -86,16 +86,17 @@ typedef struct attnfuse_variant_desc {
    * applies the rotation in-kernel to Q (once) and to every K tile.  The
    * tables hold cos / sin of position * theta^(-2r/D), row-major
    * [rope_table_len][D/2], 16-byte aligned:
-   *   rope_cos / rope_sin: fp32.  Read by attnfuse_fwd (both dtypes: Q is
-   *     rotated in fp32 before its single bf16 rounding) and
-   *     attnfuse_prerotate.
-   *   rope_cs_bf16: one 32-bit word per entry holding the bf16 pair (cos in
-   *     bits 0-15, sin in bits 16-31).  Read by attnfuse_fwd with dtype
-   *     ATTNFUSE_BF16, which rotates each K tile with two bf16 dot products
-   *     per element (the table rounding, at most 2^-9 relative, is of the
-   *     order of the bf16 rounding of the rotated keys themselves).
-   *   rope_cs_f16: the same pairs in fp16 (rounding at most 2^-12).  Read by
+   *   rope_cos / rope_sin: fp32.  Read by attnfuse_fwd with dtype
+   *     ATTNFUSE_FP32 and by attnfuse_prerotate.
+   *   rope_cs_f16: one 32-bit word per entry holding the fp16 pair (cos in
+   *     bits 0-15, sin in bits 16-31; rounding at most 2^-12, well below the
+   *     bf16 rounding of the rotated vectors).  Read by attnfuse_fwd with
+   *     dtype ATTNFUSE_BF16 (the Q rotation, in fp32 arithmetic) and by
    *     attnfuse_decode.
+   *   rope_cs_bf16: the same pairs rounded to bf16 (at most 2^-9 relative,
+   *     the order of the bf16 rounding of the rotated keys themselves).  Read
+   *     by attnfuse_fwd with dtype ATTNFUSE_BF16 (the K rotation, fp32
+   *     arithmetic on the exact bf16 values).
    * Build them with attnfuse_rope_table.  Every position used
    * (q_pos0 + Nq - 1, k_pos0 + Nk - 1) must be below rope_table_len.
    * rope_theta records the base the tables were built with.  A table an
