@@ -268,6 +268,35 @@ def test_decode_variants_small(kw):
     check_close(host(out), ref, "bf16", f"decode {kw}")
 
 
+def test_decode_shared_workspace_and_head_groups():
+    """One workspace, filled with garbage first, reused by calls of different
+    shapes and split counts; GQA groups wider than 32 q-heads (two head
+    groups per kv-head, the second one partial) and D = 64.  Every call must
+    match the oracle."""
+    rng = np.random.default_rng(11)
+    cases = [  # B, Hq, Hkv, Nk, D, splits
+        (2, 40, 1, 2000, 128, 64),
+        (1, 16, 2, 777, 64, 7),
+        (2, 40, 1, 2000, 128, 100),
+        (1, 48, 1, 300, 64, 33),
+        (1, 16, 2, 777, 64, 7),
+    ]
+    need = max(B * Hq * sp * (D + 2) * 4 for B, Hq, Hkv, Nk, D, sp in cases)
+    ws = torch.from_numpy(rng.integers(0, 2**31, need // 4, dtype=np.int32)).cuda().view(torch.float32)
+    for B, Hq, Hkv, Nk, D, sp in cases:
+        (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16(s, rng) for s in
+                                     ((B, Hq, 1, D), (B, Hkv, Nk, D), (B, Hkv, Nk, D)))
+        kw = dict(rope_theta=1e4, q_pos0=Nk)
+        qd, kd, vd = to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16")
+        assert af.decode_workspace_size(qd, kd, sp) <= need
+        log(f"case decode shared workspace B={B} Hq={Hq} Hkv={Hkv} Nk={Nk} D={D} splits={sp}")
+        out, lse = af.decode(qd, kd, vd, num_splits=sp, return_lse=True, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        ref, rlse = oracle.attention(q, k, v, **kw)
+        check_close(host(out), ref, "bf16", f"decode shared ws {B, Hq, Hkv, Nk, D, sp}")
+        check_lse(host(lse), rlse, 2e-2, f"decode shared ws {B, Hq, Hkv, Nk, D, sp}")
+
+
 def test_fwd_single_query_uses_decode_and_matches_prefill_kernel():
     rng = np.random.default_rng(6)
     (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16(s, rng) for s in
