@@ -229,6 +229,13 @@ __device__ __forceinline__ void dma16_off(uint32_t lds_base, const void* base, u
                : "memory", "m0");
 }
 
+// 16-byte LDS read at a byte address (constant parts of the address fold
+// into the instruction's offset field).
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4*)(size_t)addr);
+}
+
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Issued through the builtin so
 // the compiler's own wait bookkeeping sees it.

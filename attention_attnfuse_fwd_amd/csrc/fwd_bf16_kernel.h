@@ -267,6 +267,18 @@ fwd_bf16_kernel(const AttnParams p) {
     g.vslot = lds0 + L::V_OFF + (uint32_t)(uv % RING) * L::VSLOT;
     return g;
   };
+  // Per-lane DMA offsets of unclamped rows, fixed for the whole loop; a row
+  // clamp min(row, rmax) * stride + col becomes min(offset, rmax * stride + col).
+  uint32_t koff[NKW_HI], vdoff[NVW], vc16[NVW];
+#pragma unroll
+  for (int m = 0; m < NKW_HI; ++m) koff[m] = (uint32_t)(L::KROWS_I * (wave + NW * m) + kjr) * ksn2 + kcol;
+#pragma unroll
+  for (int j = 0; j < NVW; ++j) {
+    const int key = L::VROWS_I * (wave + NW * j) + vrow;
+    vc16[j] = 16u * (uint32_t)((lane % L::CPR) ^ vswz<D>(key));
+    vdoff[j] = (uint32_t)key * vsn2 + vc16[j];
+  }
+  const uint32_t toff = (uint32_t)kjr * (uint32_t)L::ROWB + tcol;
   // Instruction i of a group, in issue order: K low / high per pair, then
   // (RoPE) two table instructions per pair, then V.
   const uint32_t tslot = lds0 + L::T_OFF;
@@ -274,7 +286,10 @@ fwd_bf16_kernel(const AttnParams p) {
     if (i < 2 * nkw) {
       const int m = i / 2, hi = i % 2;
       const int kp = wave + NW * m;
-      const uint32_t off = (uint32_t)min(L::KROWS_I * kp + kjr, g.rmax_k) * ksn2 + kcol;
+      // min(row, rmax) * ksn2 + kcol, with the row part precomputed (rows
+      // are below 64, so the clamp bound is taken at most 63 rows: no
+      // 32-bit overflow).
+      const uint32_t off = min(koff[m], (uint32_t)min(g.rmax_k, 63) * ksn2 + kcol);
       dma16_off(g.kslot + (hi ? L::KHI : 0) + kp * 1024, hi ? g.kt + D / 2 : g.kt, off);
     } else if (i < (2 + TPK) * nkw) {
       const int m = (i - 2 * nkw) / 2, x = (i - 2 * nkw) % 2;
@@ -283,14 +298,14 @@ fwd_bf16_kernel(const AttnParams p) {
       // table only belong to masked keys and re-read its last row.
       const int prow = k_pos0 + g.k0t + L::KROWS_I * kp;
       const int row0 = min(prow, rope_last);
-      const uint32_t r = (uint32_t)min(kjr, rope_last - row0);
+      const uint32_t off = min(toff, (uint32_t)min(rope_last - row0, 63) * (uint32_t)L::ROWB + tcol);
       dma16_off(tslot + (uint32_t)kp * L::TPAIR + 1024u * x, p.rcsb + (long long)row0 * (D / 2),
-                r * (uint32_t)L::ROWB + tcol + 16u * x);
+                off + 16u * x);
     } else {
-      const int vi = wave + NW * (i - (2 + TPK) * nkw);
-      const int key = L::VROWS_I * vi + vrow;
-      const uint32_t c = (uint32_t)((lane % L::CPR) ^ vswz<D>(key));
-      dma16_off(g.vslot + vi * 1024, g.vt, (uint32_t)min(key, g.rmax_v) * vsn2 + 16u * c);
+      const int j = i - (2 + TPK) * nkw;
+      const int vi = wave + NW * j;
+      const uint32_t off = min(vdoff[j], (uint32_t)min(g.rmax_v, 63) * vsn2 + vc16[j]);
+      dma16_off(g.vslot + vi * 1024, g.vt, off);
     }
   };
   // A whole group at once (prologue); with_v = false issues the K part only,
@@ -349,6 +364,10 @@ fwd_bf16_kernel(const AttnParams p) {
     const int half = kk / (NKK / 2), c = 2 * (kk % (NKK / 2)) + lh;
     return *reinterpret_cast<const bf16x8*>(ks + half * L::KHI + (32 * st + lq) * D + 16 * (c ^ ksw));
   };
+  // Lane part of the K fragment address for chunk column c = kk % (NKK/2).
+  uint32_t klane[NKK / 2];
+#pragma unroll
+  for (int c = 0; c < NKK / 2; ++c) klane[c] = (uint32_t)(lq * D + 16 * ((2 * c + lh) ^ ksw));
   // V^T fragment (A operand of O^T += V^T P^T) for 16-key step c and d tile
   // dt: MFMA k index 8*lh + e  <->  key 16c + 8*(e/4) + 4*lh + e%4, which is
   // the order of the P^T registers.  Two transposing reads of 4 keys each.
@@ -616,19 +635,36 @@ fwd_bf16_kernel(const AttnParams p) {
     // and the second half's MFMA clusters stretch).
     auto mcluster = [&](int t, const bf16x8 (&pf)[4]) {
       __builtin_amdgcn_s_setprio(1);
-      const char* ks = smem + ((t + 1) % RING) * L::KSLOT;
+      // One VGPR base per K chunk column and per V d tile for this step's
+      // slots; the rest of every operand address is an instruction offset.
+      const uint32_t ks = lds0 + (uint32_t)((t + 1) % RING) * L::KSLOT;
       const uint32_t vs = lds0 + L::V_OFF + (uint32_t)(t % RING) * L::VSLOT;
+      uint32_t kbase[NKK / 2], vbase[NDT];
+#pragma unroll
+      for (int c = 0; c < NKK / 2; ++c) kbase[c] = ks + klane[c];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vbase[dt] = vs + voff[dt];
+      auto kf = [&](int st, int kk) -> bf16x8 {
+        return lds_read16(kbase[kk % (NKK / 2)] + (kk / (NKK / 2)) * L::KHI + 32 * st * D);
+      };
+      auto vf = [&](int c, int dt) -> bf16x8 {
+        const i16x4 r0 = lds_read_tr4(vbase[dt] + c * 32 * D);
+        const i16x4 r1 = lds_read_tr4(vbase[dt] + c * 32 * D + 16 * D);
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        return __builtin_bit_cast(bf16x8, a);
+      };
       bf16x8 afr[PF + 1], vfr[PF + 1];
 #pragma unroll
       for (int k = 0; k < PF; ++k) {
-        afr[k] = k_frag(ks, k & 1, k >> 1);
-        vfr[k] = v_frag(vs, k / NDT, k % NDT);
+        afr[k] = kf(k & 1, k >> 1);
+        vfr[k] = vf(k / NDT, k % NDT);
       }
 #pragma unroll
       for (int k = 0; k < NST; ++k) {
         if (k + PF < NST) {
-          afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
-          vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
+          afr[(k + PF) % (PF + 1)] = kf((k + PF) & 1, (k + PF) >> 1);
+          vfr[(k + PF) % (PF + 1)] = vf((k + PF) / NDT, (k + PF) % NDT);
         }
         sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? minit : sn[k & 1]);
         o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
