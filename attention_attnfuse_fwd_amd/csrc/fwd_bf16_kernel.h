@@ -444,18 +444,41 @@ fwd_bf16_kernel(const AttnParams p) {
       (SCOREMOD && p.bias) ? p.bias + b * p.bsb + h * p.bsh + (long long)iq * p.bsi : nullptr;
   const long long bsj = p.bsj;
 
+  // Dense key lists: tile u starts at key 64 * (t_begin + u), so the tiles
+  // that need no mask (inside the key range and, with a band, wholly inside
+  // it for every row of this wave) form one interval [mlo, mhi], computed
+  // once here instead of per tile.
+  int mlo = 0, mhi = -1;
+  if (!SPARSE) {
+    auto fdiv = [](long long a) -> long long { return a >= 0 ? a / 64 : -((-a + 63) / 64); };
+    long long lo = 0, hi = min((long long)n_tiles - 1, fdiv((long long)Nk - 64) - t_begin);
+    if (has_band) {
+      lo = max(lo, -fdiv(-((long long)band_lo + w_last)) - t_begin);          // k0 - w_last >= band_lo
+      hi = min(hi, fdiv((long long)band_hi + w0 - 63) - t_begin);             // k0 + 63 - w0 <= band_hi
+    }
+    if (lo <= hi) {
+      mlo = (int)lo;
+      mhi = (int)hi;
+    }
+  }
   // Masks of S^T tile u in place (only where the tile needs them: the key
   // tail, or the band edge crossing this wave's rows).  A tile past the list
   // (the last iteration's look-ahead) is masked out entirely.
   auto mask_scores = [&](int u, f32x16 (&s)[2]) {
     const bool beyond = u >= n_tiles;
-    const int k0 = tile_k0(min(u, n_tiles - 1));
-    bool need_mask = beyond || k0 + 64 > Nk;
-    if (has_band) {
-      const int dmin = k0 - w_last, dmax = k0 + 63 - w0;
-      need_mask |= (dmin < band_lo) | (dmax > band_hi);
+    bool need_mask;
+    if (SPARSE) {
+      const int k0 = tile_k0(min(u, n_tiles - 1));
+      need_mask = beyond || k0 + 64 > Nk;
+      if (has_band) {
+        const int dmin = k0 - w_last, dmax = k0 + 63 - w0;
+        need_mask |= (dmin < band_lo) | (dmax > band_hi);
+      }
+    } else {
+      need_mask = (u < mlo) | (u > mhi);
     }
     if (need_mask) {
+      const int k0 = tile_k0(min(u, n_tiles - 1));
       // Allowed register offsets form one interval [lo_off, hi_off].
       const int jd = k0 + 4 * lh - i;  // j - i at register offset 0
       int lo_off = -kBandInf, hi_off = Nk - 1 - (k0 + 4 * lh);
