@@ -7,9 +7,9 @@
 //   global -> LDS by direct DMA, K four and V three tiles ahead (no
 //   registers held) ->
 //   K rotated in place in LDS two tiles ahead ("4.1 Fused RoPE": each key is
-//   rotated once per workgroup by the thread that loaded it, with two bf16
-//   dot products per element against a precomputed bf16 (cos, sin) table
-//   whose entries the thread fetched into a private LDS slot) ->
+//   rotated once per workgroup by the thread that loaded it, in fp32 on the
+//   exact bf16 values, against a precomputed bf16 (cos, sin) table whose
+//   entries the thread fetched into a private LDS slot) ->
 //   MFMA operands (K row fragments; V read transposed by ds_read_b64_tr_b16).
 // Per tile and wave:  S^T = K' Q'^T (bf16 MFMA, fp32 acc), score mods and
 // masks only where the tile needs them, online softmax ("2 Background /
