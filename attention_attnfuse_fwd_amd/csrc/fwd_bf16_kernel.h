@@ -954,28 +954,42 @@ fwd_bf16_kernel(const AttnParams p) {
     }
     if (t < n) iteration(t, pfa, pfb);
   }
-  // No DMA may land in LDS after the workgroup ends.
+  // No DMA may land in LDS after the workgroup ends, and the epilogue reuses
+  // the ring slots: every wave's loads must have landed first.
   vmcnt_wait<0>();
+  __syncthreads();
 
   // ---- epilogue: O = O^T / l, optional lse ----
+  // A lane holds one query row's values in 8-byte pieces spread over the
+  // row; staged through LDS (rows padded against bank conflicts), they leave
+  // as whole 16-byte chunks of consecutive rows, so each store instruction
+  // writes a few complete rows.
   const float l_tot = ol[0];
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (i < p.Nq) {
-    __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh + (long long)i * p.osn;
+  constexpr int OROW = 2 * D + 16;  // bytes per staged row
+  char* const ost = smem + wave * 32 * OROW;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * lh;
-        uint2 w;
-        w.x = pack_bf16x2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
-        w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d) = w;
-      }
-    if (p.lse && lh == 0)
-      p.lse[((long long)b * p.Hq + h) * p.Nq + i] =
-          l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * dt + 8 * g + 4 * lh;
+      uint2 w;
+      w.x = pack_bf16x2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
+      w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+      *reinterpret_cast<uint2*>(ost + lq * OROW + 2 * d) = w;
+    }
+  constexpr int CPRO = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPRO;  // rows per store instruction
+  __bf16* const obase = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh;
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int row = k * RPI + lane / CPRO, ch = lane % CPRO;
+    const uint4 v = ld16(ost + row * OROW + 16 * ch);
+    if (w0 + row < p.Nq) st16(obase + (long long)(w0 + row) * p.osn + 8 * ch, v);
   }
+  if (i < p.Nq && p.lse && lh == 0)
+    p.lse[((long long)b * p.Hq + h) * p.Nq + i] =
+        l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace attnfuse
