@@ -16,7 +16,7 @@ using attnfuse::kBandInf;
 namespace {
 
 constexpr long long kMaxLen = 1LL << 30;
-constexpr long long kMaxRowStride = 1LL << 24;  // K / V row stride limit of the bf16 prefill (elements)
+constexpr long long kMaxRowStride = 1LL << 24;  // Q / K / V row stride limit of the bf16 prefill (elements)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -171,7 +171,8 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   const bool sparse = d->bs_row_ptr != nullptr;
   const bool bf16 = d->dtype == ATTNFUSE_BF16;
   // The bf16 kernel addresses a 64-key tile with 32-bit offsets.
-  if (bf16 && (d->k_stride[2] >= kMaxRowStride || d->v_stride[2] >= kMaxRowStride))
+  if (bf16 && (d->q_stride[2] >= kMaxRowStride || d->k_stride[2] >= kMaxRowStride ||
+               d->v_stride[2] >= kMaxRowStride))
     return ATTNFUSE_ERR_UNSUPPORTED;
   if (sparse) {
     if (bf16 && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;

@@ -121,7 +121,10 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
   constexpr int NDT = D / 32;  // 32-row tiles of O^T
   constexpr int RING = L::RING;
-  constexpr int LDS_BYTES = L::T_OFF + (ROPE ? L::TSLOT : 0);
+  constexpr int LDS_RING = L::T_OFF + (ROPE ? L::TSLOT : 0);
+  // The ping-pong prologue stages each wave's Q rows (32 rows of 2*D bytes)
+  // in K slot 3, V slots 2 and 3 and one more area of the same size.
+  constexpr int LDS_BYTES = LDS_RING + (NW == 8 ? 128 * D : 0);
   // DMA instructions per wave and tile.  V is spread evenly; K pairs may not
   // be (D = 64 with 8 waves: waves 0..3 take one pair each).
   static_assert(L::NVI % NW == 0, "V instructions must spread evenly over the waves");
@@ -429,6 +432,68 @@ fwd_bf16_kernel(const AttnParams p) {
     }
   };
 
+  // Ping-pong prologue: the wave's 32 Q rows reach a private LDS area by
+  // direct loads in which 16 (D = 128) or 8 lanes cover one whole row, then
+  // come back in fragment layout (chunks XOR-swizzled by row against bank
+  // conflicts); the angles are loaded as before.
+  constexpr int QCPR = D / 8;        // 16-byte chunks per row
+  constexpr int QRPI = 64 / QCPR;    // rows per load instruction
+  constexpr int QAREA = 64 * D;      // bytes per wave (32 rows)
+  const uint32_t qarea = [&]() -> uint32_t {
+    const int a = wave / 2;
+    const uint32_t base = a == 0 ? 3u * L::KSLOT
+                        : a == 1 ? (uint32_t)(L::V_OFF + 2 * L::VSLOT)
+                        : a == 2 ? (uint32_t)(L::V_OFF + 3 * L::VSLOT)
+                                 : (uint32_t)LDS_RING;
+    return lds0 + base + (uint32_t)(wave % 2) * QAREA;
+  }();
+  auto load_q_issue_staged = [&]() {
+    const int wq = min(w0, p.Nq - 1);  // first row of this wave, clamped
+    const __bf16* qw = qb + (long long)wq * p.qsn;
+#pragma unroll
+    for (int m = 0; m < 32 / QRPI; ++m) {
+      const int r = QRPI * m + lane / QCPR;
+      const int c = (lane % QCPR) ^ (r % QCPR);
+      const int rg = min(w0 + r, p.Nq - 1) - wq;
+      dma16_off(qarea + 1024u * m, qw, (uint32_t)(rg * p.qsn + 8 * c) * 2u);
+    }
+    // The angle rows (D/2 words = 2*D bytes each) are read the same whole-
+    // row way, into registers; q_rows_from_lds() reshapes them through the
+    // same area once the Q rows have left it.
+    if (ROPE) {
+#pragma unroll
+      for (int m = 0; m < 32 / QRPI; ++m) {
+        const int r = QRPI * m + lane / QCPR;
+        const uint32_t* row = p.rcs + (long long)(p.q_pos0 + min(w0 + r, p.Nq - 1)) * (D / 2);
+        const uint4 v = ld16(row + 4 * (lane % QCPR));
+        if (m % 2 == 0) qa[m / 2] = v;
+        else qb2[m / 2] = v;
+      }
+    }
+  };
+  auto q_rows_from_lds = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < NKK / 2; ++kk) {
+      const int c = 2 * kk + lh;
+      qlo[kk] = __builtin_bit_cast(uint4, lds_read16(qarea + lq * 2 * D + 16 * (c ^ (lq % QCPR))));
+      qhi[kk] = __builtin_bit_cast(uint4, lds_read16(qarea + lq * 2 * D + 16 * ((c + QCPR / 2) ^ (lq % QCPR))));
+    }
+    if (ROPE) {
+      char* const qs = smem + (qarea - lds0);
+#pragma unroll
+      for (int m = 0; m < 32 / QRPI; ++m) {
+        const int r = QRPI * m + lane / QCPR;
+        st16(qs + r * 2 * D + 16 * ((lane % QCPR) ^ (r % QCPR)), m % 2 == 0 ? qa[m / 2] : qb2[m / 2]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK / 2; ++kk) {
+        const int c = 4 * kk + 2 * lh;
+        qa[kk] = ld16(qs + lq * 2 * D + 16 * (c ^ (lq % QCPR)));
+        qb2[kk] = ld16(qs + lq * 2 * D + 16 * ((c + 1) ^ (lq % QCPR)));
+      }
+    }
+  };
+
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
@@ -636,11 +701,14 @@ fwd_bf16_kernel(const AttnParams p) {
         fetch_direct(1);
       }
     }
-    load_q_issue();
+    load_q_issue_staged();
     if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
     vmcnt_wait<0>();
-    // K(0) and K(1), which every wave reads, are rotated before the barrier;
-    // the private Q rotation and the first tile follow it.
+    // Q rows leave their staging area (K slot 3, V slots 2-3, ...) before
+    // the barrier, after which those slots are refilled.  K(0) and K(1),
+    // which every wave reads, are rotated before the barrier; the private Q
+    // rotation and the first tile follow it.
+    q_rows_from_lds();
     if (n > 0 && ROPE) {
       rotate_direct(0);
       rotate_direct(1);
