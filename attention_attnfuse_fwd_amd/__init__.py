@@ -1,17 +1,17 @@
 """MI355X (gfx950) fused attention forward: RoPE, causal / sliding-window /
 block-sparse masks, ALiBi and additive bias composed into one HIP kernel, plus
-a split-KV decode with a log-sum-exp combine.
+a split-KV decode with a log-sum-exp combine, and the attention backward.
 
 The compute lives in ``libattnfuse.so`` (C ABI in ``include/attnfuse.h``);
 this package only marshals PyTorch tensors and streams into it.
 """
 from ._abi import LIB_PATH, LibraryNotBuilt, VariantDesc, load as load_library  # noqa: F401
-from .ops import (AttnfuseError, BlockMask, block_mask_from_csr, create_block_mask,  # noqa: F401
+from .ops import (AttnfuseError, BlockMask, block_mask_from_csr, bwd, create_block_mask,  # noqa: F401
                   decode, decode_workspace_size, default_num_splits, fwd, prerotate,
                   rope_tables)
 
 __all__ = [
-    "fwd", "decode", "decode_workspace_size", "default_num_splits", "prerotate",
+    "fwd", "bwd", "decode", "decode_workspace_size", "default_num_splits", "prerotate",
     "rope_tables", "create_block_mask", "block_mask_from_csr", "BlockMask", "AttnfuseError",
     "load_library", "LIB_PATH", "LibraryNotBuilt", "VariantDesc",
 ]

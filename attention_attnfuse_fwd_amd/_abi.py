@@ -31,6 +31,8 @@ EXPORTS = (
     "attnfuse_decode",
     "attnfuse_rope_table",
     "attnfuse_prerotate",
+    "attnfuse_bwd_workspace_size",
+    "attnfuse_bwd",
     "attnfuse_status_string",
 )
 
@@ -111,6 +113,10 @@ def load() -> ctypes.CDLL:
     lib.attnfuse_rope_table.restype = ctypes.c_int
     lib.attnfuse_prerotate.argtypes = [P, P, D, ctypes.c_int32, P]
     lib.attnfuse_prerotate.restype = ctypes.c_int
+    lib.attnfuse_bwd_workspace_size.argtypes = [D]
+    lib.attnfuse_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attnfuse_bwd.argtypes = [P, P, P, P, P, P, P, P, P, D, P, ctypes.c_size_t, P]
+    lib.attnfuse_bwd.restype = ctypes.c_int
     lib.attnfuse_status_string.argtypes = [ctypes.c_int]
     lib.attnfuse_status_string.restype = ctypes.c_char_p
     _lib = lib

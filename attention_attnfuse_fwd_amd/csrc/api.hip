@@ -273,6 +273,43 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
   return hip_status(attnfuse::launch_decode_combine(p, d->D, s));
 }
 
+size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc) {
+  if (validate_common(desc) != ATTNFUSE_OK) return 0;
+  const size_t b = (size_t)desc->B * desc->Hq * desc->Nq * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, const attnfuse_variant_desc* desc,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int st = validate_common(desc);
+  if (st != ATTNFUSE_OK) return st;
+  const attnfuse_variant_desc* d = desc;
+  if (d->dtype != ATTNFUSE_BF16 || d->bias || d->bs_row_ptr) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->Nq > 0 && (!q || !out || !dout || !lse || !dq)) return ATTNFUSE_ERR_INVALID;
+  if (d->Nk > 0 && (!k || !v || !dk || !dv)) return ATTNFUSE_ERR_INVALID;
+  if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
+  const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->Nq == 0 && d->Nk == 0) return ATTNFUSE_OK;
+  const size_t need = attnfuse_bwd_workspace_size(d);
+  if (d->Nq > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return ATTNFUSE_ERR_WORKSPACE;
+  AttnParams p = base_params(q, k, v, const_cast<void*>(out), d);
+  p.lse = const_cast<float*>(lse);
+  attnfuse::BwdParams g{};
+  g.dout = static_cast<const __bf16*>(dout);
+  g.delta = static_cast<float*>(workspace);
+  g.dq = static_cast<__bf16*>(dq);
+  g.dk = static_cast<__bf16*>(dk);
+  g.dv = static_cast<__bf16*>(dv);
+  const long long gq = (long long)d->B * d->Hq * ((d->Nq + 127) / 128);
+  const long long gk = (long long)d->B * d->Hkv * ((d->Nk + 127) / 128);
+  if (gq >= (1LL << 31) || gk >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+  return hip_status(attnfuse::launch_bwd(p, g, d->D, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, float* sin_out,
                         uint32_t* cs_f16_out, uint32_t* cs_bf16_out, void* stream) {
   if (!(theta > 0.0) || !isfinite(theta) || D < 2 || D > 1024 || D % 2 || len < 1 ||

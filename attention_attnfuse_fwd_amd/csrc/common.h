@@ -69,6 +69,16 @@ struct AttnParams {
   float* ws;
 };
 
+// Backward pass buffers (the kernels read the forward's q, k, v, out, lse
+// and strides from AttnParams).
+struct BwdParams {
+  const __bf16* dout;  // [B, Hq, Nq, D], strides of out
+  float* delta;        // [B, Hq, Nq] rowsum(dO * O), workspace
+  __bf16* dq;          // strides of q
+  __bf16* dk;          // strides of k
+  __bf16* dv;          // strides of v
+};
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -27,6 +27,9 @@ hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned g
                                hipStream_t stream);
 hipError_t launch_decode_combine(const AttnParams& p, int D, hipStream_t stream);
 
+// Backward: delta, dK / dV and dQ passes on one stream.
+hipError_t launch_bwd(const AttnParams& p, const BwdParams& g, int D, hipStream_t stream);
+
 // RoPE cos / sin tables and the stand-alone pre-rotation pass.
 hipError_t launch_rope_table(double theta, int D, long long len, float* cos_out, float* sin_out,
                              uint32_t* cs_out, uint32_t* csb_out, hipStream_t stream);

@@ -276,6 +276,41 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     return (out, lse) if return_lse else out
 
 
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+        lse: torch.Tensor, *, causal: bool = False, window: int = 0,
+        rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
+        alibi_slopes=None, scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """Attention backward ("4.4 Backward Pass"): returns (dq, dk, dv), the
+    gradients of sum(out * dout) for the forward fwd(q, k, v, ...) computed
+    with the same keyword arguments; ``out`` and ``lse`` are that forward's
+    output and saved statistic (``fwd(..., return_lse=True)``).  bf16; no
+    bias or block mask.  dq / dk / dv have the strides of q / k / v."""
+    _check_inputs(q, k, v)
+    if dout.shape != out.shape:
+        raise ValueError("dout must have the shape of out")
+    if dout.stride() != out.stride():
+        dout = torch.empty_like(out).copy_(dout)
+    if lse.shape != q.shape[:3] or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, Nq]")
+    lse = lse.contiguous()
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    keep = []
+    d = _make_desc(q, k, v, out, scale=scale, causal=causal, window=window,
+                   rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0,
+                   alibi_slopes=alibi_slopes, bias=None, block_mask=None, lse=None, keep=keep)
+    lib = _abi.load()
+    need = int(lib.attnfuse_bwd_workspace_size(ctypes.byref(d)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.attnfuse_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), ctypes.byref(d), _ptr(workspace), nbytes,
+                            _stream(q.device)), "bwd")
+    return dq, dk, dv
+
+
 def prerotate(x: torch.Tensor, *, rope_theta: float, pos0: int = 0, out: Optional[torch.Tensor] = None):
     """RoPE(x) into a new tensor (the separate pre-rotation pass)."""
     if not x.is_cuda:

@@ -196,6 +196,31 @@ int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, fl
 int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* desc,
                        int32_t which, void* stream);
 
+/* Bytes of workspace attnfuse_bwd needs: B * Hq * Nq floats (the row
+ * reductions delta = rowsum(dO * O)), rounded up to 256.  Returns 0 for an
+ * invalid descriptor. */
+size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc);
+
+/* Attention backward ("4.4 Backward Pass": the FlashAttention-2 split into a
+ * row-reduction pass, a key/value-gradient pass and a query-gradient pass,
+ * no atomics): the gradients of sum(out * dout) with respect to q, k and v,
+ * for the forward attnfuse_fwd computes with the same desc.
+ *   q, k, v, out: the forward's inputs and output (bf16, desc's strides);
+ *   dout: gradient of the output, [B, Hq, Nq, D] with out's strides (o_stride);
+ *   lse: the forward's saved statistic [B, Hq, Nq] fp32 (natural log; rows
+ *        with no visible key hold -inf and get zero gradients);
+ *   dq: written with q's strides; dk, dv: written with k's and v's strides
+ *       (with GQA each kv-head's gradient sums over its q-heads);
+ *   workspace: caller-owned device memory of at least
+ *       attnfuse_bwd_workspace_size bytes, 16-byte aligned (else
+ *       ATTNFUSE_ERR_WORKSPACE); its contents on entry do not matter.
+ * Supports bf16 with rope (fp32 cos / sin tables required), causal, window
+ * and alibi; bias, block_sparse and fp32 return ATTNFUSE_ERR_UNSUPPORTED.
+ * All pointers 16-byte aligned.  Runs three kernels on `stream`. */
+int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, const attnfuse_variant_desc* desc,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* attnfuse_status_string(int status);
 

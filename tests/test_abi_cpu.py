@@ -160,6 +160,24 @@ def test_decode_validation(lib):
                            rope_table_len=100), 16, FAKE, ws_need) == _abi.ERR_INVALID
 
 
+def test_bwd_validation(lib):
+    d = _good_desc()
+    need = lib.attnfuse_bwd_workspace_size(ctypes.byref(d))
+    assert need == (d.B * d.Hq * d.Nq * 4 + 255) // 256 * 256
+    call = lambda d, ws, nb, lse=FAKE: lib.attnfuse_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, lse, FAKE, FAKE,
+                                                      FAKE, ctypes.byref(d), ws, nb, None)
+    assert call(d, FAKE, need - 4) == _abi.ERR_WORKSPACE
+    assert call(d, None, need) == _abi.ERR_WORKSPACE
+    assert call(d, FAKE, need, lse=None) == _abi.ERR_INVALID
+    assert call(_good_desc(bias=0x1000), FAKE, need) == _abi.ERR_UNSUPPORTED
+    assert call(_good_desc(dtype=_abi.FP32), FAKE, 10**9) == _abi.ERR_UNSUPPORTED
+    # the backward reads the fp32 cos / sin tables
+    assert call(_good_desc(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_cs_bf16=0x2000,
+                           rope_table_len=10**5), FAKE, need) == _abi.ERR_INVALID
+    assert lib.attnfuse_bwd(ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            ctypes.byref(d), FAKE, need, None) == _abi.ERR_UNSUPPORTED
+
+
 def test_rope_table_and_prerotate_validation(lib):
     assert lib.attnfuse_rope_table(0.0, 64, 10, FAKE, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID
     assert lib.attnfuse_rope_table(1e4, 63, 10, FAKE, FAKE, FAKE, FAKE, None) == _abi.ERR_INVALID

@@ -1,0 +1,77 @@
+"""GPU parity of the attention backward ("4.4 Backward Pass") against the fp64
+oracle backward, through the C ABI, at shapes that span several tiles (128-row
+query blocks, 64-key and 128-key tiles) with ragged tails, for each supported
+mask / score combinator, GQA, position offsets and both head dims.
+
+Tolerance (derived from the arithmetic): every gradient element is a sum of
+products whose MFMA operands are bf16-rounded (Q', K', P, dS: relative error
+2^-9 each) with fp32 accumulation, and the result is rounded to bf16.  The
+errors are relative to the size of the gradients, so the bar is relative to
+the largest reference magnitude: max|err| <= 2e-2 * max|ref| and
+mean|err| <= 2e-3 * max|ref| (the forward's bar, scaled)."""
+import numpy as np
+import pytest
+import torch
+
+import attention_attnfuse_fwd_amd as af
+import oracle
+import workloads
+from gpu_helpers import host, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "rope_causal_d128_gqa": dict(B=1, Hq=4, Hkv=2, Nq=200, Nk=200, D=128, rope_theta=1e4, causal=True),
+    "plain_d128_mha": dict(B=2, Hq=2, Hkv=2, Nq=150, Nk=170, D=128),
+    "window_alibi_d64": dict(B=1, Hq=4, Hkv=4, Nq=260, Nk=260, D=64, causal=True, window=70, alibi=True),
+    "rope_offsets_prefix_d64_gqa8": dict(B=1, Hq=8, Hkv=1, Nq=90, Nk=300, D=64, rope_theta=5e5,
+                                         causal=True, q_pos0=210, k_pos0=0),
+    "noncausal_window_d128": dict(B=1, Hq=2, Hkv=1, Nq=130, Nk=190, D=128, window=40, rope_theta=500.0),
+}
+
+
+def _run(c, seed):
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, Nq, Nk, D = c["B"], c["Hq"], c["Hkv"], c["Nq"], c["Nk"], c["D"]
+    (qb, q), (kb, k), (vb, v), (gb, g) = (workloads.normal_bf16(s, rng) for s in
+                                          ((B, Hq, Nq, D), (B, Hkv, Nk, D), (B, Hkv, Nk, D), (B, Hq, Nq, D)))
+    kw = dict(causal=c.get("causal", False), window=c.get("window", 0), rope_theta=c.get("rope_theta"),
+              q_pos0=c.get("q_pos0", 0), k_pos0=c.get("k_pos0", 0))
+    okw = dict(kw)
+    if c.get("alibi"):
+        sl = workloads.alibi_slopes(Hq)
+        kw["alibi_slopes"] = torch.from_numpy(sl).cuda()
+        okw["alibi_slopes"] = sl.astype(np.float64)
+    qd, kd, vd, gd = (to_dev(x, "bf16") for x in (qb, kb, vb, gb))
+    out, lse = af.fwd(qd, kd, vd, return_lse=True, decode_fast_path=False, **kw)
+    dq, dk, dv = af.bwd(qd, kd, vd, out, gd, lse, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(q, k, v, g, **okw)
+    return (host(dq), host(dk), host(dv)), ref
+
+
+def _check(name, got, ref):
+    for nm, a, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(a)), f"{name} {nm}: non-finite"
+        err = np.abs(a - r)
+        scale = float(np.abs(r).max())
+        where = np.unravel_index(int(err.argmax()), err.shape)
+        log(f"{name} {nm}: max {err.max():.3e} mean {err.mean():.3e} (max|ref| {scale:.3e}) at {where}")
+        assert err.max() <= 2e-2 * scale, (name, nm, float(err.max()), scale)
+        assert err.mean() <= 2e-3 * scale, (name, nm, float(err.mean()), scale)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_matches_oracle(name):
+    log(f"case bwd {name}")
+    got, ref = _run(CASES[name], seed=hash(name) % 1000)
+    _check(name, got, ref)
+
+
+def test_backward_rows_without_keys_get_zero_dq():
+    # causal with the keys placed after the queries: rows 0..2 see no key
+    c = dict(B=1, Hq=2, Hkv=1, Nq=70, Nk=70, D=64, causal=True, q_pos0=0, k_pos0=3)
+    log("case bwd rows without keys")
+    got, ref = _run(c, seed=3)
+    assert np.all(got[0][:, :, :3] == 0.0)
+    _check("rows_without_keys", got, ref)
