@@ -54,27 +54,48 @@ __device__ __forceinline__ uint4 ld_row8(const __bf16* base, long long sn, int r
   return ld16(base + (long long)row * sn + c);
 }
 
-// Loads rows [r0, r0 + R) of a [N, D] bf16 matrix (rows clamped to N - 1)
-// into a padded LDS tile, rotated by RoPE at positions pos0 + row when rope.
+// Rows [r0, r0 + R) of a [N, D] bf16 matrix (rows clamped to N - 1), staged
+// in two steps so the next tile's loads can be in flight while the current
+// one is multiplied: load() reads this thread's share into registers (with
+// the RoPE angles when rope), store() rotates it and writes a padded LDS tile.
 template <int D, int R, int RS>
-__device__ __forceinline__ void stage_rows(__bf16* tile, const __bf16* src, long long sn, int r0,
-                                           int N, bool rope, const AttnParams& p, int pos0) {
-  constexpr int CH = D / 16;  // 8-element chunks per half row
-  for (int u = threadIdx.x; u < R * CH; u += kBwdThreads) {
-    const int row = u / CH, c = u % CH;
-    const int rs = min(r0 + row, N - 1);
-    uint4 lo = ld_row8(src, sn, rs, 8 * c);
-    uint4 hi = ld_row8(src, sn, rs, D / 2 + 8 * c);
-    if (rope) {
-      const int pos = min(pos0 + rs, p.rope_len - 1);
-      const F8 cs = ld_f8(p.rcos + (long long)pos * (D / 2) + 8 * c);
-      const F8 sn8 = ld_f8(p.rsin + (long long)pos * (D / 2) + 8 * c);
-      rope_rotate_bf16x8(lo, hi, cs, sn8);
+struct RowStage {
+  static constexpr int CH = D / 16;                         // chunk pairs per row
+  static constexpr int U = (R * CH + kBwdThreads - 1) / kBwdThreads;
+  uint4 lo[U], hi[U];
+  F8 c[U], s[U];
+  __device__ __forceinline__ void load(const __bf16* src, long long sn, int r0, int N, bool rope,
+                                       const AttnParams& p, int pos0) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int u = threadIdx.x + kBwdThreads * k;
+      if ((R * CH) % kBwdThreads == 0 || u < R * CH) {
+        const int row = u / CH, ch = u % CH;
+        const int rs = min(r0 + row, N - 1);
+        lo[k] = ld_row8(src, sn, rs, 8 * ch);
+        hi[k] = ld_row8(src, sn, rs, D / 2 + 8 * ch);
+        if (rope) {
+          const int pos = min(pos0 + rs, p.rope_len - 1);
+          c[k] = ld_f8(p.rcos + (long long)pos * (D / 2) + 8 * ch);
+          s[k] = ld_f8(p.rsin + (long long)pos * (D / 2) + 8 * ch);
+        }
+      }
     }
-    st16(tile + row * RS + 8 * c, lo);
-    st16(tile + row * RS + D / 2 + 8 * c, hi);
   }
-}
+  __device__ __forceinline__ void store(__bf16* tile, bool rope) {
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int u = threadIdx.x + kBwdThreads * k;
+      if ((R * CH) % kBwdThreads == 0 || u < R * CH) {
+        const int row = u / CH, ch = u % CH;
+        uint4 l = lo[k], h = hi[k];
+        if (rope) rope_rotate_bf16x8(l, h, c[k], s[k]);
+        st16(tile + row * RS + 8 * ch, l);
+        st16(tile + row * RS + D / 2 + 8 * ch, h);
+      }
+    }
+  }
+};
 
 // Register fragments of one row (lane's row) as a B operand over the head
 // dim: f[kk] = row[16 kk + 8 kb .. +7]; rotated when rope (the low and high
@@ -211,11 +232,21 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dq_kernel(const AttnParams
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
   const uint32_t ks_lds = lds_addr(ks);
-  for (int k0 = (j_lo / 64) * 64; j_hi >= j_lo && k0 <= j_hi; k0 += 64) {
+  RowStage<D, 64, RS> kst, vst;
+  const int kt0 = (j_lo / 64) * 64;
+  if (j_hi >= j_lo) {
+    kst.load(kb, p.ksn, kt0, p.Nk, rope, p, p.k_pos0);
+    vst.load(vb, p.vsn, kt0, p.Nk, false, p, 0);
+  }
+  for (int k0 = kt0; j_hi >= j_lo && k0 <= j_hi; k0 += 64) {
     __syncthreads();
-    stage_rows<D, 64, RS>(ks, kb, p.ksn, k0, p.Nk, rope, p, p.k_pos0);
-    stage_rows<D, 64, RS>(vs, vb, p.vsn, k0, p.Nk, false, p, 0);
+    kst.store(ks, rope);
+    vst.store(vs, false);
     __syncthreads();
+    if (k0 + 64 <= j_hi) {  // the next tile's loads overlap this tile's products
+      kst.load(kb, p.ksn, k0 + 64, p.Nk, rope, p, p.k_pos0);
+      vst.load(vb, p.vsn, k0 + 64, p.Nk, false, p, 0);
+    }
     // S^T and dP^T for two 32-key subtiles (lane = query column).
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -299,63 +330,79 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dk[dt] = dv[dt] = f32x16{};
   const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
-  for (int h = kvh * p.G; h < (kvh + 1) * p.G; ++h) {
-    const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qsb + h * p.qsh;
-    const __bf16* dob = g.dout + b * p.osb + h * p.osh;
-    const long long rbase = ((long long)b * p.Hq + h) * p.Nq;
+  // (head, query tile) steps: the group's q-heads one after the other, each
+  // over the query tiles the band allows; the next step's loads are issued
+  // before this step's products.
+  const int qt0 = (i_lo / 32) * 32;
+  const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 32 + 1 : 0;
+  const int nsteps = ntq * p.G;
+  RowStage<D, 32, RS> qst, dst;
+  float lse_r = 0.f, delta_r = 0.f;
+  auto load_step = [&](int t) {
+    const int h = kvh * p.G + t / ntq, q0 = qt0 + 32 * (t % ntq);
+    qst.load(reinterpret_cast<const __bf16*>(p.q) + b * p.qsb + h * p.qsh, p.qsn, q0, p.Nq, rope, p,
+             p.q_pos0);
+    dst.load(g.dout + b * p.osb + h * p.osh, p.osn, q0, p.Nq, false, p, 0);
+    if (threadIdx.x < 32) {
+      const long long rr = ((long long)b * p.Hq + h) * p.Nq + min(q0 + (int)threadIdx.x, p.Nq - 1);
+      lse_r = p.lse[rr];
+      delta_r = g.delta[rr];
+    }
+  };
+  if (nsteps > 0) load_step(0);
+  for (int t = 0; t < nsteps; ++t) {
+    const int h = kvh * p.G + t / ntq, q0 = qt0 + 32 * (t % ntq);
     const float slope2 = p.alibi ? p.alibi[h] * kLog2e : 0.f;
-    for (int q0 = (i_lo / 32) * 32; i_hi >= i_lo && q0 <= i_hi; q0 += 32) {
-      __syncthreads();
-      stage_rows<D, 32, RS>(qs, qb, p.qsn, q0, p.Nq, rope, p, p.q_pos0);
-      stage_rows<D, 32, RS>(dos, dob, p.osn, q0, p.Nq, false, p, 0);
-      if (threadIdx.x < 32) {
-        const int ii = min(q0 + (int)threadIdx.x, p.Nq - 1);
-        lse_s[threadIdx.x] = p.lse[rbase + ii];
-        delta_s[threadIdx.x] = g.delta[rbase + ii];
-      }
-      __syncthreads();
-      // S and dP (32 query rows x the wave's 32 keys; lane = key column).
-      f32x16 s = f32x16{}, dpv = f32x16{};
+    __syncthreads();
+    qst.store(qs, rope);
+    dst.store(dos, false);
+    if (threadIdx.x < 32) {
+      lse_s[threadIdx.x] = lse_r;
+      delta_s[threadIdx.x] = delta_r;
+    }
+    __syncthreads();
+    if (t + 1 < nsteps) load_step(t + 1);
+    // S and dP (32 query rows x the wave's 32 keys; lane = key column).
+    f32x16 s = f32x16{}, dpv = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32(row_frag<RS>(qs, lq, kk), kf[kk], s);
-        dpv = mfma32(row_frag<RS>(dos, lq, kk), vf[kk], dpv);
+    for (int kk = 0; kk < NKK; ++kk) {
+      s = mfma32(row_frag<RS>(qs, lq, kk), kf[kk], s);
+      dpv = mfma32(row_frag<RS>(dos, lq, kk), vf[kk], dpv);
+    }
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t wp[4], wd[4];
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        float pv[2], dsv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = 8 * c + 2 * q2 + e;
+          const int m = 8 * (r / 4) + 4 * lh + r % 4;  // query row within the tile
+          const int ii = q0 + m;
+          const float lse = lse_s[m];
+          bool ok = ii < p.Nq && j < p.Nk && lse != -INFINITY;
+          if (p.has_band) ok = ok && (j - ii >= p.band_lo) && (j - ii <= p.band_hi);
+          float x = s[r] * p.scale_log2 - lse * kLog2e;
+          if (p.alibi) x = __builtin_fmaf(slope2, (float)(j - ii + dpos), x);
+          pv[e] = ok ? fast_exp2(x) : 0.f;
+          dsv[e] = pv[e] * (dpv[r] - delta_s[m]);
+        }
+        wp[q2] = pack_bf16x2(pv[0], pv[1]);
+        wd[q2] = pack_bf16x2(dsv[0], dsv[1]);
       }
-      bf16x8 pf[2], dsf[2];
+      pf[c] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+      dsf[c] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+    }
+    // dV^T += dO^T P,  dK'^T += Q'^T dS.
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        uint32_t wp[4], wd[4];
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          float pv[2], dsv[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int r = 8 * c + 2 * q2 + e;
-            const int m = 8 * (r / 4) + 4 * lh + r % 4;  // query row within the tile
-            const int ii = q0 + m;
-            const float lse = lse_s[m];
-            bool ok = ii < p.Nq && j < p.Nk && lse != -INFINITY;
-            if (p.has_band) ok = ok && (j - ii >= p.band_lo) && (j - ii <= p.band_hi);
-            float x = s[r] * p.scale_log2 - lse * kLog2e;
-            if (p.alibi) x = __builtin_fmaf(slope2, (float)(j - ii + dpos), x);
-            pv[e] = ok ? fast_exp2(x) : 0.f;
-            dsv[e] = pv[e] * (dpv[r] - delta_s[m]);
-          }
-          wp[q2] = pack_bf16x2(pv[0], pv[1]);
-          wd[q2] = pack_bf16x2(dsv[0], dsv[1]);
-        }
-        pf[c] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
-        dsf[c] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+        dv[dt] = mfma32(tr_frag<RS>(dos_lds, 16 * c, 32 * dt), pf[c], dv[dt]);
+        dk[dt] = mfma32(tr_frag<RS>(qs_lds, 16 * c, 32 * dt), dsf[c], dk[dt]);
       }
-      // dV^T += dO^T P,  dK'^T += Q'^T dS.
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          dv[dt] = mfma32(tr_frag<RS>(dos_lds, 16 * c, 32 * dt), pf[c], dv[dt]);
-          dk[dt] = mfma32(tr_frag<RS>(qs_lds, 16 * c, 32 * dt), dsf[c], dk[dt]);
-        }
-    }
   }
   if (j < p.Nk) {
     __bf16* dkd = g.dk + b * p.ksb + kvh * p.ksh + (long long)j * p.ksn;
