@@ -273,10 +273,26 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
   return hip_status(attnfuse::launch_decode_combine(p, d->D, s));
 }
 
+namespace {
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+// Workspace of the backward: delta [B, Hq, Nq] fp32, then with RoPE the
+// rotated copies Q' [B, Hq, Nq, D] and K' [B, Hkv, Nk, D] in bf16.
+size_t bwd_delta_bytes(const attnfuse_variant_desc* d) {
+  return round256((size_t)d->B * d->Hq * d->Nq * sizeof(float));
+}
+// The rotated copies are only read when there are both queries and keys.
+bool bwd_rotates(const attnfuse_variant_desc* d) { return d->rope && d->Nq > 0 && d->Nk > 0; }
+size_t bwd_qrot_bytes(const attnfuse_variant_desc* d) {
+  return bwd_rotates(d) ? round256((size_t)d->B * d->Hq * d->Nq * d->D * 2) : 0;
+}
+size_t bwd_krot_bytes(const attnfuse_variant_desc* d) {
+  return bwd_rotates(d) ? round256((size_t)d->B * d->Hkv * d->Nk * d->D * 2) : 0;
+}
+}  // namespace
+
 size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc) {
   if (validate_common(desc) != ATTNFUSE_OK) return 0;
-  const size_t b = (size_t)desc->B * desc->Hq * desc->Nq * sizeof(float);
-  return (b + 255) / 256 * 256;
+  return bwd_delta_bytes(desc) + bwd_qrot_bytes(desc) + bwd_krot_bytes(desc);
 }
 
 int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -294,7 +310,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
     if (x && !aligned16(x)) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->Nq == 0 && d->Nk == 0) return ATTNFUSE_OK;
   const size_t need = attnfuse_bwd_workspace_size(d);
-  if (d->Nq > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return ATTNFUSE_ERR_WORKSPACE;
   AttnParams p = base_params(q, k, v, const_cast<void*>(out), d);
   p.lse = const_cast<float*>(lse);
@@ -304,9 +320,31 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   g.dq = static_cast<__bf16*>(dq);
   g.dk = static_cast<__bf16*>(dk);
   g.dv = static_cast<__bf16*>(dv);
+  char* ws = static_cast<char*>(workspace);
+  if (bwd_rotates(d)) {
+    g.qrot = reinterpret_cast<__bf16*>(ws + bwd_delta_bytes(d));
+    g.krot = reinterpret_cast<__bf16*>(ws + bwd_delta_bytes(d) + bwd_qrot_bytes(d));
+    g.qr = g.qrot;
+    g.kr = g.krot;
+    g.qr_sb = (long long)d->Hq * d->Nq * d->D;
+    g.qr_sh = (long long)d->Nq * d->D;
+    g.kr_sb = (long long)d->Hkv * d->Nk * d->D;
+    g.kr_sh = (long long)d->Nk * d->D;
+    g.qr_sn = g.kr_sn = d->D;
+  } else {
+    g.qr = static_cast<const __bf16*>(q);
+    g.kr = static_cast<const __bf16*>(k);
+    g.qr_sb = d->q_stride[0]; g.qr_sh = d->q_stride[1]; g.qr_sn = d->q_stride[2];
+    g.kr_sb = d->k_stride[0]; g.kr_sh = d->k_stride[1]; g.kr_sn = d->k_stride[2];
+  }
   const long long gq = (long long)d->B * d->Hq * ((d->Nq + 127) / 128);
   const long long gk = (long long)d->B * d->Hkv * ((d->Nk + 127) / 128);
-  if (gq >= (1LL << 31) || gk >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+  // The rotation and row-reduction passes use at most one 256-thread block
+  // per 16 rows (D = 128 row reduction).
+  const long long row_blocks = (long long)d->B * (d->Hq > d->Hkv ? d->Hq : d->Hkv) *
+                               (d->Nq > d->Nk ? d->Nq : d->Nk) / 16 + 1;
+  if (gq >= (1LL << 31) || gk >= (1LL << 31) || row_blocks >= (1LL << 31))
+    return ATTNFUSE_ERR_UNSUPPORTED;
   return hip_status(attnfuse::launch_bwd(p, g, d->D, reinterpret_cast<hipStream_t>(stream)));
 }
 

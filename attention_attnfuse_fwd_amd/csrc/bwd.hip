@@ -1,19 +1,26 @@
 // Attention backward ("4.4 Backward Pass"), the FlashAttention-2 split into
-// three passes, none of which needs atomics:
+// passes none of which needs atomics:
+//   0. with RoPE: Q' = RoPE(Q) and K' = RoPE(K) into the workspace, rounded
+//      once to bf16 (the forward rounds its rotated operands the same way);
+//      the three passes below read them many times over
 //   1. delta[b, h, i] = sum_d dO[i, d] O[i, d]            (row reduction)
 //   2. per (b, kv-head, block of 128 keys): dK and dV, looping over the
-//      q-heads of the group and the query tiles the masks allow
-//   3. per (b, q-head, block of 128 query rows): dQ, looping over key tiles
+//      q-heads of the group and the 64-row query tiles the masks allow
+//   3. per (b, q-head, block of 128 query rows): dQ, looping over 64-key tiles
 // Probabilities are re-derived tile by tile from the forward's saved
 // L = m + ln l:  P = exp(S - L),  dS = P (dP - delta),  dQ' = scale dS K',
 // dK' = scale dS^T Q',  dV = P^T dO; the RoPE gradients rotate dQ' and dK'
 // back by the negative angle (the rotation is orthogonal).
 //
-// All products run on bf16 MFMA (32x32x16, fp32 accumulate) with the
-// operands the forward uses: rotated Q and K rounded once to bf16, P and dS
-// rounded to bf16.  Tiles are staged through padded row-major LDS; the
-// transposed operands (dO^T, Q'^T, K'^T) are read with ds_read_b64_tr_b16.
-// This first version loads each tile synchronously (no prefetch).
+// All products run on bf16 MFMA (32x32x16, fp32 accumulate) with P and dS
+// rounded to bf16.  Tiles are staged through padded row-major LDS, double
+// buffered: the next tile's global loads are in flight during the current
+// tile's products and one barrier separates tiles.  The transposed operands
+// (dO^T, Q'^T, K'^T) are read with ds_read_b64_tr_b16.  Each wave classifies
+// its part of a tile as fully visible (no mask arithmetic), fully masked
+// (skipped) or partial (per-element band and bound tests).
+#include <climits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -56,67 +63,38 @@ __device__ __forceinline__ uint4 ld_row8(const __bf16* base, long long sn, int r
 
 // Rows [r0, r0 + R) of a [N, D] bf16 matrix (rows clamped to N - 1), staged
 // in two steps so the next tile's loads can be in flight while the current
-// one is multiplied: load() reads this thread's share into registers (with
-// the RoPE angles when rope), store() rotates it and writes a padded LDS tile.
+// one is multiplied: load() reads this thread's share into registers,
+// store() writes it to a padded LDS tile.
 template <int D, int R, int RS>
 struct RowStage {
-  static constexpr int CH = D / 16;                         // chunk pairs per row
-  static constexpr int U = (R * CH + kBwdThreads - 1) / kBwdThreads;
-  uint4 lo[U], hi[U];
-  F8 c[U], s[U];
-  __device__ __forceinline__ void load(const __bf16* src, long long sn, int r0, int N, bool rope,
-                                       const AttnParams& p, int pos0) {
+  static constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  static constexpr int U = (R * CPR + kBwdThreads - 1) / kBwdThreads;
+  uint4 x[U];
+  __device__ __forceinline__ void load(const __bf16* src, long long sn, int r0, int N) {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int u = threadIdx.x + kBwdThreads * k;
-      if ((R * CH) % kBwdThreads == 0 || u < R * CH) {
-        const int row = u / CH, ch = u % CH;
-        const int rs = min(r0 + row, N - 1);
-        lo[k] = ld_row8(src, sn, rs, 8 * ch);
-        hi[k] = ld_row8(src, sn, rs, D / 2 + 8 * ch);
-        if (rope) {
-          const int pos = min(pos0 + rs, p.rope_len - 1);
-          c[k] = ld_f8(p.rcos + (long long)pos * (D / 2) + 8 * ch);
-          s[k] = ld_f8(p.rsin + (long long)pos * (D / 2) + 8 * ch);
-        }
-      }
+      if ((R * CPR) % kBwdThreads == 0 || u < R * CPR)
+        x[k] = ld_row8(src, sn, min(r0 + u / CPR, N - 1), 8 * (u % CPR));
     }
   }
-  __device__ __forceinline__ void store(__bf16* tile, bool rope) {
+  __device__ __forceinline__ void store(__bf16* tile) const {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int u = threadIdx.x + kBwdThreads * k;
-      if ((R * CH) % kBwdThreads == 0 || u < R * CH) {
-        const int row = u / CH, ch = u % CH;
-        uint4 l = lo[k], h = hi[k];
-        if (rope) rope_rotate_bf16x8(l, h, c[k], s[k]);
-        st16(tile + row * RS + 8 * ch, l);
-        st16(tile + row * RS + D / 2 + 8 * ch, h);
-      }
+      if ((R * CPR) % kBwdThreads == 0 || u < R * CPR) st16(tile + (u / CPR) * RS + 8 * (u % CPR), x[k]);
     }
   }
 };
 
 // Register fragments of one row (lane's row) as a B operand over the head
-// dim: f[kk] = row[16 kk + 8 kb .. +7]; rotated when rope (the low and high
-// halves of the row sit in f[kk] and f[kk + D/32]).
+// dim: f[kk] = row[16 kk + 8 kb .. +7].
 template <int D>
 __device__ __forceinline__ void row_frags(bf16x8 (&f)[D / 16], const __bf16* src, long long sn,
-                                          int row, bool rope, const AttnParams& p, int pos) {
+                                          int row) {
   const int kb = (threadIdx.x & 63) >> 5;
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    const int d0 = 16 * kk + 8 * kb;
-    uint4 lo = ld_row8(src, sn, row, d0);
-    uint4 hi = ld_row8(src, sn, row, D / 2 + d0);
-    if (rope) {
-      const int ps = min(pos, p.rope_len - 1);
-      rope_rotate_bf16x8(lo, hi, ld_f8(p.rcos + (long long)ps * (D / 2) + d0),
-                         ld_f8(p.rsin + (long long)ps * (D / 2) + d0));
-    }
-    f[kk] = __builtin_bit_cast(bf16x8, lo);
-    f[kk + D / 32] = __builtin_bit_cast(bf16x8, hi);
-  }
+  for (int kk = 0; kk < D / 16; ++kk) f[kk] = __builtin_bit_cast(bf16x8, ld_row8(src, sn, row, 16 * kk + 8 * kb));
 }
 
 // Un-rotate (rotate by the negative angle) an accumulator held as
@@ -157,7 +135,88 @@ __device__ __forceinline__ void store_grad_row(__bf16* dst, const f32x16 (&acc)[
     }
 }
 
+// Workgroup -> (unit, block rank) with rank 0 (the longest block under a
+// causal band) dispatched first for every unit, and, when the units split
+// evenly over the 8 XCDs (consecutive workgroup ids go to consecutive XCDs),
+// each XCD's workgroups on a contiguous range of units so that the units'
+// shared operands stay in that XCD's L2.
+__device__ __forceinline__ void bwd_tile_of(int nunits, int& unit, int& rank) {
+  const int id = blockIdx.x;
+  if (nunits % 8 == 0) {
+    const int upx = nunits / 8, m = id / 8;
+    unit = (id % 8) * upx + m % upx;
+    rank = m / upx;
+  } else {
+    unit = id % nunits;
+    rank = id / nunits;
+  }
+}
+
+// P = exp2(S scale log2e - L log2e) and dS = P (dP - delta) for one 32x32
+// block held as accumulators s (scores) and dp, packed to bf16 as two
+// 16-row MFMA B operands (chunk c holds the accumulator rows 8c .. 8c+7).
+// Accumulator row r of the lane is block row row0 + 8 (r/4) + 4 kb + r%4.
+// ROWQ: block rows are queries and the lane's column is key `col`; else
+// block rows are keys and the lane's column is query `col`.  L2[r] holds
+// L log2e of the row's query (+inf for rows without keys, so that P = 0),
+// Dl[r] its delta.  MASK applies the key bound and the band per element.
+template <bool MASK, bool ALIBI, bool ROWQ, bool WANTP>
+__device__ __forceinline__ void p_ds(const f32x16& s, const f32x16& dp, const float (&L2)[16],
+                                     const float (&Dl)[16], int row0, int col, const AttnParams& p,
+                                     float slope2, int dpos, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
+  const int kb = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint32_t wp[4], wd[4];
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      float pv[2], dsv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 8 * c + 2 * q2 + e;
+        const int row = row0 + 8 * (r / 4) + 4 * kb + r % 4;
+        const int i = ROWQ ? row : col, j = ROWQ ? col : row;
+        float x = __builtin_fmaf(s[r], p.scale_log2, -L2[r]);
+        if (ALIBI) x = __builtin_fmaf(slope2, (float)(j - i + dpos), x);
+        float pr = fast_exp2(x);
+        if (MASK) {
+          const bool ok = (j < p.Nk) & (j - i >= p.band_lo) & (j - i <= p.band_hi);
+          pr = ok ? pr : 0.f;
+        }
+        pv[e] = pr;
+        dsv[e] = pr * (dp[r] - Dl[r]);
+      }
+      if (WANTP) wp[q2] = pack_bf16x2(pv[0], pv[1]);
+      wd[q2] = pack_bf16x2(dsv[0], dsv[1]);
+    }
+    if (WANTP) pf[c] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+    dsf[c] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+  }
+}
+
 }  // namespace
+
+// ---- pass 0: Q' / K' = RoPE(x) into a contiguous [B][H][N][D] copy ----
+template <int D>
+__global__ void __launch_bounds__(256) bwd_rotate_kernel(const __bf16* x, long long sb, long long sh,
+                                                         long long sn, int H, int N, long long rows,
+                                                         int pos0, const AttnParams p, __bf16* y) {
+  constexpr int CH = D / 16;  // chunk pairs per row
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * CH) return;
+  const int c = (int)(idx % CH);
+  const long long row = idx / CH;
+  const int n = (int)(row % N);
+  const long long bh = row / N;
+  const int hh = (int)(bh % H), bb = (int)(bh / H);
+  const __bf16* src = x + bb * sb + hh * sh + n * sn;
+  uint4 lo = ld16(src + 8 * c), hi = ld16(src + D / 2 + 8 * c);
+  const long long t = (long long)min(pos0 + n, p.rope_len - 1) * (D / 2) + 8 * c;
+  rope_rotate_bf16x8(lo, hi, ld_f8(p.rcos + t), ld_f8(p.rsin + t));
+  __bf16* dst = y + row * D;
+  st16(dst + 8 * c, lo);
+  st16(dst + D / 2 + 8 * c, hi);
+}
 
 // ---- pass 1: delta = rowsum(dO * O) ----
 template <int D>
@@ -187,38 +246,40 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const AttnParams p, cons
 }
 
 // ---- pass 3: dQ.  4 waves x 32 query rows of one q-head; key tiles of 64. ----
-template <int D>
+template <int D, bool ALIBI>
 __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dq_kernel(const AttnParams p, const BwdParams g) {
-  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[64 * RS];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[64 * RS];
+  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8, TILE = 64 * RS;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (K', V) x 2 buffers
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lq = lane & 31, lh = lane >> 5;
+  const int lq = lane & 31;
   const int nqb = (p.Nq + 127) / 128;
-  const int qblk = blockIdx.x % nqb;
-  const int bh = blockIdx.x / nqb;
+  int bh, rank;
+  bwd_tile_of(p.B * p.Hq, bh, rank);
+  const int qblk = nqb - 1 - rank;  // later query blocks see more keys under a causal band
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.G;
   const int r0 = qblk * 128;
-  const int i = r0 + 32 * wave + lq;
+  const int i0 = r0 + 32 * wave;  // the wave's first row
+  const int i = i0 + lq;
   const int iq = min(i, p.Nq - 1);
-  const bool rope = p.rcos != nullptr;
+  const int wlast = min(i0 + 31, p.Nq - 1);
 
-  const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qsb + h * p.qsh;
-  const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ksb + kvh * p.ksh;
+  const __bf16* kb = g.kr + b * g.kr_sb + kvh * g.kr_sh;
   const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh;
-  const __bf16* dob = g.dout + b * p.osb + h * p.osh;
 
   // The lane's query row: Q' and dO as B operands over the head dim.
   bf16x8 qf[NKK], df[NKK];
-  row_frags<D>(qf, qb, p.qsn, iq, rope, p, p.q_pos0 + iq);
-  row_frags<D>(df, dob, p.osn, iq, false, p, 0);
+  row_frags<D>(qf, g.qr + b * g.qr_sb + h * g.qr_sh, g.qr_sn, iq);
+  row_frags<D>(df, g.dout + b * p.osb + h * p.osh, p.osn, iq);
   const long long row_id = ((long long)b * p.Hq + h) * p.Nq + iq;
   const float lse = p.lse[row_id];
-  const float lse2 = lse * kLog2e;
-  const float delta = g.delta[row_id];
-  const bool row_ok = i < p.Nq && lse != -INFINITY;
-  const float slope2 = p.alibi ? p.alibi[h] * kLog2e : 0.f;
+  float L2[16], Dl[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    L2[r] = (i < p.Nq && lse != -INFINITY) ? lse * kLog2e : INFINITY;
+    Dl[r] = g.delta[row_id];
+  }
+  const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
   const int dpos = p.k_pos0 - p.q_pos0;
 
   // Key tiles any row of the block may see (the band is j - i in index space).
@@ -231,92 +292,98 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dq_kernel(const AttnParams
   f32x16 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
-  const uint32_t ks_lds = lds_addr(ks);
-  RowStage<D, 64, RS> kst, vst;
   const int kt0 = (j_lo / 64) * 64;
-  if (j_hi >= j_lo) {
-    kst.load(kb, p.ksn, kt0, p.Nk, rope, p, p.k_pos0);
-    vst.load(vb, p.vsn, kt0, p.Nk, false, p, 0);
+  const int ntiles = j_hi >= j_lo ? (j_hi - kt0) / 64 + 1 : 0;
+  RowStage<D, 64, RS> kst, vst;
+  if (ntiles > 0) {
+    kst.load(kb, g.kr_sn, kt0, p.Nk);
+    vst.load(vb, p.vsn, kt0, p.Nk);
+    kst.store(smem);
+    vst.store(smem + TILE);
+    if (ntiles > 1) {
+      kst.load(kb, g.kr_sn, kt0 + 64, p.Nk);
+      vst.load(vb, p.vsn, kt0 + 64, p.Nk);
+    }
   }
-  for (int k0 = kt0; j_hi >= j_lo && k0 <= j_hi; k0 += 64) {
-    __syncthreads();
-    kst.store(ks, rope);
-    vst.store(vs, false);
-    __syncthreads();
-    if (k0 + 64 <= j_hi) {  // the next tile's loads overlap this tile's products
-      kst.load(kb, p.ksn, k0 + 64, p.Nk, rope, p, p.k_pos0);
-      vst.load(vb, p.vsn, k0 + 64, p.Nk, false, p, 0);
-    }
-    // S^T and dP^T for two 32-key subtiles (lane = query column).
-    f32x16 s[2], dp[2];
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = kt0 + 64 * t;
+    const __bf16* ks = smem + (t & 1) * 2 * TILE;
+    const __bf16* vs = ks + TILE;
+    const int klast = min(k0 + 63, p.Nk - 1);
+    // The wave's rows i0 .. wlast against keys k0 .. klast.
+    const bool skip = i0 >= p.Nq || (p.has_band && (klast - i0 < p.band_lo || k0 - wlast > p.band_hi));
+    if (!skip) {
+      const bool full = i0 + 31 < p.Nq && k0 + 63 < p.Nk &&
+                        (!p.has_band || (k0 - (i0 + 31) >= p.band_lo && k0 + 63 - i0 <= p.band_hi));
+      // S^T and dP^T for two 32-key subtiles (lane = query column).
+      f32x16 s[2], dp[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = f32x16{};
-      dp[st] = f32x16{};
+      for (int st = 0; st < 2; ++st) {
+        s[st] = f32x16{};
+        dp[st] = f32x16{};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s[st] = mfma32(row_frag<RS>(ks, 32 * st + lq, kk), qf[kk], s[st]);
-        dp[st] = mfma32(row_frag<RS>(vs, 32 * st + lq, kk), df[kk], dp[st]);
-      }
-    }
-    // dS^T = P^T (dP^T - delta), packed to bf16 in 16-key chunks.
-    bf16x8 dsf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint32_t w[4];
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        float x2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int st = c / 2, r = 8 * (c % 2) + 2 * q2 + e;
-          const int j = k0 + 32 * st + 8 * (r / 4) + 4 * lh + r % 4;
-          bool ok = row_ok && j < p.Nk;
-          if (p.has_band) ok = ok && (j - i >= p.band_lo) && (j - i <= p.band_hi);
-          float x = s[st][r] * p.scale_log2 - lse2;
-          if (p.alibi) x = __builtin_fmaf(slope2, (float)(j - i + dpos), x);
-          const float pr = ok ? fast_exp2(x) : 0.f;
-          x2[e] = pr * (dp[st][r] - delta);
+        for (int kk = 0; kk < NKK; ++kk) {
+          s[st] = mfma32(row_frag<RS>(ks, 32 * st + lq, kk), qf[kk], s[st]);
+          dp[st] = mfma32(row_frag<RS>(vs, 32 * st + lq, kk), df[kk], dp[st]);
         }
-        w[q2] = pack_bf16x2(x2[0], x2[1]);
       }
-      dsf[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      // dS^T = P^T (dP^T - delta), packed to bf16 in 16-key chunks.
+      bf16x8 dsf[2][2], unused[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (full)
+          p_ds<false, ALIBI, false, false>(s[st], dp[st], L2, Dl, k0 + 32 * st, i, p, slope2, dpos,
+                                           unused, dsf[st]);
+        else
+          p_ds<true, ALIBI, false, false>(s[st], dp[st], L2, Dl, k0 + 32 * st, i, p, slope2, dpos,
+                                          unused, dsf[st]);
+      }
+      // dQ'^T += K'^T dS^T.
+      const uint32_t ks_lds = lds_addr(ks);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[dt] = mfma32(tr_frag<RS>(ks_lds, 16 * c, 32 * dt), dsf[c / 2][c % 2], acc[dt]);
     }
-    // dQ'^T += K'^T dS^T.
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[dt] = mfma32(tr_frag<RS>(ks_lds, 16 * c, 32 * dt), dsf[c], acc[dt]);
+    if (t + 1 < ntiles) {  // the other buffer was last read before the previous barrier
+      __bf16* nk = smem + ((t + 1) & 1) * 2 * TILE;
+      kst.store(nk);
+      vst.store(nk + TILE);
+      if (t + 2 < ntiles) {
+        kst.load(kb, g.kr_sn, k0 + 128, p.Nk);
+        vst.load(vb, p.vsn, k0 + 128, p.Nk);
+      }
+    }
+    __syncthreads();
   }
   if (i < p.Nq) {
     __bf16* dst = g.dq + b * p.qsb + h * p.qsh + (long long)i * p.qsn;
-    store_grad_row<D>(dst, acc, p.scale_log2 / kLog2e, rope, p, p.q_pos0 + i);
+    store_grad_row<D>(dst, acc, p.scale_log2 / kLog2e, p.rcos != nullptr, p, p.q_pos0 + i);
   }
 }
 
-// ---- pass 2: dK, dV.  4 waves x 32 keys of one kv-head; query tiles of 32. ----
-template <int D>
+// ---- pass 2: dK, dV.  4 waves x 32 keys of one kv-head; query tiles of 64. ----
+template <int D, bool ALIBI>
 __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnParams p, const BwdParams g) {
-  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8;
-  __shared__ __attribute__((aligned(16))) __bf16 qs[32 * RS];
-  __shared__ __attribute__((aligned(16))) __bf16 dos[32 * RS];
-  __shared__ float lse_s[32], delta_s[32];
+  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8, TILE = 64 * RS;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (Q', dO) x 2 buffers
+  __shared__ __attribute__((aligned(16))) float stat[2][2][64];   // [buffer][L log2e, delta][row]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lq = lane & 31, lh = lane >> 5;
-  const int nkb = (p.Nk + 127) / 128;
-  const int kblk = blockIdx.x % nkb;
-  const int bk = blockIdx.x / nkb;
+  int bk, kblk;
+  bwd_tile_of(p.B * p.Hkv, bk, kblk);  // key block 0 sees the most queries under a causal band
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
   const int k0 = kblk * 128;
-  const int j = k0 + 32 * wave + lq;  // the lane's key (result column)
+  const int jw = k0 + 32 * wave;  // the wave's first key
+  const int j = jw + lq;          // the lane's key (result column)
   const int jc = min(j, p.Nk - 1);
-  const bool rope = p.rcos != nullptr;
+  const int jwl = min(jw + 31, p.Nk - 1);
 
-  const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ksb + kvh * p.ksh;
-  const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh;
   bf16x8 kf[NKK], vf[NKK];
-  row_frags<D>(kf, kb, p.ksn, jc, rope, p, p.k_pos0 + jc);
-  row_frags<D>(vf, vb, p.vsn, jc, false, p, 0);
+  row_frags<D>(kf, g.kr + b * g.kr_sb + kvh * g.kr_sh, g.kr_sn, jc);
+  row_frags<D>(vf, reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh, p.vsn, jc);
   const int dpos = p.k_pos0 - p.q_pos0;
 
   // Query rows that may see a key of the block: band_lo <= j - i <= band_hi.
@@ -329,108 +396,137 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
   f32x16 dk[NDT], dv[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dk[dt] = dv[dt] = f32x16{};
-  const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
+
   // (head, query tile) steps: the group's q-heads one after the other, each
-  // over the query tiles the band allows; the next step's loads are issued
-  // before this step's products.
-  const int qt0 = (i_lo / 32) * 32;
-  const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 32 + 1 : 0;
+  // over the 64-row query tiles the band allows.
+  const int qt0 = (i_lo / 64) * 64;
+  const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 64 + 1 : 0;
   const int nsteps = ntq * p.G;
-  RowStage<D, 32, RS> qst, dst;
-  float lse_r = 0.f, delta_r = 0.f;
+  RowStage<D, 64, RS> qst, dst;
+  float st_l2 = 0.f, st_delta = 0.f;
   auto load_step = [&](int t) {
-    const int h = kvh * p.G + t / ntq, q0 = qt0 + 32 * (t % ntq);
-    qst.load(reinterpret_cast<const __bf16*>(p.q) + b * p.qsb + h * p.qsh, p.qsn, q0, p.Nq, rope, p,
-             p.q_pos0);
-    dst.load(g.dout + b * p.osb + h * p.osh, p.osn, q0, p.Nq, false, p, 0);
-    if (threadIdx.x < 32) {
-      const long long rr = ((long long)b * p.Hq + h) * p.Nq + min(q0 + (int)threadIdx.x, p.Nq - 1);
-      lse_r = p.lse[rr];
-      delta_r = g.delta[rr];
+    const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
+    qst.load(g.qr + b * g.qr_sb + h * g.qr_sh, g.qr_sn, q0, p.Nq);
+    dst.load(g.dout + b * p.osb + h * p.osh, p.osn, q0, p.Nq);
+    if (threadIdx.x < 64) {
+      const int ii = q0 + (int)threadIdx.x;
+      const long long rr = ((long long)b * p.Hq + h) * p.Nq + min(ii, p.Nq - 1);
+      const float l = p.lse[rr];
+      st_l2 = (ii < p.Nq && l != -INFINITY) ? l * kLog2e : INFINITY;
+      st_delta = g.delta[rr];
     }
   };
-  if (nsteps > 0) load_step(0);
+  auto store_step = [&](int buf) {
+    qst.store(smem + buf * 2 * TILE);
+    dst.store(smem + buf * 2 * TILE + TILE);
+    if (threadIdx.x < 64) {
+      stat[buf][0][threadIdx.x] = st_l2;
+      stat[buf][1][threadIdx.x] = st_delta;
+    }
+  };
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+    if (nsteps > 1) load_step(1);
+  }
+  __syncthreads();
   for (int t = 0; t < nsteps; ++t) {
-    const int h = kvh * p.G + t / ntq, q0 = qt0 + 32 * (t % ntq);
-    const float slope2 = p.alibi ? p.alibi[h] * kLog2e : 0.f;
-    __syncthreads();
-    qst.store(qs, rope);
-    dst.store(dos, false);
-    if (threadIdx.x < 32) {
-      lse_s[threadIdx.x] = lse_r;
-      delta_s[threadIdx.x] = delta_r;
-    }
-    __syncthreads();
-    if (t + 1 < nsteps) load_step(t + 1);
-    // S and dP (32 query rows x the wave's 32 keys; lane = key column).
-    f32x16 s = f32x16{}, dpv = f32x16{};
+    const int buf = t & 1;
+    const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
+    const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
+    const __bf16* qs = smem + buf * 2 * TILE;
+    const __bf16* dos = qs + TILE;
+    const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      s = mfma32(row_frag<RS>(qs, lq, kk), kf[kk], s);
-      dpv = mfma32(row_frag<RS>(dos, lq, kk), vf[kk], dpv);
-    }
-    bf16x8 pf[2], dsf[2];
+    for (int st = 0; st < 2; ++st) {
+      // The wave's keys jw .. jwl against query rows ia .. ib.
+      const int ia = q0 + 32 * st, ib = min(ia + 31, p.Nq - 1);
+      const bool skip = ia >= p.Nq || jw >= p.Nk ||
+                        (p.has_band && (jwl - ia < p.band_lo || jw - ib > p.band_hi));
+      if (skip) continue;  // P = dS = 0
+      const bool full = ia + 31 < p.Nq && jw + 31 < p.Nk &&
+                        (!p.has_band || (jw - (ia + 31) >= p.band_lo && jw + 31 - ia <= p.band_hi));
+      // S and dP (32 query rows x the wave's 32 keys; lane = key column).
+      f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t wp[4], wd[4];
+      for (int kk = 0; kk < NKK; ++kk) {
+        sa = mfma32(row_frag<RS>(qs, 32 * st + lq, kk), kf[kk], sa);
+        da = mfma32(row_frag<RS>(dos, 32 * st + lq, kk), vf[kk], da);
+      }
+      float L2[16], Dl[16];
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        float pv[2], dsv[2];
+      for (int a = 0; a < 4; ++a) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&stat[buf][0][32 * st + 8 * a + 4 * lh]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&stat[buf][1][32 * st + 8 * a + 4 * lh]);
+        L2[4 * a] = l4.x; L2[4 * a + 1] = l4.y; L2[4 * a + 2] = l4.z; L2[4 * a + 3] = l4.w;
+        Dl[4 * a] = d4.x; Dl[4 * a + 1] = d4.y; Dl[4 * a + 2] = d4.z; Dl[4 * a + 3] = d4.w;
+      }
+      bf16x8 pf[2], dsf[2];
+      if (full)
+        p_ds<false, ALIBI, true, true>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
+      else
+        p_ds<true, ALIBI, true, true>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
+      // dV^T += dO^T P,  dK'^T += Q'^T dS.
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = 8 * c + 2 * q2 + e;
-          const int m = 8 * (r / 4) + 4 * lh + r % 4;  // query row within the tile
-          const int ii = q0 + m;
-          const float lse = lse_s[m];
-          bool ok = ii < p.Nq && j < p.Nk && lse != -INFINITY;
-          if (p.has_band) ok = ok && (j - ii >= p.band_lo) && (j - ii <= p.band_hi);
-          float x = s[r] * p.scale_log2 - lse * kLog2e;
-          if (p.alibi) x = __builtin_fmaf(slope2, (float)(j - ii + dpos), x);
-          pv[e] = ok ? fast_exp2(x) : 0.f;
-          dsv[e] = pv[e] * (dpv[r] - delta_s[m]);
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          dv[dt] = mfma32(tr_frag<RS>(dos_lds, 32 * st + 16 * c, 32 * dt), pf[c], dv[dt]);
+          dk[dt] = mfma32(tr_frag<RS>(qs_lds, 32 * st + 16 * c, 32 * dt), dsf[c], dk[dt]);
         }
-        wp[q2] = pack_bf16x2(pv[0], pv[1]);
-        wd[q2] = pack_bf16x2(dsv[0], dsv[1]);
-      }
-      pf[c] = __builtin_bit_cast(bf16x8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
-      dsf[c] = __builtin_bit_cast(bf16x8, make_uint4(wd[0], wd[1], wd[2], wd[3]));
     }
-    // dV^T += dO^T P,  dK'^T += Q'^T dS.
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        dv[dt] = mfma32(tr_frag<RS>(dos_lds, 16 * c, 32 * dt), pf[c], dv[dt]);
-        dk[dt] = mfma32(tr_frag<RS>(qs_lds, 16 * c, 32 * dt), dsf[c], dk[dt]);
-      }
+    if (t + 1 < nsteps) {  // the other buffer was last read before the previous barrier
+      store_step((t + 1) & 1);
+      if (t + 2 < nsteps) load_step(t + 2);
+    }
+    __syncthreads();
   }
   if (j < p.Nk) {
     __bf16* dkd = g.dk + b * p.ksb + kvh * p.ksh + (long long)j * p.ksn;
     __bf16* dvd = g.dv + b * p.vsb + kvh * p.vsh + (long long)j * p.vsn;
-    store_grad_row<D>(dkd, dk, p.scale_log2 / kLog2e, rope, p, p.k_pos0 + j);
+    store_grad_row<D>(dkd, dk, p.scale_log2 / kLog2e, p.rcos != nullptr, p, p.k_pos0 + j);
     store_grad_row<D>(dvd, dv, 1.f, false, p, 0);
   }
 }
 
-hipError_t launch_bwd(const AttnParams& p, const BwdParams& g, int D, hipStream_t stream) {
-  const long long rows = (long long)p.B * p.Hq * p.Nq;
+template <int D, bool ALIBI>
+static void launch_bwd_main(const AttnParams& p, const BwdParams& g, unsigned grid_k,
+                            unsigned grid_q, hipStream_t stream) {
+  if (grid_k > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI>), dim3(grid_k), dim3(kBwdThreads), 0, stream, p, g);
+  if (grid_q > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI>), dim3(grid_q), dim3(kBwdThreads), 0, stream, p, g);
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const AttnParams& p, const BwdParams& g, hipStream_t stream) {
+  const long long rows_q = (long long)p.B * p.Hq * p.Nq;
+  const long long rows_k = (long long)p.B * p.Hkv * p.Nk;
+  constexpr int CH = D / 16;
+  if (g.qrot && rows_q > 0)
+    hipLaunchKernelGGL(bwd_rotate_kernel<D>, dim3((unsigned)((rows_q * CH + 255) / 256)), dim3(256), 0,
+                       stream, reinterpret_cast<const __bf16*>(p.q), p.qsb, p.qsh, p.qsn, p.Hq, p.Nq,
+                       rows_q, p.q_pos0, p, g.qrot);
+  if (g.krot && rows_k > 0)
+    hipLaunchKernelGGL(bwd_rotate_kernel<D>, dim3((unsigned)((rows_k * CH + 255) / 256)), dim3(256), 0,
+                       stream, reinterpret_cast<const __bf16*>(p.k), p.ksb, p.ksh, p.ksn, p.Hkv, p.Nk,
+                       rows_k, p.k_pos0, p, g.krot);
+  constexpr int rpb = 256 / (D / 8);
+  if (rows_q > 0)
+    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows_q + rpb - 1) / rpb)), dim3(256), 0,
+                       stream, p, g);
   const unsigned grid_q = (unsigned)((long long)p.B * p.Hq * ((p.Nq + 127) / 128));
   const unsigned grid_k = (unsigned)((long long)p.B * p.Hkv * ((p.Nk + 127) / 128));
-#define ATTNFUSE_BWD(DD)                                                                           \
-  if (D == DD) {                                                                                   \
-    constexpr int rpb = 256 / (DD / 8);                                                            \
-    if (rows > 0)                                                                                  \
-      hipLaunchKernelGGL(bwd_delta_kernel<DD>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), \
-                         0, stream, p, g);                                                         \
-    if (grid_k > 0)                                                                                \
-      hipLaunchKernelGGL(bwd_dkdv_kernel<DD>, dim3(grid_k), dim3(kBwdThreads), 0, stream, p, g);    \
-    if (grid_q > 0)                                                                                \
-      hipLaunchKernelGGL(bwd_dq_kernel<DD>, dim3(grid_q), dim3(kBwdThreads), 0, stream, p, g);      \
-    return hipGetLastError();                                                                      \
-  }
-  ATTNFUSE_BWD(64)
-  ATTNFUSE_BWD(128)
-#undef ATTNFUSE_BWD
+  if (p.alibi)
+    launch_bwd_main<D, true>(p, g, grid_k, grid_q, stream);
+  else
+    launch_bwd_main<D, false>(p, g, grid_k, grid_q, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const AttnParams& p, const BwdParams& g, int D, hipStream_t stream) {
+  if (D == 64) return launch_bwd_d<64>(p, g, stream);
+  if (D == 128) return launch_bwd_d<128>(p, g, stream);
   return hipErrorInvalidValue;
 }
 

@@ -77,6 +77,13 @@ struct BwdParams {
   __bf16* dq;          // strides of q
   __bf16* dk;          // strides of k
   __bf16* dv;          // strides of v
+  // Q and K as the products read them (element strides of batch, head, row):
+  // the rotated copies qrot / krot when RoPE is on, else q and k themselves.
+  const __bf16* qr;
+  const __bf16* kr;
+  long long qr_sb, qr_sh, qr_sn, kr_sb, kr_sh, kr_sn;
+  __bf16* qrot;        // [B, Hq, Nq, D] contiguous workspace, or nullptr
+  __bf16* krot;        // [B, Hkv, Nk, D] contiguous workspace, or nullptr
 };
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {

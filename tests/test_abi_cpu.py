@@ -174,6 +174,12 @@ def test_bwd_validation(lib):
     # the backward reads the fp32 cos / sin tables
     assert call(_good_desc(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_cs_bf16=0x2000,
                            rope_table_len=10**5), FAKE, need) == _abi.ERR_INVALID
+    # with RoPE the workspace also holds the rotated Q and K (bf16)
+    dr = _good_desc(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=10**5)
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lib.attnfuse_bwd_workspace_size(ctypes.byref(dr)) == (
+        need + r256(dr.B * dr.Hq * dr.Nq * dr.D * 2) + r256(dr.B * dr.Hkv * dr.Nk * dr.D * 2))
+    assert call(dr, FAKE, need) == _abi.ERR_WORKSPACE
     assert lib.attnfuse_bwd(ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             ctypes.byref(d), FAKE, need, None) == _abi.ERR_UNSUPPORTED
 
