@@ -149,7 +149,7 @@ const char* attnfuse_status_string(int status) {
     case ATTNFUSE_OK: return "ok";
     case ATTNFUSE_ERR_INVALID: return "invalid argument or descriptor";
     case ATTNFUSE_ERR_UNSUPPORTED: return "unsupported variant or shape";
-    case ATTNFUSE_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case ATTNFUSE_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTNFUSE_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -288,11 +288,25 @@ size_t bwd_qrot_bytes(const attnfuse_variant_desc* d) {
 size_t bwd_krot_bytes(const attnfuse_variant_desc* d) {
   return bwd_rotates(d) ? round256((size_t)d->B * d->Hkv * d->Nk * d->D * 2) : 0;
 }
+
+// Under a causal or windowed band the dK/dV work of the key blocks differs by
+// up to Nk/128 times; when the grid is too small to even that out over the
+// 256 CUs, each (kv-head, key block) is split over two workgroups (each
+// taking half of its (q-head, query tile) steps) that write fp32 partial
+// sums, which a last pass adds up.
+int bwd_kv_parts(const attnfuse_variant_desc* d) {
+  const long long gk = (long long)d->B * d->Hkv * ((d->Nk + 127) / 128);
+  return ((d->causal || d->window > 0) && d->Nq > 0 && gk > 0 && gk <= 512) ? 2 : 1;
+}
+size_t bwd_part_bytes(const attnfuse_variant_desc* d) {
+  const int parts = bwd_kv_parts(d);
+  return parts > 1 ? round256((size_t)parts * 2 * d->B * d->Hkv * d->Nk * d->D * sizeof(float)) : 0;
+}
 }  // namespace
 
 size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc) {
   if (validate_common(desc) != ATTNFUSE_OK) return 0;
-  return bwd_delta_bytes(desc) + bwd_qrot_bytes(desc) + bwd_krot_bytes(desc);
+  return bwd_delta_bytes(desc) + bwd_qrot_bytes(desc) + bwd_krot_bytes(desc) + bwd_part_bytes(desc);
 }
 
 int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -321,6 +335,10 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   g.dk = static_cast<__bf16*>(dk);
   g.dv = static_cast<__bf16*>(dv);
   char* ws = static_cast<char*>(workspace);
+  g.kv_parts = bwd_kv_parts(d);
+  g.kv_part = g.kv_parts > 1 ? reinterpret_cast<float*>(ws + bwd_delta_bytes(d) + bwd_qrot_bytes(d) +
+                                                        bwd_krot_bytes(d))
+                             : nullptr;
   if (bwd_rotates(d)) {
     g.qrot = reinterpret_cast<__bf16*>(ws + bwd_delta_bytes(d));
     g.krot = reinterpret_cast<__bf16*>(ws + bwd_delta_bytes(d) + bwd_qrot_bytes(d));
@@ -338,7 +356,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
     g.kr_sb = d->k_stride[0]; g.kr_sh = d->k_stride[1]; g.kr_sn = d->k_stride[2];
   }
   const long long gq = (long long)d->B * d->Hq * ((d->Nq + 127) / 128);
-  const long long gk = (long long)d->B * d->Hkv * ((d->Nk + 127) / 128);
+  const long long gk = (long long)d->B * d->Hkv * ((d->Nk + 127) / 128) * g.kv_parts;
   // The rotation and row-reduction passes use at most one 256-thread block
   // per 16 rows (D = 128 row reduction).
   const long long row_blocks = (long long)d->B * (d->Hq > d->Hkv ? d->Hq : d->Hkv) *

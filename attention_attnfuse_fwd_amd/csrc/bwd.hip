@@ -152,6 +152,18 @@ __device__ __forceinline__ void bwd_tile_of(int nunits, int& unit, int& rank) {
   }
 }
 
+// An accumulator row as held by store_grad_row's acc, stored unscaled in fp32.
+template <int D>
+__device__ __forceinline__ void store_part_row(float* dst, const f32x16 (&acc)[D / 32]) {
+  const int kb = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(dst + 32 * dt + 8 * g + 4 * kb) =
+          make_float4(acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+}
+
 // P = exp2(S scale log2e - L log2e) and dS = P (dP - delta) for one 32x32
 // block held as accumulators s (scores) and dp, packed to bf16 as two
 // 16-row MFMA B operands (chunk c holds the accumulator rows 8c .. 8c+7).
@@ -372,8 +384,9 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
   __shared__ __attribute__((aligned(16))) float stat[2][2][64];   // [buffer][L log2e, delta][row]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lq = lane & 31, lh = lane >> 5;
-  int bk, kblk;
-  bwd_tile_of(p.B * p.Hkv, bk, kblk);  // key block 0 sees the most queries under a causal band
+  int bk, rank;
+  bwd_tile_of(p.B * p.Hkv, bk, rank);  // key block 0 sees the most queries under a causal band
+  const int kblk = rank / g.kv_parts, part = rank % g.kv_parts;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
   const int k0 = kblk * 128;
   const int jw = k0 + 32 * wave;  // the wave's first key
@@ -398,10 +411,11 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
   for (int dt = 0; dt < NDT; ++dt) dk[dt] = dv[dt] = f32x16{};
 
   // (head, query tile) steps: the group's q-heads one after the other, each
-  // over the 64-row query tiles the band allows.
+  // over the 64-row query tiles the band allows; this workgroup's part of them.
   const int qt0 = (i_lo / 64) * 64;
   const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 64 + 1 : 0;
-  const int nsteps = ntq * p.G;
+  const int t_begin = (int)((long long)part * ntq * p.G / g.kv_parts);
+  const int t_end = (int)((long long)(part + 1) * ntq * p.G / g.kv_parts);
   RowStage<D, 64, RS> qst, dst;
   float st_l2 = 0.f, st_delta = 0.f;
   auto load_step = [&](int t) {
@@ -424,14 +438,14 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
       stat[buf][1][threadIdx.x] = st_delta;
     }
   };
-  if (nsteps > 0) {
-    load_step(0);
+  if (t_end > t_begin) {
+    load_step(t_begin);
     store_step(0);
-    if (nsteps > 1) load_step(1);
+    if (t_end > t_begin + 1) load_step(t_begin + 1);
   }
   __syncthreads();
-  for (int t = 0; t < nsteps; ++t) {
-    const int buf = t & 1;
+  for (int t = t_begin; t < t_end; ++t) {
+    const int buf = (t - t_begin) & 1;
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
     const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
     const __bf16* qs = smem + buf * 2 * TILE;
@@ -475,18 +489,78 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
           dk[dt] = mfma32(tr_frag<RS>(qs_lds, 32 * st + 16 * c, 32 * dt), dsf[c], dk[dt]);
         }
     }
-    if (t + 1 < nsteps) {  // the other buffer was last read before the previous barrier
-      store_step((t + 1) & 1);
-      if (t + 2 < nsteps) load_step(t + 2);
+    if (t + 1 < t_end) {  // the other buffer was last read before the previous barrier
+      store_step(buf ^ 1);
+      if (t + 2 < t_end) load_step(t + 2);
     }
     __syncthreads();
   }
   if (j < p.Nk) {
-    __bf16* dkd = g.dk + b * p.ksb + kvh * p.ksh + (long long)j * p.ksn;
-    __bf16* dvd = g.dv + b * p.vsb + kvh * p.vsh + (long long)j * p.vsn;
-    store_grad_row<D>(dkd, dk, p.scale_log2 / kLog2e, p.rcos != nullptr, p, p.k_pos0 + j);
-    store_grad_row<D>(dvd, dv, 1.f, false, p, 0);
+    if (g.kv_parts == 1) {
+      __bf16* dkd = g.dk + b * p.ksb + kvh * p.ksh + (long long)j * p.ksn;
+      __bf16* dvd = g.dv + b * p.vsb + kvh * p.vsh + (long long)j * p.vsn;
+      store_grad_row<D>(dkd, dk, p.scale_log2 / kLog2e, p.rcos != nullptr, p, p.k_pos0 + j);
+      store_grad_row<D>(dvd, dv, 1.f, false, p, 0);
+    } else {
+      const long long rows_k = (long long)p.B * p.Hkv * p.Nk;
+      const long long krow = ((long long)b * p.Hkv + kvh) * p.Nk + j;
+      store_part_row<D>(g.kv_part + ((2LL * part) * rows_k + krow) * D, dk);
+      store_part_row<D>(g.kv_part + ((2LL * part + 1) * rows_k + krow) * D, dv);
+    }
   }
+}
+
+// ---- pass 2b (kv_parts > 1): dK = scale * RoPE^-1(sum of the dK' parts), dV = sum ----
+template <int D>
+__global__ void __launch_bounds__(256) bwd_kv_reduce_kernel(const AttnParams p, const BwdParams g) {
+  constexpr int CH = D / 16;  // chunk pairs per row
+  const long long rows_k = (long long)p.B * p.Hkv * p.Nk;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows_k * CH) return;
+  const int c = (int)(idx % CH);
+  const long long row = idx / CH;
+  const int j = (int)(row % p.Nk);
+  const long long bh = row / p.Nk;
+  const int kvh = (int)(bh % p.Hkv), b = (int)(bh / p.Hkv);
+  float k_lo[8] = {}, k_hi[8] = {}, v_lo[8] = {}, v_hi[8] = {};
+  for (int part = 0; part < g.kv_parts; ++part) {
+    const float* pk = g.kv_part + ((2LL * part) * rows_k + row) * D;
+    const float* pv = g.kv_part + ((2LL * part + 1) * rows_k + row) * D;
+    const F8 a = ld_f8(pk + 8 * c), bb = ld_f8(pk + D / 2 + 8 * c);
+    const F8 x = ld_f8(pv + 8 * c), y = ld_f8(pv + D / 2 + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      k_lo[e] += f8_at(a, e);
+      k_hi[e] += f8_at(bb, e);
+      v_lo[e] += f8_at(x, e);
+      v_hi[e] += f8_at(y, e);
+    }
+  }
+  const float scale = p.scale_log2 / kLog2e;
+  if (p.rcos) {
+    const long long t = (long long)min(p.k_pos0 + j, p.rope_len - 1) * (D / 2) + 8 * c;
+    const F8 cs = ld_f8(p.rcos + t), sn = ld_f8(p.rsin + t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float co = f8_at(cs, e), si = f8_at(sn, e), lo = k_lo[e], hi = k_hi[e];
+      k_lo[e] = lo * co + hi * si;
+      k_hi[e] = hi * co - lo * si;
+    }
+  }
+  uint32_t wk0[4], wk1[4], wv0[4], wv1[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wk0[w] = pack_bf16x2(scale * k_lo[2 * w], scale * k_lo[2 * w + 1]);
+    wk1[w] = pack_bf16x2(scale * k_hi[2 * w], scale * k_hi[2 * w + 1]);
+    wv0[w] = pack_bf16x2(v_lo[2 * w], v_lo[2 * w + 1]);
+    wv1[w] = pack_bf16x2(v_hi[2 * w], v_hi[2 * w + 1]);
+  }
+  __bf16* dkd = g.dk + b * p.ksb + kvh * p.ksh + (long long)j * p.ksn;
+  __bf16* dvd = g.dv + b * p.vsb + kvh * p.vsh + (long long)j * p.vsn;
+  st16(dkd + 8 * c, make_uint4(wk0[0], wk0[1], wk0[2], wk0[3]));
+  st16(dkd + D / 2 + 8 * c, make_uint4(wk1[0], wk1[1], wk1[2], wk1[3]));
+  st16(dvd + 8 * c, make_uint4(wv0[0], wv0[1], wv0[2], wv0[3]));
+  st16(dvd + D / 2 + 8 * c, make_uint4(wv1[0], wv1[1], wv1[2], wv1[3]));
 }
 
 template <int D, bool ALIBI>
@@ -516,11 +590,14 @@ static hipError_t launch_bwd_d(const AttnParams& p, const BwdParams& g, hipStrea
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows_q + rpb - 1) / rpb)), dim3(256), 0,
                        stream, p, g);
   const unsigned grid_q = (unsigned)((long long)p.B * p.Hq * ((p.Nq + 127) / 128));
-  const unsigned grid_k = (unsigned)((long long)p.B * p.Hkv * ((p.Nk + 127) / 128));
+  const unsigned grid_k = (unsigned)((long long)p.B * p.Hkv * ((p.Nk + 127) / 128) * g.kv_parts);
   if (p.alibi)
     launch_bwd_main<D, true>(p, g, grid_k, grid_q, stream);
   else
     launch_bwd_main<D, false>(p, g, grid_k, grid_q, stream);
+  if (g.kv_parts > 1 && rows_k > 0)
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel<D>, dim3((unsigned)((rows_k * CH + 255) / 256)), dim3(256), 0,
+                       stream, p, g);
   return hipGetLastError();
 }
 

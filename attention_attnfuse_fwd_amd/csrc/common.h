@@ -84,6 +84,10 @@ struct BwdParams {
   long long qr_sb, qr_sh, qr_sn, kr_sb, kr_sh, kr_sn;
   __bf16* qrot;        // [B, Hq, Nq, D] contiguous workspace, or nullptr
   __bf16* krot;        // [B, Hkv, Nk, D] contiguous workspace, or nullptr
+  // kv_parts > 1: each (kv-head, key block) is split over kv_parts workgroups
+  // that write fp32 partial sums [part][dK', dV][B * Hkv * Nk][D] to kv_part.
+  int kv_parts;
+  float* kv_part;
 };
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {

@@ -276,14 +276,16 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     return (out, lse) if return_lse else out
 
 
-def bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
-                       rope_theta: Optional[float] = None, q_pos0: int = 0) -> int:
-    """Bytes of workspace bwd() needs for these shapes (the row reductions,
-    plus the rotated Q and K when rope_theta is given)."""
+def bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                       window: int = 0, rope_theta: Optional[float] = None, q_pos0: int = 0,
+                       k_pos0: int = 0) -> int:
+    """Bytes of workspace bwd() needs for these shapes and masks (the row
+    reductions, the rotated Q and K when rope_theta is given, and fp32
+    partial dK / dV sums when a band's key blocks are split)."""
     _check_inputs(q, k, v)
     keep = []
-    d = _make_desc(q, k, v, q, scale=None, causal=False, window=0, rope_theta=rope_theta,
-                   q_pos0=q_pos0, k_pos0=0, alibi_slopes=None, bias=None, block_mask=None,
+    d = _make_desc(q, k, v, q, scale=None, causal=causal, window=window, rope_theta=rope_theta,
+                   q_pos0=q_pos0, k_pos0=k_pos0, alibi_slopes=None, bias=None, block_mask=None,
                    lse=None, keep=keep)
     return int(_abi.load().attnfuse_bwd_workspace_size(ctypes.byref(d)))
 

@@ -52,7 +52,7 @@ typedef enum attnfuse_status {
   ATTNFUSE_OK = 0,
   ATTNFUSE_ERR_INVALID = -1,     /* malformed descriptor or argument          */
   ATTNFUSE_ERR_UNSUPPORTED = -2, /* well formed, but no kernel implements it  */
-  ATTNFUSE_ERR_WORKSPACE = -3,   /* decode workspace missing or too small     */
+  ATTNFUSE_ERR_WORKSPACE = -3,   /* decode / backward workspace missing or too small */
   ATTNFUSE_ERR_HIP = -4          /* a HIP runtime call or launch failed        */
 } attnfuse_status;
 
@@ -196,9 +196,14 @@ int attnfuse_rope_table(double theta, int32_t D, int64_t len, float* cos_out, fl
 int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* desc,
                        int32_t which, void* stream);
 
-/* Bytes of workspace attnfuse_bwd needs: B * Hq * Nq floats (the row
- * reductions delta = rowsum(dO * O)), rounded up to 256.  Returns 0 for an
- * invalid descriptor. */
+/* Bytes of workspace attnfuse_bwd needs, each part rounded up to 256:
+ *   B * Hq * Nq floats (the row reductions delta = rowsum(dO * O));
+ *   with rope (and Nq, Nk > 0): the rotated copies RoPE(q) [B, Hq, Nq, D] and
+ *     RoPE(k) [B, Hkv, Nk, D] in bf16, which the gradient passes read;
+ *   with causal or window > 0 when B * Hkv * ceil(Nk / 128) <= 512: two fp32
+ *     partial sums of dK and dV, [2][2][B * Hkv * Nk][D] (each key block's
+ *     work is split over two workgroups to even out the band's imbalance).
+ * Returns 0 for an invalid descriptor. */
 size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc);
 
 /* Attention backward ("4.4 Backward Pass": the FlashAttention-2 split into a
@@ -216,7 +221,8 @@ size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc);
  *       ATTNFUSE_ERR_WORKSPACE); its contents on entry do not matter.
  * Supports bf16 with rope (fp32 cos / sin tables required), causal, window
  * and alibi; bias, block_sparse and fp32 return ATTNFUSE_ERR_UNSUPPORTED.
- * All pointers 16-byte aligned.  Runs three kernels on `stream`. */
+ * All pointers 16-byte aligned.  Runs three to six kernels on `stream` (with
+ * rope the two rotations first; with split key blocks a final reduction).  */
 int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, const attnfuse_variant_desc* desc,
                  void* workspace, size_t workspace_bytes, void* stream);

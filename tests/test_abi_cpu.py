@@ -163,7 +163,11 @@ def test_decode_validation(lib):
 def test_bwd_validation(lib):
     d = _good_desc()
     need = lib.attnfuse_bwd_workspace_size(ctypes.byref(d))
-    assert need == (d.B * d.Hq * d.Nq * 4 + 255) // 256 * 256
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert need == r256(d.B * d.Hq * d.Nq * 4)
+    # a causal band on a small grid splits each key block over two workgroups (fp32 partials)
+    dc = _good_desc(causal=1)
+    assert lib.attnfuse_bwd_workspace_size(ctypes.byref(dc)) == need + r256(2 * 2 * dc.B * dc.Hkv * dc.Nk * dc.D * 4)
     call = lambda d, ws, nb, lse=FAKE: lib.attnfuse_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, lse, FAKE, FAKE,
                                                       FAKE, ctypes.byref(d), ws, nb, None)
     assert call(d, FAKE, need - 4) == _abi.ERR_WORKSPACE
@@ -176,7 +180,6 @@ def test_bwd_validation(lib):
                            rope_table_len=10**5), FAKE, need) == _abi.ERR_INVALID
     # with RoPE the workspace also holds the rotated Q and K (bf16)
     dr = _good_desc(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=10**5)
-    r256 = lambda x: (x + 255) // 256 * 256
     assert lib.attnfuse_bwd_workspace_size(ctypes.byref(dr)) == (
         need + r256(dr.B * dr.Hq * dr.Nq * dr.D * 2) + r256(dr.B * dr.Hkv * dr.Nk * dr.D * 2))
     assert call(dr, FAKE, need) == _abi.ERR_WORKSPACE
