@@ -355,7 +355,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
     g.qr_sb = d->q_stride[0]; g.qr_sh = d->q_stride[1]; g.qr_sn = d->q_stride[2];
     g.kr_sb = d->k_stride[0]; g.kr_sh = d->k_stride[1]; g.kr_sn = d->k_stride[2];
   }
-  const long long gq = (long long)d->B * d->Hq * ((d->Nq + 127) / 128);
+  const long long gq = (long long)d->B * d->Hq * ((d->Nq + 255) / 256);
   const long long gk = (long long)d->B * d->Hkv * ((d->Nk + 127) / 128) * g.kv_parts;
   // The rotation and row-reduction passes use at most one 256-thread block
   // per 16 rows (D = 128 row reduction).

@@ -20,6 +20,7 @@
 // its part of a tile as fully visible (no mask arithmetic), fully masked
 // (skipped) or partial (per-element band and bound tests).
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -28,7 +29,9 @@ namespace attnfuse {
 
 namespace {
 
-constexpr int kBwdThreads = 256;  // 4 waves
+constexpr int kBwdThreads = 256;    // 4 waves (dK/dV)
+constexpr int kDqThreads = 512;     // 8 waves, two per SIMD (dQ)
+constexpr int kDqRows = 256;        // query rows per dQ workgroup
 
 // Transposed A operand (32 rows of the result x 16 contraction steps) from a
 // row-major bf16 tile T[row][RS] in LDS, for MFMA k index 8*kb + e  <->  tile
@@ -65,24 +68,24 @@ __device__ __forceinline__ uint4 ld_row8(const __bf16* base, long long sn, int r
 // in two steps so the next tile's loads can be in flight while the current
 // one is multiplied: load() reads this thread's share into registers,
 // store() writes it to a padded LDS tile.
-template <int D, int R, int RS>
+template <int D, int R, int RS, int NT = kBwdThreads>
 struct RowStage {
   static constexpr int CPR = D / 8;                          // 16-byte chunks per row
-  static constexpr int U = (R * CPR + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int U = (R * CPR + NT - 1) / NT;
   uint4 x[U];
   __device__ __forceinline__ void load(const __bf16* src, long long sn, int r0, int N) {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int u = threadIdx.x + kBwdThreads * k;
-      if ((R * CPR) % kBwdThreads == 0 || u < R * CPR)
+      const int u = threadIdx.x + NT * k;
+      if ((R * CPR) % NT == 0 || u < R * CPR)
         x[k] = ld_row8(src, sn, min(r0 + u / CPR, N - 1), 8 * (u % CPR));
     }
   }
   __device__ __forceinline__ void store(__bf16* tile) const {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
-      const int u = threadIdx.x + kBwdThreads * k;
-      if ((R * CPR) % kBwdThreads == 0 || u < R * CPR) st16(tile + (u / CPR) * RS + 8 * (u % CPR), x[k]);
+      const int u = threadIdx.x + NT * k;
+      if ((R * CPR) % NT == 0 || u < R * CPR) st16(tile + (u / CPR) * RS + 8 * (u % CPR), x[k]);
     }
   }
 };
@@ -257,20 +260,23 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const AttnParams p, cons
   if (row < rows && c == 0) g.delta[row] = acc;
 }
 
-// ---- pass 3: dQ.  4 waves x 32 query rows of one q-head; key tiles of 64. ----
+// ---- pass 3: dQ.  8 waves (two per SIMD) x 32 query rows of one q-head;
+// key tiles of 64.  Each wave keeps its rows' Q' and dO as MFMA operands and
+// its dQ' accumulators in registers (at most 256 per wave), and walks the
+// tile's two 32-key subtiles one after the other: S^T, dP^T, dS^T, dQ'^T.
 template <int D, bool ALIBI>
-__global__ void __launch_bounds__(kBwdThreads, 1) bwd_dq_kernel(const AttnParams p, const BwdParams g) {
+__global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams p, const BwdParams g) {
   constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8, TILE = 64 * RS;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (K', V) x 2 buffers
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lq = lane & 31;
-  const int nqb = (p.Nq + 127) / 128;
+  const int nqb = (p.Nq + kDqRows - 1) / kDqRows;
   int bh, rank;
   bwd_tile_of(p.B * p.Hq, bh, rank);
   const int qblk = nqb - 1 - rank;  // later query blocks see more keys under a causal band
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.G;
-  const int r0 = qblk * 128;
+  const int r0 = qblk * kDqRows;
   const int i0 = r0 + 32 * wave;  // the wave's first row
   const int i = i0 + lq;
   const int iq = min(i, p.Nq - 1);
@@ -295,7 +301,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dq_kernel(const AttnParams
   const int dpos = p.k_pos0 - p.q_pos0;
 
   // Key tiles any row of the block may see (the band is j - i in index space).
-  const int wg_last = min(r0 + 127, p.Nq - 1);
+  const int wg_last = min(r0 + kDqRows - 1, p.Nq - 1);
   int j_lo = 0, j_hi = p.Nk - 1;
   if (p.has_band) {
     j_lo = max(j_lo, (int)max((long long)r0 + p.band_lo, 0LL));
@@ -306,7 +312,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dq_kernel(const AttnParams
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
   const int kt0 = (j_lo / 64) * 64;
   const int ntiles = j_hi >= j_lo ? (j_hi - kt0) / 64 + 1 : 0;
-  RowStage<D, 64, RS> kst, vst;
+  RowStage<D, 64, RS, kDqThreads> kst, vst;
   if (ntiles > 0) {
     kst.load(kb, g.kr_sn, kt0, p.Nk);
     vst.load(vb, p.vsn, kt0, p.Nk);
@@ -322,42 +328,35 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dq_kernel(const AttnParams
     const int k0 = kt0 + 64 * t;
     const __bf16* ks = smem + (t & 1) * 2 * TILE;
     const __bf16* vs = ks + TILE;
-    const int klast = min(k0 + 63, p.Nk - 1);
-    // The wave's rows i0 .. wlast against keys k0 .. klast.
-    const bool skip = i0 >= p.Nq || (p.has_band && (klast - i0 < p.band_lo || k0 - wlast > p.band_hi));
-    if (!skip) {
-      const bool full = i0 + 31 < p.Nq && k0 + 63 < p.Nk &&
-                        (!p.has_band || (k0 - (i0 + 31) >= p.band_lo && k0 + 63 - i0 <= p.band_hi));
-      // S^T and dP^T for two 32-key subtiles (lane = query column).
-      f32x16 s[2], dp[2];
+    const uint32_t ks_lds = lds_addr(ks);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = f32x16{};
-        dp[st] = f32x16{};
+    for (int st = 0; st < 2; ++st) {
+      // The wave's rows i0 .. wlast against keys ka .. kl.
+      const int ka = k0 + 32 * st, kl = min(ka + 31, p.Nk - 1);
+      const bool skip = i0 >= p.Nq || ka >= p.Nk ||
+                        (p.has_band && (kl - i0 < p.band_lo || ka - wlast > p.band_hi));
+      if (skip) continue;  // dS = 0
+      const bool full = i0 + 31 < p.Nq && ka + 31 < p.Nk &&
+                        (!p.has_band || (ka - (i0 + 31) >= p.band_lo && ka + 31 - i0 <= p.band_hi));
+      // S^T and dP^T (lane = query column).
+      f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          s[st] = mfma32(row_frag<RS>(ks, 32 * st + lq, kk), qf[kk], s[st]);
-          dp[st] = mfma32(row_frag<RS>(vs, 32 * st + lq, kk), df[kk], dp[st]);
-        }
+      for (int kk = 0; kk < NKK; ++kk) {
+        sa = mfma32(row_frag<RS>(ks, 32 * st + lq, kk), qf[kk], sa);
+        da = mfma32(row_frag<RS>(vs, 32 * st + lq, kk), df[kk], da);
       }
       // dS^T = P^T (dP^T - delta), packed to bf16 in 16-key chunks.
-      bf16x8 dsf[2][2], unused[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (full)
-          p_ds<false, ALIBI, false, false>(s[st], dp[st], L2, Dl, k0 + 32 * st, i, p, slope2, dpos,
-                                           unused, dsf[st]);
-        else
-          p_ds<true, ALIBI, false, false>(s[st], dp[st], L2, Dl, k0 + 32 * st, i, p, slope2, dpos,
-                                          unused, dsf[st]);
-      }
+      bf16x8 dsf[2], unused[2];
+      if (full)
+        p_ds<false, ALIBI, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, unused, dsf);
+      else
+        p_ds<true, ALIBI, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, unused, dsf);
       // dQ'^T += K'^T dS^T.
-      const uint32_t ks_lds = lds_addr(ks);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[dt] = mfma32(tr_frag<RS>(ks_lds, 16 * c, 32 * dt), dsf[c / 2][c % 2], acc[dt]);
+        for (int c = 0; c < 2; ++c)
+          acc[dt] = mfma32(tr_frag<RS>(ks_lds, 32 * st + 16 * c, 32 * dt), dsf[c], acc[dt]);
     }
     if (t + 1 < ntiles) {  // the other buffer was last read before the previous barrier
       __bf16* nk = smem + ((t + 1) & 1) * 2 * TILE;
@@ -569,7 +568,7 @@ static void launch_bwd_main(const AttnParams& p, const BwdParams& g, unsigned gr
   if (grid_k > 0)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI>), dim3(grid_k), dim3(kBwdThreads), 0, stream, p, g);
   if (grid_q > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI>), dim3(grid_q), dim3(kBwdThreads), 0, stream, p, g);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI>), dim3(grid_q), dim3(kDqThreads), 0, stream, p, g);
 }
 
 template <int D>
@@ -589,7 +588,7 @@ static hipError_t launch_bwd_d(const AttnParams& p, const BwdParams& g, hipStrea
   if (rows_q > 0)
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows_q + rpb - 1) / rpb)), dim3(256), 0,
                        stream, p, g);
-  const unsigned grid_q = (unsigned)((long long)p.B * p.Hq * ((p.Nq + 127) / 128));
+  const unsigned grid_q = (unsigned)((long long)p.B * p.Hq * ((p.Nq + kDqRows - 1) / kDqRows));
   const unsigned grid_k = (unsigned)((long long)p.B * p.Hkv * ((p.Nk + 127) / 128) * g.kv_parts);
   if (p.alibi)
     launch_bwd_main<D, true>(p, g, grid_k, grid_q, stream);
