@@ -29,7 +29,8 @@ namespace attnfuse {
 
 namespace {
 
-constexpr int kBwdThreads = 256;    // 4 waves (dK/dV)
+constexpr int kBwdThreads = 256;    // default thread count of the row stages
+constexpr int kKvThreads = 512;     // 8 waves, two per SIMD (dK/dV)
 constexpr int kDqThreads = 512;     // 8 waves, two per SIMD (dQ)
 constexpr int kDqRows = 256;        // query rows per dQ workgroup
 
@@ -175,13 +176,14 @@ __device__ __forceinline__ void store_part_row(float* dst, const f32x16 (&acc)[D
 // block rows are keys and the lane's column is query `col`.  L2[r] holds
 // L log2e of the row's query (+inf for rows without keys, so that P = 0),
 // Dl[r] its delta.  MASK applies the key bound and the band per element.
-template <bool MASK, bool ALIBI, bool ROWQ, bool WANTP>
+// Only the chunks C0 .. C1-1 are computed (and only their L2 / Dl entries read).
+template <bool MASK, bool ALIBI, bool ROWQ, bool WANTP, int C0 = 0, int C1 = 2>
 __device__ __forceinline__ void p_ds(const f32x16& s, const f32x16& dp, const float (&L2)[16],
                                      const float (&Dl)[16], int row0, int col, const AttnParams& p,
                                      float slope2, int dpos, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
   const int kb = (threadIdx.x & 63) >> 5;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = C0; c < C1; ++c) {
     uint32_t wp[4], wd[4];
 #pragma unroll
     for (int q2 = 0; q2 < 4; ++q2) {
@@ -375,27 +377,42 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
   }
 }
 
-// ---- pass 2: dK, dV.  4 waves x 32 keys of one kv-head; query tiles of 64. ----
+// ---- pass 2: dK, dV.  8 waves (two per SIMD) over 128 keys of one kv-head;
+// query tiles of 64.  Waves w and w + 4 own the same 32 keys (the result
+// columns) and take the tile's first and second 32 query rows; their dK' and
+// dV accumulators are added through LDS at the end.  K' and V of the block
+// stay in LDS (read as B operands each step) so that a wave needs at most 256
+// registers.
 template <int D, bool ALIBI>
-__global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnParams p, const BwdParams g) {
-  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8, TILE = 64 * RS;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (Q', dO) x 2 buffers
-  __shared__ __attribute__((aligned(16))) float stat[2][2][64];   // [buffer][L log2e, delta][row]
+__global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParams p, const BwdParams g) {
+  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8, TILE = 64 * RS, BLK = 128 * RS;
+  // [K' block | V block] then (Q', dO) x 2 buffers; reused for the final sums
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BLK + 4 * TILE];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][64];  // [buffer][L log2e, delta][row]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lq = lane & 31, lh = lane >> 5;
+  const int kw = wave & 3, st = wave >> 2;  // key group, query half of each tile
   int bk, rank;
   bwd_tile_of(p.B * p.Hkv, bk, rank);  // key block 0 sees the most queries under a causal band
   const int kblk = rank / g.kv_parts, part = rank % g.kv_parts;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
   const int k0 = kblk * 128;
-  const int jw = k0 + 32 * wave;  // the wave's first key
-  const int j = jw + lq;          // the lane's key (result column)
-  const int jc = min(j, p.Nk - 1);
+  const int jw = k0 + 32 * kw;  // the wave's first key
+  const int j = jw + lq;        // the lane's key (result column)
   const int jwl = min(jw + 31, p.Nk - 1);
+  const __bf16* kblk_s = smem;
+  const __bf16* vblk_s = smem + BLK;
+  __bf16* tiles = smem + 2 * BLK;
 
-  bf16x8 kf[NKK], vf[NKK];
-  row_frags<D>(kf, g.kr + b * g.kr_sb + kvh * g.kr_sh, g.kr_sn, jc);
-  row_frags<D>(vf, reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh, p.vsn, jc);
+  {  // K' and V rows of the block (clamped to Nk - 1) into LDS
+    const __bf16* kb = g.kr + b * g.kr_sb + kvh * g.kr_sh;
+    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh;
+    RowStage<D, 128, RS, kKvThreads> ks, vs;
+    ks.load(kb, g.kr_sn, k0, p.Nk);
+    vs.load(vb, p.vsn, k0, p.Nk);
+    ks.store(smem);
+    vs.store(smem + BLK);
+  }
   const int dpos = p.k_pos0 - p.q_pos0;
 
   // Query rows that may see a key of the block: band_lo <= j - i <= band_hi.
@@ -415,7 +432,7 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
   const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 64 + 1 : 0;
   const int t_begin = (int)((long long)part * ntq * p.G / g.kv_parts);
   const int t_end = (int)((long long)(part + 1) * ntq * p.G / g.kv_parts);
-  RowStage<D, 64, RS> qst, dst;
+  RowStage<D, 64, RS, kKvThreads> qst, dst;
   float st_l2 = 0.f, st_delta = 0.f;
   auto load_step = [&](int t) {
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
@@ -430,8 +447,8 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
     }
   };
   auto store_step = [&](int buf) {
-    qst.store(smem + buf * 2 * TILE);
-    dst.store(smem + buf * 2 * TILE + TILE);
+    qst.store(tiles + buf * 2 * TILE);
+    dst.store(tiles + buf * 2 * TILE + TILE);
     if (threadIdx.x < 64) {
       stat[buf][0][threadIdx.x] = st_l2;
       stat[buf][1][threadIdx.x] = st_delta;
@@ -446,53 +463,81 @@ __global__ void __launch_bounds__(kBwdThreads, 1) bwd_dkdv_kernel(const AttnPara
   for (int t = t_begin; t < t_end; ++t) {
     const int buf = (t - t_begin) & 1;
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
-    const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
-    const __bf16* qs = smem + buf * 2 * TILE;
+    const __bf16* qs = tiles + buf * 2 * TILE;
     const __bf16* dos = qs + TILE;
-    const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      // The wave's keys jw .. jwl against query rows ia .. ib.
-      const int ia = q0 + 32 * st, ib = min(ia + 31, p.Nq - 1);
-      const bool skip = ia >= p.Nq || jw >= p.Nk ||
-                        (p.has_band && (jwl - ia < p.band_lo || jw - ib > p.band_hi));
-      if (skip) continue;  // P = dS = 0
+    // The wave's keys jw .. jwl against query rows ia .. ib.
+    const int ia = q0 + 32 * st, ib = min(ia + 31, p.Nq - 1);
+    const bool skip = ia >= p.Nq || jw >= p.Nk ||
+                      (p.has_band && (jwl - ia < p.band_lo || jw - ib > p.band_hi));
+    if (!skip) {  // else P = dS = 0
       const bool full = ia + 31 < p.Nq && jw + 31 < p.Nk &&
                         (!p.has_band || (jw - (ia + 31) >= p.band_lo && jw + 31 - ia <= p.band_hi));
+      const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
       // S and dP (32 query rows x the wave's 32 keys; lane = key column).
       f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sa = mfma32(row_frag<RS>(qs, 32 * st + lq, kk), kf[kk], sa);
-        da = mfma32(row_frag<RS>(dos, 32 * st + lq, kk), vf[kk], da);
+        sa = mfma32(row_frag<RS>(qs, 32 * st + lq, kk), row_frag<RS>(kblk_s, 32 * kw + lq, kk), sa);
+        da = mfma32(row_frag<RS>(dos, 32 * st + lq, kk), row_frag<RS>(vblk_s, 32 * kw + lq, kk), da);
       }
-      float L2[16], Dl[16];
+      // Per 16-row chunk: P and dS (bf16), then dV^T += dO^T P, dK'^T += Q'^T dS.
+      const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
+      auto chunk = [&](auto c_tag) {
+        constexpr int c = decltype(c_tag)::value;
+        float L2[16], Dl[16];  // only rows 8c .. 8c+7 are read
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&stat[buf][0][32 * st + 8 * a + 4 * lh]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&stat[buf][1][32 * st + 8 * a + 4 * lh]);
-        L2[4 * a] = l4.x; L2[4 * a + 1] = l4.y; L2[4 * a + 2] = l4.z; L2[4 * a + 3] = l4.w;
-        Dl[4 * a] = d4.x; Dl[4 * a + 1] = d4.y; Dl[4 * a + 2] = d4.z; Dl[4 * a + 3] = d4.w;
-      }
-      bf16x8 pf[2], dsf[2];
-      if (full)
-        p_ds<false, ALIBI, true, true>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
-      else
-        p_ds<true, ALIBI, true, true>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
-      // dV^T += dO^T P,  dK'^T += Q'^T dS.
+        for (int a4 = 2 * c; a4 < 2 * c + 2; ++a4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&stat[buf][0][32 * st + 8 * a4 + 4 * lh]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&stat[buf][1][32 * st + 8 * a4 + 4 * lh]);
+          L2[4 * a4] = l4.x; L2[4 * a4 + 1] = l4.y; L2[4 * a4 + 2] = l4.z; L2[4 * a4 + 3] = l4.w;
+          Dl[4 * a4] = d4.x; Dl[4 * a4 + 1] = d4.y; Dl[4 * a4 + 2] = d4.z; Dl[4 * a4 + 3] = d4.w;
+        }
+        bf16x8 pf[2], dsf[2];
+        if (full)
+          p_ds<false, ALIBI, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
+        else
+          p_ds<true, ALIBI, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int dt = 0; dt < NDT; ++dt) {
           dv[dt] = mfma32(tr_frag<RS>(dos_lds, 32 * st + 16 * c, 32 * dt), pf[c], dv[dt]);
           dk[dt] = mfma32(tr_frag<RS>(qs_lds, 32 * st + 16 * c, 32 * dt), dsf[c], dk[dt]);
         }
+      };
+      chunk(std::integral_constant<int, 0>{});
+      chunk(std::integral_constant<int, 1>{});
     }
     if (t + 1 < t_end) {  // the other buffer was last read before the previous barrier
       store_step(buf ^ 1);
       if (t + 2 < t_end) load_step(t + 2);
     }
     __syncthreads();
+  }
+  // Waves 4..7 hand their sums to waves 0..3 (dK' in the tile area, dV in the
+  // block area; every wave has passed the loop's last barrier).
+  {
+    float4* red_k = reinterpret_cast<float4*>(tiles) + kw * (NDT * 4 * 64);
+    float4* red_v = reinterpret_cast<float4*>(smem) + kw * (NDT * 4 * 64);
+    if (st == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          red_k[(dt * 4 + g4) * 64 + lane] =
+              make_float4(dk[dt][4 * g4], dk[dt][4 * g4 + 1], dk[dt][4 * g4 + 2], dk[dt][4 * g4 + 3]);
+          red_v[(dt * 4 + g4) * 64 + lane] =
+              make_float4(dv[dt][4 * g4], dv[dt][4 * g4 + 1], dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]);
+        }
+    }
+    __syncthreads();
+    if (st == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 x = red_k[(dt * 4 + g4) * 64 + lane], y = red_v[(dt * 4 + g4) * 64 + lane];
+        dk[dt][4 * g4] += x.x; dk[dt][4 * g4 + 1] += x.y; dk[dt][4 * g4 + 2] += x.z; dk[dt][4 * g4 + 3] += x.w;
+        dv[dt][4 * g4] += y.x; dv[dt][4 * g4 + 1] += y.y; dv[dt][4 * g4 + 2] += y.z; dv[dt][4 * g4 + 3] += y.w;
+      }
   }
   if (j < p.Nk) {
     if (g.kv_parts == 1) {
@@ -566,7 +611,7 @@ template <int D, bool ALIBI>
 static void launch_bwd_main(const AttnParams& p, const BwdParams& g, unsigned grid_k,
                             unsigned grid_q, hipStream_t stream) {
   if (grid_k > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI>), dim3(grid_k), dim3(kBwdThreads), 0, stream, p, g);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI>), dim3(grid_k), dim3(kKvThreads), 0, stream, p, g);
   if (grid_q > 0)
     hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI>), dim3(grid_q), dim3(kDqThreads), 0, stream, p, g);
 }
