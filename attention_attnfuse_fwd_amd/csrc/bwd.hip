@@ -13,7 +13,7 @@
 // back by the negative angle (the rotation is orthogonal).
 //
 // All products run on bf16 MFMA (32x32x16, fp32 accumulate) with P and dS
-// rounded to bf16.  Tiles are staged through padded row-major LDS, double
+// rounded to bf16.  Tiles are staged through swizzled row-major LDS, double
 // buffered: the next tile's global loads are in flight during the current
 // tile's products and one barrier separates tiles.  The transposed operands
 // (dO^T, Q'^T, K'^T) are read with ds_read_b64_tr_b16.  Each wave classifies
@@ -34,18 +34,35 @@ constexpr int kKvThreads = 512;     // 8 waves, two per SIMD (dK/dV)
 constexpr int kDqThreads = 512;     // 8 waves, two per SIMD (dQ)
 constexpr int kDqRows = 256;        // query rows per dQ workgroup
 
+// LDS tiles are unpadded row-major [rows][D] bf16 with the 16-byte chunks of
+// row r permuted by chunk ^ swz(r), chosen so that both access patterns are
+// free of bank conflicts on the 64-bank LDS: a row read (16 lanes, 16
+// consecutive rows, one chunk each) and a transposed read (32 lanes, four
+// consecutive rows, four consecutive chunks each).  D = 128 rows fill the 256
+// bytes of the banks; D = 64 rows share them in pairs.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {  // bytes
+  return r * D * 2 + 16 * (c ^ swz<D>(r));
+}
+
 // Transposed A operand (32 rows of the result x 16 contraction steps) from a
-// row-major bf16 tile T[row][RS] in LDS, for MFMA k index 8*kb + e  <->  tile
-// row row0 + 8*(e/4) + 4*kb + e%4 (the order in which a 32x32 accumulator
-// holds its rows), result row = column col0 + lane % 32.
-template <int RS>
+// tile in LDS, for MFMA k index 8*kb + e  <->  tile row row0 + 8*(e/4) + 4*kb
+// + e%4 (the order in which a 32x32 accumulator holds its rows), result row =
+// column col0 + lane % 32.
+template <int D>
 __device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, int row0, int col0) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, i = lane & 15;
   const int kb = g >> 1, c16 = 16 * (g & 1);
   const int a = i >> 2, bq = i & 3;
-  const uint32_t r1 = tile + (uint32_t)(((row0 + 4 * kb + a) * RS + col0 + c16 + 4 * bq) * 2);
-  const uint32_t r2 = r1 + (uint32_t)(8 * RS * 2);
+  const int r = row0 + 4 * kb + a, col = col0 + c16 + 4 * bq;
+  const uint32_t r1 = tile + (uint32_t)(tile_off<D>(r, col >> 3) + 2 * (col & 7));
+  const uint32_t r2 = tile + (uint32_t)(tile_off<D>(r + 8, col >> 3) + 2 * (col & 7));
   const i16x4 x = lds_read_tr4(r1), y = lds_read_tr4(r2);
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
@@ -54,10 +71,11 @@ __device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, int row0, int col0) {
 
 // Row-major A / B operand: 8 consecutive elements of row `row`, columns
 // 16*kk + 8*kb .. +7.
-template <int RS>
+template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const __bf16* tile, int row, int kk) {
   const int kb = (threadIdx.x & 63) >> 5;
-  return *reinterpret_cast<const bf16x8*>(tile + row * RS + 16 * kk + 8 * kb);
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) +
+                                          tile_off<D>(row, 2 * kk + kb));
 }
 
 // 8 bf16 values of row `row` (global, element stride sn), columns c .. c+7.
@@ -68,8 +86,8 @@ __device__ __forceinline__ uint4 ld_row8(const __bf16* base, long long sn, int r
 // Rows [r0, r0 + R) of a [N, D] bf16 matrix (rows clamped to N - 1), staged
 // in two steps so the next tile's loads can be in flight while the current
 // one is multiplied: load() reads this thread's share into registers,
-// store() writes it to a padded LDS tile.
-template <int D, int R, int RS, int NT = kBwdThreads>
+// store() writes it to a swizzled LDS tile.
+template <int D, int R, int NT = kBwdThreads>
 struct RowStage {
   static constexpr int CPR = D / 8;                          // 16-byte chunks per row
   static constexpr int U = (R * CPR + NT - 1) / NT;
@@ -86,7 +104,8 @@ struct RowStage {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int u = threadIdx.x + NT * k;
-      if ((R * CPR) % NT == 0 || u < R * CPR) st16(tile + (u / CPR) * RS + 8 * (u % CPR), x[k]);
+      if ((R * CPR) % NT == 0 || u < R * CPR)
+        st16(reinterpret_cast<char*>(tile) + tile_off<D>(u / CPR, u % CPR), x[k]);
     }
   }
 };
@@ -268,7 +287,7 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const AttnParams p, cons
 // tile's two 32-key subtiles one after the other: S^T, dP^T, dS^T, dQ'^T.
 template <int D, bool ALIBI>
 __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams p, const BwdParams g) {
-  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8, TILE = 64 * RS;
+  constexpr int NKK = D / 16, NDT = D / 32, TILE = 64 * D;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (K', V) x 2 buffers
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lq = lane & 31;
@@ -314,7 +333,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
   const int kt0 = (j_lo / 64) * 64;
   const int ntiles = j_hi >= j_lo ? (j_hi - kt0) / 64 + 1 : 0;
-  RowStage<D, 64, RS, kDqThreads> kst, vst;
+  RowStage<D, 64, kDqThreads> kst, vst;
   if (ntiles > 0) {
     kst.load(kb, g.kr_sn, kt0, p.Nk);
     vst.load(vb, p.vsn, kt0, p.Nk);
@@ -344,8 +363,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
       f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sa = mfma32(row_frag<RS>(ks, 32 * st + lq, kk), qf[kk], sa);
-        da = mfma32(row_frag<RS>(vs, 32 * st + lq, kk), df[kk], da);
+        sa = mfma32(row_frag<D>(ks, 32 * st + lq, kk), qf[kk], sa);
+        da = mfma32(row_frag<D>(vs, 32 * st + lq, kk), df[kk], da);
       }
       // dS^T = P^T (dP^T - delta), packed to bf16 in 16-key chunks.
       bf16x8 dsf[2], unused[2];
@@ -358,7 +377,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          acc[dt] = mfma32(tr_frag<RS>(ks_lds, 32 * st + 16 * c, 32 * dt), dsf[c], acc[dt]);
+          acc[dt] = mfma32(tr_frag<D>(ks_lds, 32 * st + 16 * c, 32 * dt), dsf[c], acc[dt]);
     }
     if (t + 1 < ntiles) {  // the other buffer was last read before the previous barrier
       __bf16* nk = smem + ((t + 1) & 1) * 2 * TILE;
@@ -385,7 +404,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
 // registers.
 template <int D, bool ALIBI>
 __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParams p, const BwdParams g) {
-  constexpr int NKK = D / 16, NDT = D / 32, RS = D + 8, TILE = 64 * RS, BLK = 128 * RS;
+  constexpr int NKK = D / 16, NDT = D / 32, TILE = 64 * D, BLK = 128 * D;
   // [K' block | V block] then (Q', dO) x 2 buffers; reused for the final sums
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BLK + 4 * TILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][64];  // [buffer][L log2e, delta][row]
@@ -407,7 +426,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
   {  // K' and V rows of the block (clamped to Nk - 1) into LDS
     const __bf16* kb = g.kr + b * g.kr_sb + kvh * g.kr_sh;
     const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh;
-    RowStage<D, 128, RS, kKvThreads> ks, vs;
+    RowStage<D, 128, kKvThreads> ks, vs;
     ks.load(kb, g.kr_sn, k0, p.Nk);
     vs.load(vb, p.vsn, k0, p.Nk);
     ks.store(smem);
@@ -432,7 +451,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
   const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 64 + 1 : 0;
   const int t_begin = (int)((long long)part * ntq * p.G / g.kv_parts);
   const int t_end = (int)((long long)(part + 1) * ntq * p.G / g.kv_parts);
-  RowStage<D, 64, RS, kKvThreads> qst, dst;
+  RowStage<D, 64, kKvThreads> qst, dst;
   float st_l2 = 0.f, st_delta = 0.f;
   auto load_step = [&](int t) {
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
@@ -477,8 +496,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
       f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sa = mfma32(row_frag<RS>(qs, 32 * st + lq, kk), row_frag<RS>(kblk_s, 32 * kw + lq, kk), sa);
-        da = mfma32(row_frag<RS>(dos, 32 * st + lq, kk), row_frag<RS>(vblk_s, 32 * kw + lq, kk), da);
+        sa = mfma32(row_frag<D>(qs, 32 * st + lq, kk), row_frag<D>(kblk_s, 32 * kw + lq, kk), sa);
+        da = mfma32(row_frag<D>(dos, 32 * st + lq, kk), row_frag<D>(vblk_s, 32 * kw + lq, kk), da);
       }
       // Per 16-row chunk: P and dS (bf16), then dV^T += dO^T P, dK'^T += Q'^T dS.
       const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
@@ -499,8 +518,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
           p_ds<true, ALIBI, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          dv[dt] = mfma32(tr_frag<RS>(dos_lds, 32 * st + 16 * c, 32 * dt), pf[c], dv[dt]);
-          dk[dt] = mfma32(tr_frag<RS>(qs_lds, 32 * st + 16 * c, 32 * dt), dsf[c], dk[dt]);
+          dv[dt] = mfma32(tr_frag<D>(dos_lds, 32 * st + 16 * c, 32 * dt), pf[c], dv[dt]);
+          dk[dt] = mfma32(tr_frag<D>(qs_lds, 32 * st + 16 * c, 32 * dt), dsf[c], dk[dt]);
         }
       };
       chunk(std::integral_constant<int, 0>{});
