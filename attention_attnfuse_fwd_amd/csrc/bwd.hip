@@ -78,6 +78,45 @@ __device__ __forceinline__ bf16x8 row_frag(const __bf16* tile, int row, int kk) 
                                           tile_off<D>(row, 2 * kk + kb));
 }
 
+// Per-lane LDS byte offsets, computed once: the swizzle of a row depends only
+// on its index mod 16, so moving by whole 16-row groups (subtile, chunk, wave
+// row block) is a constant added to these.
+//   row[kk]: row_frag of row lq, chunk 2 kk + kb
+//   tr[2 dt + h]: tr_frag of rows 4 kb + a + 8 h, column 32 dt + c16 + 4 bq
+template <int D>
+struct LdsOffsets {
+  uint32_t row[D / 16];
+  uint32_t tr[D / 16];
+  __device__ __forceinline__ LdsOffsets() {
+    const int lane = threadIdx.x & 63;
+    const int lq = lane & 31, kb = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) row[kk] = (uint32_t)tile_off<D>(lq, 2 * kk + kb);
+    const int g = lane >> 4, i = lane & 15;
+    const int tkb = g >> 1, c16 = 16 * (g & 1), a = i >> 2, bq = i & 3;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = 32 * dt + c16 + 4 * bq;
+        tr[2 * dt + h] = (uint32_t)(tile_off<D>(4 * tkb + a + 8 * h, col >> 3) + 2 * (col & 7));
+      }
+  }
+  // A operand from row-major rows row0 + lq (row0 a multiple of 16), chunk kk.
+  __device__ __forceinline__ bf16x8 rowf(uint32_t tile, int row0, int kk) const {
+    return lds_read16(tile + row[kk] + (uint32_t)(row0 * D * 2));
+  }
+  // Transposed A operand: tile rows row0 + 8 (e/4) + 4 kb + e%4 (row0 a multiple
+  // of 16), result rows = columns 32 dt + lane % 32.
+  __device__ __forceinline__ bf16x8 trf(uint32_t tile, int row0, int dt) const {
+    const uint32_t base = tile + (uint32_t)(row0 * D * 2);
+    const i16x4 x = lds_read_tr4(base + tr[2 * dt]), y = lds_read_tr4(base + tr[2 * dt + 1]);
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
 // 8 bf16 values of row `row` (global, element stride sn), columns c .. c+7.
 __device__ __forceinline__ uint4 ld_row8(const __bf16* base, long long sn, int row, int c) {
   return ld16(base + (long long)row * sn + c);
@@ -345,11 +384,10 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
     }
   }
   __syncthreads();
+  const LdsOffsets<D> lo;
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = kt0 + 64 * t;
-    const __bf16* ks = smem + (t & 1) * 2 * TILE;
-    const __bf16* vs = ks + TILE;
-    const uint32_t ks_lds = lds_addr(ks);
+    const uint32_t ks_lds = lds_addr(smem) + (uint32_t)((t & 1) * 2 * TILE * 2), vs_lds = ks_lds + TILE * 2;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       // The wave's rows i0 .. wlast against keys ka .. kl.
@@ -363,8 +401,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
       f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        sa = mfma32(row_frag<D>(ks, 32 * st + lq, kk), qf[kk], sa);
-        da = mfma32(row_frag<D>(vs, 32 * st + lq, kk), df[kk], da);
+        sa = mfma32(lo.rowf(ks_lds, 32 * st, kk), qf[kk], sa);
+        da = mfma32(lo.rowf(vs_lds, 32 * st, kk), df[kk], da);
       }
       // dS^T = P^T (dP^T - delta), packed to bf16 in 16-key chunks.
       bf16x8 dsf[2], unused[2];
@@ -372,12 +410,13 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
         p_ds<false, ALIBI, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, unused, dsf);
       else
         p_ds<true, ALIBI, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, unused, dsf);
-      // dQ'^T += K'^T dS^T.
+      // dQ'^T += K'^T dS^T (chunk-major, so that consecutive products
+      // update different accumulators).
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[dt] = mfma32(tr_frag<D>(ks_lds, 32 * st + 16 * c, 32 * dt), dsf[c], acc[dt]);
+        for (int dt = 0; dt < NDT; ++dt)
+          acc[dt] = mfma32(lo.trf(ks_lds, 32 * st + 16 * c, dt), dsf[c], acc[dt]);
     }
     if (t + 1 < ntiles) {  // the other buffer was last read before the previous barrier
       __bf16* nk = smem + ((t + 1) & 1) * 2 * TILE;
@@ -484,6 +523,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
     const __bf16* qs = tiles + buf * 2 * TILE;
     const __bf16* dos = qs + TILE;
+    const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
     // The wave's keys jw .. jwl against query rows ia .. ib.
     const int ia = q0 + 32 * st, ib = min(ia + 31, p.Nq - 1);
     const bool skip = ia >= p.Nq || jw >= p.Nk ||
@@ -500,7 +540,6 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
         da = mfma32(row_frag<D>(dos, 32 * st + lq, kk), row_frag<D>(vblk_s, 32 * kw + lq, kk), da);
       }
       // Per 16-row chunk: P and dS (bf16), then dV^T += dO^T P, dK'^T += Q'^T dS.
-      const uint32_t qs_lds = lds_addr(qs), dos_lds = lds_addr(dos);
       auto chunk = [&](auto c_tag) {
         constexpr int c = decltype(c_tag)::value;
         float L2[16], Dl[16];  // only rows 8c .. 8c+7 are read
