@@ -75,3 +75,30 @@ def test_backward_rows_without_keys_get_zero_dq():
     got, ref = _run(c, seed=3)
     assert np.all(got[0][:, :, :3] == 0.0)
     _check("rows_without_keys", got, ref)
+
+
+def test_backward_full_size_bench_config():
+    """Llama-3-8B shape (B=1, Hq=32, Hkv=8, N=4096, D=128, RoPE theta=5e5,
+    causal) in the launch configuration the benchmark times (workspace from
+    bwd_workspace_size, so the split key blocks and their reduction run):
+    full gradients of two kv-head groups (q-heads 0-3 / kv-head 0 and
+    q-heads 28-31 / kv-head 7) against the oracle."""
+    w = workloads.WORKLOADS["llama3_8b_rope_causal_n4096"]
+    inp = workloads.make_inputs(w)
+    log("case bwd full size llama3_8b_rope_causal_n4096")
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q_dev, inp.k_dev, inp.v_dev))
+    rng = np.random.default_rng(3)
+    dout = torch.from_numpy(rng.standard_normal(q.shape, dtype=np.float32)).cuda().to(torch.bfloat16)
+    kw = dict(causal=w.causal, window=w.window, rope_theta=w.rope_theta)
+    out, lse = af.fwd(q, k, v, return_lse=True, **kw)
+    ws = torch.empty(af.bwd_workspace_size(q, k, v, **kw) // 4 + 4, dtype=torch.float32, device="cuda")
+    dq, dk, dv = af.bwd(q, k, v, out, dout, lse, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    qh, kh, vh, gh = host(q), host(k), host(v), host(dout)
+    G = w.Hq // w.Hkv
+    for kvh in (0, w.Hkv - 1):
+        hs = slice(kvh * G, (kvh + 1) * G)
+        ref = oracle.attention_backward(qh[:, hs], kh[:, kvh:kvh + 1], vh[:, kvh:kvh + 1], gh[:, hs],
+                                        rope_theta=w.rope_theta, causal=True)
+        got = (host(dq[:, hs]), host(dk[:, kvh:kvh + 1]), host(dv[:, kvh:kvh + 1]))
+        _check(f"full_size_kvh{kvh}", got, ref)
