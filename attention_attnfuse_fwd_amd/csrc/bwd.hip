@@ -328,7 +328,8 @@ template <int D, bool ALIBI>
 __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams p, const BwdParams g) {
   constexpr int NKK = D / 16, NDT = D / 32, TILE = 64 * D;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (K', V) x 2 buffers
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int lq = lane & 31;
   const int nqb = (p.Nq + kDqRows - 1) / kDqRows;
   int bh, rank;
@@ -447,7 +448,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
   // [K' block | V block] then (Q', dO) x 2 buffers; reused for the final sums
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BLK + 4 * TILE];
   __shared__ __attribute__((aligned(16))) float stat[2][2][64];  // [buffer][L log2e, delta][row]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int lq = lane & 31, lh = lane >> 5;
   const int kw = wave & 3, st = wave >> 2;  // key group, query half of each tile
   int bk, rank;
