@@ -79,6 +79,8 @@ class VariantDesc(ctypes.Structure):
         ("bs_head_stride", ctypes.c_int64),
         ("bs_nnz", ctypes.c_int64),
         ("lse", ctypes.c_void_p),
+        ("tile_waves", ctypes.c_int32),
+        ("tile_heads", ctypes.c_int32),
     ]
 
     @classmethod

@@ -209,15 +209,43 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
       }
     }
     if (!found) return ATTNFUSE_ERR_UNSUPPORTED;
-  } else {
-    const int rb_need = (d->Nq + 31) / 32;
-    while (NW > 2 && NW > hp && (NW / hp) / 2 >= rb_need) NW /= 2;
   }
   const bool rope = d->rope != 0;
   const bool scoremod = d->alibi_slopes != nullptr || d->bias != nullptr;
+  if (!use_sparse) {
+    // Tile table, from the tile sweep on MI355X (GPT-2-small grid, B=4 H=12
+    // D=64 N=512..4096 over seven variants, and the Llama-3-8B shape): eight
+    // waves with as many q-heads of a group as fit, unless that under-fills
+    // the 256 CUs: halve the waves while the grid has fewer than 128
+    // workgroups (or a workgroup would hold more row blocks than there are
+    // rows); a score modifier (ALiBi, bias) takes four waves when eight
+    // would leave fewer than 256 workgroups.
+    auto grid_of = [&](int nw) {
+      const int h2 = hp < nw ? hp : nw;
+      const long long rows = 32LL * (nw / h2);
+      return (long long)d->B * d->Hkv * (p.G / h2) * ((d->Nq + rows - 1) / rows);
+    };
+    const int rb_need = (d->Nq + 31) / 32;
+    while (NW > 2 && NW > hp && (NW / hp) / 2 >= rb_need) NW /= 2;
+    while (NW > 2 && grid_of(NW) < 128) NW /= 2;
+    if (scoremod && NW == 8 && grid_of(8) < 256) NW = 4;
+    if (hp > NW) hp = NW;
+  }
   if (!attnfuse::fwd_bf16_supported(d->D, NW, rope, scoremod, use_sparse)) {
     NW /= 2;  // fewer waves, twice the registers each
     if (hp > NW) hp = NW;
+  }
+  if (d->tile_waves != 0 || d->tile_heads != 0) {  // caller's tile choice
+    const int nw = d->tile_waves != 0 ? d->tile_waves : NW;
+    int h2 = d->tile_heads != 0 ? d->tile_heads : (hp < nw ? hp : nw);
+    const bool pow2 = (nw == 2 || nw == 4 || nw == 8) && (h2 == 1 || h2 == 2 || h2 == 4 || h2 == 8);
+    if (!pow2 || h2 > nw || p.G % h2 != 0) return ATTNFUSE_ERR_UNSUPPORTED;
+    if (use_sparse && (d->bs_block_m % (32 * (nw / h2)) != 0 || (d->bs_head_stride > 0 && h2 != 1)))
+      return ATTNFUSE_ERR_UNSUPPORTED;
+    if (!attnfuse::fwd_bf16_supported(d->D, nw, rope, scoremod, use_sparse))
+      return ATTNFUSE_ERR_UNSUPPORTED;
+    NW = nw;
+    hp = h2;
   }
   p.hp = hp;
   const int RB = NW / hp;

@@ -211,11 +211,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         window: int = 0, rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
         alibi_slopes=None, bias=None, block_mask: Optional[BlockMask] = None,
         scale: Optional[float] = None, return_lse: bool = False,
-        out: Optional[torch.Tensor] = None, decode_fast_path: bool = True):
+        out: Optional[torch.Tensor] = None, decode_fast_path: bool = True,
+        tile: Optional[tuple] = None):
     """Fused attention forward; q [B, Hq, Nq, D], k / v [B, Hkv, Nk, D] on the GPU.
 
     A single query row (Nq == 1, bf16, no bias or block mask) takes the split-KV
-    decode path, as the pages' runtime dispatch does.
+    decode path, as the pages' runtime dispatch does.  ``tile = (waves, heads)``
+    overrides the library's tile table for the bf16 prefill kernel.
     """
     _check_inputs(q, k, v)
     if (decode_fast_path and q.shape[2] == 1 and q.dtype == torch.bfloat16 and bias is None
@@ -231,6 +233,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
                    rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0,
                    alibi_slopes=alibi_slopes, bias=bias, block_mask=block_mask, lse=lse,
                    keep=keep)
+    if tile is not None:
+        d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
     _check(_abi.load().attnfuse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(d),
                                     _stream(q.device)), "fwd")
     return (out, lse) if return_lse else out

@@ -147,6 +147,19 @@ typedef struct attnfuse_variant_desc {
    * optional fp32 output [B, Hq, Nq], contiguous.  Rows with no visible key
    * get -inf (and an all-zero output row).  NULL = not written. */
   float* lse;
+
+  /* Tile choice of attnfuse_fwd's bf16 prefill kernel ("3.2 From DSL to
+   * Kernel", the Tile pass): tile_waves = waves per workgroup (2, 4 or 8),
+   * tile_heads = q-heads of a GQA group per workgroup (1, 2, 4 or 8, dividing
+   * Hq / Hkv, at most tile_waves); the workgroup covers 32 * tile_waves /
+   * tile_heads query rows against 64-key tiles.  0 = the library's dispatch
+   * table (from a tile sweep on MI355X).  A choice the kernels cannot run
+   * (a block mask whose bs_block_m is not a multiple of the workgroup's rows,
+   * per-head masks with tile_heads > 1, or a variant without an instance at
+   * that size) returns ATTNFUSE_ERR_UNSUPPORTED.  Ignored by the other entry
+   * points and by fp32. */
+  int32_t tile_waves;
+  int32_t tile_heads;
 } attnfuse_variant_desc;
 
 /* Fused attention forward: out = attention(q, k, v) under `desc`.

@@ -80,6 +80,13 @@ def _fwd(lib, d):
     return lib.attnfuse_fwd(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), None)
 
 
+@pytest.mark.parametrize("tile", [(3, 1), (8, 3), (2, 4), (16, 1), (4, 4)])
+def test_unsupported_tile_choices_are_rejected_before_launch(lib, tile):
+    # the default descriptor has G = Hq / Hkv = 2: tile_heads 4 does not divide it
+    d = _good_desc(tile_waves=tile[0], tile_heads=tile[1])
+    assert _fwd(lib, d) == _abi.ERR_UNSUPPORTED
+
+
 def test_empty_query_is_ok_without_work(lib):
     assert _fwd(lib, _good_desc(Nq=0)) == _abi.OK
 

@@ -105,6 +105,27 @@ WORKLOADS = {
         seed=5, rope_theta=500000.0, q_pos0=32768, k_pos0=0, decode_splits=64),
 }
 
+# Second grid: the GPT-2-small geometry of the pages' head-to-head tables
+# ("6.1 Forward Head-to-Head on Ampere", Table 6: Dense, Causal, SW W=256,
+# Causal+ALiBi; "6.2 RoPE on Ampere", Table 7: RoPE + Dense / Causal / SW),
+# B=4, H=12, D=64, N in {512, 1024, 2048, 4096}, in bf16 (the pages: fp16).
+GPT2_VARIANTS = {
+    "dense": dict(),
+    "causal": dict(causal=True),
+    "sw256": dict(window=256),
+    "causal_alibi": dict(causal=True, alibi=True),
+    "rope_dense": dict(rope_theta=10000.0),
+    "rope_causal": dict(rope_theta=10000.0, causal=True),
+    "rope_sw256": dict(rope_theta=10000.0, window=256),
+}
+GPT2_NS = (512, 1024, 2048, 4096)
+
+
+def gpt2_small(variant: str, N: int) -> Workload:
+    """GPT-2-small geometry workload (seed 6 for every cell)."""
+    return Workload(f"gpt2s_{variant}_n{N}", "bf16", B=4, Hq=12, Hkv=12, Nq=N, Nk=N, D=64,
+                    seed=6, **GPT2_VARIANTS[variant])
+
 
 def alibi_slopes(H: int) -> np.ndarray:
     """ALiBi head slopes 2^(-8h/H) for h = 1..H, as float32 (index 0 = head 0)."""
