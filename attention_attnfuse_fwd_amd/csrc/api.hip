@@ -343,7 +343,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
-  if (d->dtype != ATTNFUSE_BF16 || d->bias || d->bs_row_ptr) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->dtype != ATTNFUSE_BF16 || d->bs_row_ptr) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->Nq > 0 && (!q || !out || !dout || !lse || !dq)) return ATTNFUSE_ERR_INVALID;
   if (d->Nk > 0 && (!k || !v || !dk || !dv)) return ATTNFUSE_ERR_INVALID;
   if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;

@@ -226,6 +226,8 @@ __device__ __forceinline__ void store_part_row(float* dst, const f32x16 (&acc)[D
           make_float4(acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
 }
 
+constexpr int kSmAlibi = 1, kSmBias = 2;
+
 // P = exp2(S scale log2e - L log2e) and dS = P (dP - delta) for one 32x32
 // block held as accumulators s (scores) and dp, packed to bf16 as two
 // 16-row MFMA B operands (chunk c holds the accumulator rows 8c .. 8c+7).
@@ -235,10 +237,14 @@ __device__ __forceinline__ void store_part_row(float* dst, const f32x16 (&acc)[D
 // L log2e of the row's query (+inf for rows without keys, so that P = 0),
 // Dl[r] its delta.  MASK applies the key bound and the band per element.
 // Only the chunks C0 .. C1-1 are computed (and only their L2 / Dl entries read).
-template <bool MASK, bool ALIBI, bool ROWQ, bool WANTP, int C0 = 0, int C1 = 2>
+// SM: score modifiers, kSmAlibi (slope2 = ALiBi slope * log2 e, dpos = key
+// position - query position of index 0 pairs) and kSmBias (bias_bh = the
+// (b, h) plane of the additive bias).
+template <bool MASK, int SM, bool ROWQ, bool WANTP, int C0 = 0, int C1 = 2>
 __device__ __forceinline__ void p_ds(const f32x16& s, const f32x16& dp, const float (&L2)[16],
                                      const float (&Dl)[16], int row0, int col, const AttnParams& p,
-                                     float slope2, int dpos, bf16x8 (&pf)[2], bf16x8 (&dsf)[2]) {
+                                     float slope2, int dpos, const float* bias_bh, bf16x8 (&pf)[2],
+                                     bf16x8 (&dsf)[2]) {
   const int kb = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int c = C0; c < C1; ++c) {
@@ -252,7 +258,10 @@ __device__ __forceinline__ void p_ds(const f32x16& s, const f32x16& dp, const fl
         const int row = row0 + 8 * (r / 4) + 4 * kb + r % 4;
         const int i = ROWQ ? row : col, j = ROWQ ? col : row;
         float x = __builtin_fmaf(s[r], p.scale_log2, -L2[r]);
-        if (ALIBI) x = __builtin_fmaf(slope2, (float)(j - i + dpos), x);
+        if (SM & kSmAlibi) x = __builtin_fmaf(slope2, (float)(j - i + dpos), x);
+        if (SM & kSmBias)  // indices clamped: masked-out rows and keys still read in bounds
+          x = __builtin_fmaf(bias_bh[(long long)min(i, p.Nq - 1) * p.bsi + (long long)min(j, p.Nk - 1) * p.bsj],
+                             kLog2e, x);
         float pr = fast_exp2(x);
         if (MASK) {
           const bool ok = (j < p.Nk) & (j - i >= p.band_lo) & (j - i <= p.band_hi);
@@ -324,7 +333,7 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const AttnParams p, cons
 // key tiles of 64.  Each wave keeps its rows' Q' and dO as MFMA operands and
 // its dQ' accumulators in registers (at most 256 per wave), and walks the
 // tile's two 32-key subtiles one after the other: S^T, dP^T, dS^T, dQ'^T.
-template <int D, bool ALIBI>
+template <int D, int SM>
 __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams p, const BwdParams g) {
   constexpr int NKK = D / 16, NDT = D / 32, TILE = 64 * D;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (K', V) x 2 buffers
@@ -358,7 +367,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
     L2[r] = (i < p.Nq && lse != -INFINITY) ? lse * kLog2e : INFINITY;
     Dl[r] = g.delta[row_id];
   }
-  const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
+  const float slope2 = (SM & kSmAlibi) ? p.alibi[h] * kLog2e : 0.f;
+  const float* bias_bh = (SM & kSmBias) ? p.bias + b * p.bsb + h * p.bsh : nullptr;
   const int dpos = p.k_pos0 - p.q_pos0;
 
   // Key tiles any row of the block may see (the band is j - i in index space).
@@ -408,9 +418,9 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
       // dS^T = P^T (dP^T - delta), packed to bf16 in 16-key chunks.
       bf16x8 dsf[2], unused[2];
       if (full)
-        p_ds<false, ALIBI, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, unused, dsf);
+        p_ds<false, SM, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, bias_bh, unused, dsf);
       else
-        p_ds<true, ALIBI, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, unused, dsf);
+        p_ds<true, SM, false, false>(sa, da, L2, Dl, ka, i, p, slope2, dpos, bias_bh, unused, dsf);
       // dQ'^T += K'^T dS^T (chunk-major, so that consecutive products
       // update different accumulators).
 #pragma unroll
@@ -442,7 +452,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
 // dV accumulators are added through LDS at the end.  K' and V of the block
 // stay in LDS (read as B operands each step) so that a wave needs at most 256
 // registers.
-template <int D, bool ALIBI>
+template <int D, int SM>
 __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParams p, const BwdParams g) {
   constexpr int NKK = D / 16, NDT = D / 32, TILE = 64 * D, BLK = 128 * D;
   // [K' block | V block] then (Q', dO) x 2 buffers; reused for the final sums
@@ -533,7 +543,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
     if (!skip) {  // else P = dS = 0
       const bool full = ia + 31 < p.Nq && jw + 31 < p.Nk &&
                         (!p.has_band || (jw - (ia + 31) >= p.band_lo && jw + 31 - ia <= p.band_hi));
-      const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
+      const float slope2 = (SM & kSmAlibi) ? p.alibi[h] * kLog2e : 0.f;
+      const float* bias_bh = (SM & kSmBias) ? p.bias + b * p.bsb + h * p.bsh : nullptr;
       // S and dP (32 query rows x the wave's 32 keys; lane = key column).
       f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
@@ -554,9 +565,9 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
         }
         bf16x8 pf[2], dsf[2];
         if (full)
-          p_ds<false, ALIBI, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
+          p_ds<false, SM, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, bias_bh, pf, dsf);
         else
-          p_ds<true, ALIBI, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, pf, dsf);
+          p_ds<true, SM, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, bias_bh, pf, dsf);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           dv[dt] = mfma32(tr_frag<D>(dos_lds, 32 * st + 16 * c, 32 * dt), pf[c], dv[dt]);
@@ -667,13 +678,13 @@ __global__ void __launch_bounds__(256) bwd_kv_reduce_kernel(const AttnParams p, 
   st16(dvd + D / 2 + 8 * c, make_uint4(wv1[0], wv1[1], wv1[2], wv1[3]));
 }
 
-template <int D, bool ALIBI>
+template <int D, int SM>
 static void launch_bwd_main(const AttnParams& p, const BwdParams& g, unsigned grid_k,
                             unsigned grid_q, hipStream_t stream) {
   if (grid_k > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, ALIBI>), dim3(grid_k), dim3(kKvThreads), 0, stream, p, g);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SM>), dim3(grid_k), dim3(kKvThreads), 0, stream, p, g);
   if (grid_q > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, ALIBI>), dim3(grid_q), dim3(kDqThreads), 0, stream, p, g);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, SM>), dim3(grid_q), dim3(kDqThreads), 0, stream, p, g);
 }
 
 template <int D>
@@ -695,10 +706,11 @@ static hipError_t launch_bwd_d(const AttnParams& p, const BwdParams& g, hipStrea
                        stream, p, g);
   const unsigned grid_q = (unsigned)((long long)p.B * p.Hq * ((p.Nq + kDqRows - 1) / kDqRows));
   const unsigned grid_k = (unsigned)((long long)p.B * p.Hkv * ((p.Nk + 127) / 128) * g.kv_parts);
-  if (p.alibi)
-    launch_bwd_main<D, true>(p, g, grid_k, grid_q, stream);
-  else
-    launch_bwd_main<D, false>(p, g, grid_k, grid_q, stream);
+  const int sm = (p.alibi ? kSmAlibi : 0) | (p.bias ? kSmBias : 0);
+  if (sm == 0) launch_bwd_main<D, 0>(p, g, grid_k, grid_q, stream);
+  else if (sm == kSmAlibi) launch_bwd_main<D, kSmAlibi>(p, g, grid_k, grid_q, stream);
+  else if (sm == kSmBias) launch_bwd_main<D, kSmBias>(p, g, grid_k, grid_q, stream);
+  else launch_bwd_main<D, kSmAlibi | kSmBias>(p, g, grid_k, grid_q, stream);
   if (g.kv_parts > 1 && rows_k > 0)
     hipLaunchKernelGGL(bwd_kv_reduce_kernel<D>, dim3((unsigned)((rows_k * CH + 255) / 256)), dim3(256), 0,
                        stream, p, g);

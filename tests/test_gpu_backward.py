@@ -27,6 +27,9 @@ CASES = {
     "rope_offsets_prefix_d64_gqa8": dict(B=1, Hq=8, Hkv=1, Nq=90, Nk=300, D=64, rope_theta=5e5,
                                          causal=True, q_pos0=210, k_pos0=0),
     "noncausal_window_d128": dict(B=1, Hq=2, Hkv=1, Nq=130, Nk=190, D=128, window=40, rope_theta=500.0),
+    "bias_d64_gqa": dict(B=2, Hq=4, Hkv=2, Nq=140, Nk=170, D=64, bias="full"),
+    "bias_broadcast_rope_causal_alibi_d128": dict(B=1, Hq=2, Hkv=2, Nq=200, Nk=200, D=128, bias="rows",
+                                                  rope_theta=1e4, causal=True, alibi=True),
 }
 
 
@@ -42,6 +45,14 @@ def _run(c, seed):
         sl = workloads.alibi_slopes(Hq)
         kw["alibi_slopes"] = torch.from_numpy(sl).cuda()
         okw["alibi_slopes"] = sl.astype(np.float64)
+    if c.get("bias") == "full":  # one bias plane per (b, h)
+        bias = rng.standard_normal((B, Hq, Nq, Nk)).astype(np.float32)
+        kw["bias"] = torch.from_numpy(bias).cuda()
+        okw["bias"] = bias.astype(np.float64)
+    elif c.get("bias") == "rows":  # one [Nq, Nk] plane broadcast over b and h (zero strides)
+        bias = rng.standard_normal((Nq, Nk)).astype(np.float32)
+        kw["bias"] = torch.from_numpy(bias).cuda().expand(B, Hq, Nq, Nk)
+        okw["bias"] = np.broadcast_to(bias.astype(np.float64), (B, Hq, Nq, Nk))
     qd, kd, vd, gd = (to_dev(x, "bf16") for x in (qb, kb, vb, gb))
     out, lse = af.fwd(qd, kd, vd, return_lse=True, decode_fast_path=False, **kw)
     dq, dk, dv = af.bwd(qd, kd, vd, out, gd, lse, **kw)
