@@ -343,7 +343,8 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
-  if (d->dtype != ATTNFUSE_BF16 || d->bs_row_ptr) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->dtype != ATTNFUSE_BF16) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->bs_row_ptr && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->Nq > 0 && (!q || !out || !dout || !lse || !dq)) return ATTNFUSE_ERR_INVALID;
   if (d->Nk > 0 && (!k || !v || !dk || !dv)) return ATTNFUSE_ERR_INVALID;
   if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
@@ -355,6 +356,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return ATTNFUSE_ERR_WORKSPACE;
   AttnParams p = base_params(q, k, v, const_cast<void*>(out), d);
+  if (d->Nk == 0) p.row_ptr = nullptr;  // no keys: nothing to visit
   p.lse = const_cast<float*>(lse);
   attnfuse::BwdParams g{};
   g.dout = static_cast<const __bf16*>(dout);
@@ -383,7 +385,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
     g.qr_sb = d->q_stride[0]; g.qr_sh = d->q_stride[1]; g.qr_sn = d->q_stride[2];
     g.kr_sb = d->k_stride[0]; g.kr_sh = d->k_stride[1]; g.kr_sn = d->k_stride[2];
   }
-  const long long gq = (long long)d->B * d->Hq * ((d->Nq + 255) / 256);
+  const long long gq = (long long)d->B * d->Hq * ((d->Nq + 63) / 64);
   const long long gk = (long long)d->B * d->Hkv * ((d->Nk + 127) / 128) * g.kv_parts;
   // The rotation and row-reduction passes use at most one 256-thread block
   // per 16 rows (D = 128 row reduction).

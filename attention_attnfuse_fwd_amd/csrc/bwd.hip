@@ -278,6 +278,25 @@ __device__ __forceinline__ void p_ds(const f32x16& s, const f32x16& dp, const fl
   }
 }
 
+// CSR row of query block qb for q-head h: offsets [beg, end) into col_idx,
+// clamped to [0, nnz] (a malformed mask gives wrong numbers, never an
+// out-of-bounds read).  Columns are clamped to [0, number of key blocks].
+struct CsrRow {
+  int beg, end;
+};
+typedef __attribute__((address_space(4))) const int* csr_ptr_t;  // scalar loads
+__device__ __forceinline__ CsrRow csr_row(const AttnParams& p, int h, int qb) {
+  const int* rp = p.row_ptr + (p.bs_head_stride ? (long long)h * p.bs_head_stride : 0);
+  const long long nnz = p.bs_nnz;
+  const long long a = min(max((long long)((csr_ptr_t)rp)[qb], 0LL), nnz);
+  const long long e = min(max((long long)((csr_ptr_t)rp)[qb + 1], a), nnz);
+  return CsrRow{(int)a, (int)e};
+}
+__device__ __forceinline__ int csr_col(const AttnParams& p, int e) {
+  const int nkb = (p.Nk + p.bn - 1) / p.bn;
+  return min(max(((csr_ptr_t)p.col_idx)[e], 0), nkb);
+}
+
 }  // namespace
 
 // ---- pass 0: Q' / K' = RoPE(x) into a contiguous [B][H][N][D] copy ----
@@ -333,20 +352,24 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const AttnParams p, cons
 // key tiles of 64.  Each wave keeps its rows' Q' and dO as MFMA operands and
 // its dQ' accumulators in registers (at most 256 per wave), and walks the
 // tile's two 32-key subtiles one after the other: S^T, dP^T, dS^T, dQ'^T.
-template <int D, int SM>
-__global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams p, const BwdParams g) {
+// With a block mask (SPARSE) a workgroup is 2 waves = 64 rows, inside one
+// CSR block row, and visits only that row's listed key blocks.
+template <int D, int SM, bool SPARSE>
+__global__ void __launch_bounds__(SPARSE ? 128 : kDqThreads, 1) bwd_dq_kernel(const AttnParams p,
+                                                                            const BwdParams g) {
   constexpr int NKK = D / 16, NDT = D / 32, TILE = 64 * D;
+  constexpr int NT = SPARSE ? 128 : kDqThreads, ROWS = NT / 2;
   __shared__ __attribute__((aligned(16))) __bf16 smem[4 * TILE];  // (K', V) x 2 buffers
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
   const int lq = lane & 31;
-  const int nqb = (p.Nq + kDqRows - 1) / kDqRows;
+  const int nqb = (p.Nq + ROWS - 1) / ROWS;
   int bh, rank;
   bwd_tile_of(p.B * p.Hq, bh, rank);
   const int qblk = nqb - 1 - rank;  // later query blocks see more keys under a causal band
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.G;
-  const int r0 = qblk * kDqRows;
+  const int r0 = qblk * ROWS;
   const int i0 = r0 + 32 * wave;  // the wave's first row
   const int i = i0 + lq;
   const int iq = min(i, p.Nq - 1);
@@ -371,33 +394,48 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
   const float* bias_bh = (SM & kSmBias) ? p.bias + b * p.bsb + h * p.bsh : nullptr;
   const int dpos = p.k_pos0 - p.q_pos0;
 
-  // Key tiles any row of the block may see (the band is j - i in index space).
-  const int wg_last = min(r0 + kDqRows - 1, p.Nq - 1);
-  int j_lo = 0, j_hi = p.Nk - 1;
-  if (p.has_band) {
-    j_lo = max(j_lo, (int)max((long long)r0 + p.band_lo, 0LL));
-    j_hi = min(j_hi, (int)min((long long)wg_last + p.band_hi, (long long)p.Nk - 1));
+  // Key tiles the block visits: the band's range (the band is j - i in index
+  // space), or the listed key blocks of the block's CSR row.
+  const int wg_last = min(r0 + ROWS - 1, p.Nq - 1);
+  int ntiles, kt0 = 0, s_begin = 0, tpb = 1;
+  if (SPARSE) {
+    const CsrRow row = csr_row(p, h, r0 / p.bm);
+    s_begin = row.beg;
+    tpb = p.bn / 64;
+    ntiles = (row.end - row.beg) * tpb;
+  } else {
+    int j_lo = 0, j_hi = p.Nk - 1;
+    if (p.has_band) {
+      j_lo = max(j_lo, (int)max((long long)r0 + p.band_lo, 0LL));
+      j_hi = min(j_hi, (int)min((long long)wg_last + p.band_hi, (long long)p.Nk - 1));
+    }
+    kt0 = (j_lo / 64) * 64;
+    ntiles = j_hi >= j_lo ? (j_hi - kt0) / 64 + 1 : 0;
   }
+  // First key of tile t; a listed column past the keys lands at k0 >= Nk and
+  // is skipped (its loads are clamped to the last key).
+  auto tile_k0 = [&](int t) -> int {
+    if (SPARSE) return csr_col(p, s_begin + t / tpb) * p.bn + (t % tpb) * 64;
+    return kt0 + 64 * t;
+  };
   f32x16 acc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
-  const int kt0 = (j_lo / 64) * 64;
-  const int ntiles = j_hi >= j_lo ? (j_hi - kt0) / 64 + 1 : 0;
-  RowStage<D, 64, kDqThreads> kst, vst;
+  RowStage<D, 64, NT> kst, vst;
   if (ntiles > 0) {
-    kst.load(kb, g.kr_sn, kt0, p.Nk);
-    vst.load(vb, p.vsn, kt0, p.Nk);
+    kst.load(kb, g.kr_sn, tile_k0(0), p.Nk);
+    vst.load(vb, p.vsn, tile_k0(0), p.Nk);
     kst.store(smem);
     vst.store(smem + TILE);
     if (ntiles > 1) {
-      kst.load(kb, g.kr_sn, kt0 + 64, p.Nk);
-      vst.load(vb, p.vsn, kt0 + 64, p.Nk);
+      kst.load(kb, g.kr_sn, tile_k0(1), p.Nk);
+      vst.load(vb, p.vsn, tile_k0(1), p.Nk);
     }
   }
   __syncthreads();
   const LdsOffsets<D> lo;
   for (int t = 0; t < ntiles; ++t) {
-    const int k0 = kt0 + 64 * t;
+    const int k0 = tile_k0(t);
     const uint32_t ks_lds = lds_addr(smem) + (uint32_t)((t & 1) * 2 * TILE * 2), vs_lds = ks_lds + TILE * 2;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -434,8 +472,8 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
       kst.store(nk);
       vst.store(nk + TILE);
       if (t + 2 < ntiles) {
-        kst.load(kb, g.kr_sn, k0 + 128, p.Nk);
-        vst.load(vb, p.vsn, k0 + 128, p.Nk);
+        kst.load(kb, g.kr_sn, tile_k0(t + 2), p.Nk);
+        vst.load(vb, p.vsn, tile_k0(t + 2), p.Nk);
       }
     }
     __syncthreads();
@@ -452,7 +490,7 @@ __global__ void __launch_bounds__(kDqThreads, 1) bwd_dq_kernel(const AttnParams 
 // dV accumulators are added through LDS at the end.  K' and V of the block
 // stay in LDS (read as B operands each step) so that a wave needs at most 256
 // registers.
-template <int D, int SM>
+template <int D, int SM, bool SPARSE>
 __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParams p, const BwdParams g) {
   constexpr int NKK = D / 16, NDT = D / 32, TILE = 64 * D, BLK = 128 * D;
   // [K' block | V block] then (Q', dO) x 2 buffers; reused for the final sums
@@ -524,14 +562,38 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
       stat[buf][1][threadIdx.x] = st_delta;
     }
   };
-  if (t_end > t_begin) {
-    load_step(t_begin);
+  // With a block mask a step is visited only when its CSR row lists one of
+  // the workgroup's key blocks (bit 0: the block of key k0, bit 1: the block
+  // of the last key; the same block sets both), and a wave computes only when
+  // its own key block is listed.  Dense steps are all visited.
+  const int kb_lo = SPARSE ? k0 / p.bn : 0, kb_hi = SPARSE ? k_last / p.bn : 0;
+  const int wbit = (SPARSE && jw / p.bn != kb_lo) ? 2 : 1;
+  auto vis = [&](int t) -> int {
+    if (!SPARSE) return 3;
+    const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
+    const CsrRow row = csr_row(p, h, q0 / p.bm);
+    int m = 0;
+    for (int e = row.beg; e < row.end; ++e) {
+      const int c = csr_col(p, e);
+      m |= (c == kb_lo ? 1 : 0) | (c == kb_hi ? 2 : 0);
+    }
+    return m;
+  };
+  auto next_vis = [&](int t) {
+    if (SPARSE)
+      while (t < t_end && vis(t) == 0) ++t;
+    return t;
+  };
+  int cur = next_vis(t_begin);
+  int nxt = cur < t_end ? next_vis(cur + 1) : t_end;
+  if (cur < t_end) {
+    load_step(cur);
     store_step(0);
-    if (t_end > t_begin + 1) load_step(t_begin + 1);
+    if (nxt < t_end) load_step(nxt);
   }
   __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
+  for (int buf = 0; cur < t_end; buf ^= 1) {
+    const int t = cur;
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
     const __bf16* qs = tiles + buf * 2 * TILE;
     const __bf16* dos = qs + TILE;
@@ -539,7 +601,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
     // The wave's keys jw .. jwl against query rows ia .. ib.
     const int ia = q0 + 32 * st, ib = min(ia + 31, p.Nq - 1);
     const bool skip = ia >= p.Nq || jw >= p.Nk ||
-                      (p.has_band && (jwl - ia < p.band_lo || jw - ib > p.band_hi));
+                      (p.has_band && (jwl - ia < p.band_lo || jw - ib > p.band_hi)) ||
+                      (SPARSE && !(vis(t) & wbit));
     if (!skip) {  // else P = dS = 0
       const bool full = ia + 31 < p.Nq && jw + 31 < p.Nk &&
                         (!p.has_band || (jw - (ia + 31) >= p.band_lo && jw + 31 - ia <= p.band_hi));
@@ -577,11 +640,14 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
       chunk(std::integral_constant<int, 0>{});
       chunk(std::integral_constant<int, 1>{});
     }
-    if (t + 1 < t_end) {  // the other buffer was last read before the previous barrier
+    const int nn = nxt < t_end ? next_vis(nxt + 1) : t_end;
+    if (nxt < t_end) {  // the other buffer was last read before the previous barrier
       store_step(buf ^ 1);
-      if (t + 2 < t_end) load_step(t + 2);
+      if (nn < t_end) load_step(nn);
     }
     __syncthreads();
+    cur = nxt;
+    nxt = nn;
   }
   // Waves 4..7 hand their sums to waves 0..3 (dK' in the tile area, dV in the
   // block area; every wave has passed the loop's last barrier).
@@ -680,11 +746,22 @@ __global__ void __launch_bounds__(256) bwd_kv_reduce_kernel(const AttnParams p, 
 
 template <int D, int SM>
 static void launch_bwd_main(const AttnParams& p, const BwdParams& g, unsigned grid_k,
-                            unsigned grid_q, hipStream_t stream) {
-  if (grid_k > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SM>), dim3(grid_k), dim3(kKvThreads), 0, stream, p, g);
-  if (grid_q > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, SM>), dim3(grid_q), dim3(kDqThreads), 0, stream, p, g);
+                            hipStream_t stream) {
+  const bool sparse = p.row_ptr != nullptr;
+  const int rows_q = sparse ? 64 : kDqRows;
+  const unsigned grid_q = (unsigned)((long long)p.B * p.Hq * ((p.Nq + rows_q - 1) / rows_q));
+  if (grid_k > 0) {
+    if (sparse)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, SM, true>), dim3(grid_k), dim3(kKvThreads), 0, stream, p, g);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, SM, false>), dim3(grid_k), dim3(kKvThreads), 0, stream, p, g);
+  }
+  if (grid_q > 0) {
+    if (sparse)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, SM, true>), dim3(grid_q), dim3(128), 0, stream, p, g);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, SM, false>), dim3(grid_q), dim3(kDqThreads), 0, stream, p, g);
+  }
 }
 
 template <int D>
@@ -704,13 +781,12 @@ static hipError_t launch_bwd_d(const AttnParams& p, const BwdParams& g, hipStrea
   if (rows_q > 0)
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows_q + rpb - 1) / rpb)), dim3(256), 0,
                        stream, p, g);
-  const unsigned grid_q = (unsigned)((long long)p.B * p.Hq * ((p.Nq + kDqRows - 1) / kDqRows));
   const unsigned grid_k = (unsigned)((long long)p.B * p.Hkv * ((p.Nk + 127) / 128) * g.kv_parts);
   const int sm = (p.alibi ? kSmAlibi : 0) | (p.bias ? kSmBias : 0);
-  if (sm == 0) launch_bwd_main<D, 0>(p, g, grid_k, grid_q, stream);
-  else if (sm == kSmAlibi) launch_bwd_main<D, kSmAlibi>(p, g, grid_k, grid_q, stream);
-  else if (sm == kSmBias) launch_bwd_main<D, kSmBias>(p, g, grid_k, grid_q, stream);
-  else launch_bwd_main<D, kSmAlibi | kSmBias>(p, g, grid_k, grid_q, stream);
+  if (sm == 0) launch_bwd_main<D, 0>(p, g, grid_k, stream);
+  else if (sm == kSmAlibi) launch_bwd_main<D, kSmAlibi>(p, g, grid_k, stream);
+  else if (sm == kSmBias) launch_bwd_main<D, kSmBias>(p, g, grid_k, stream);
+  else launch_bwd_main<D, kSmAlibi | kSmBias>(p, g, grid_k, stream);
   if (g.kv_parts > 1 && rows_k > 0)
     hipLaunchKernelGGL(bwd_kv_reduce_kernel<D>, dim3((unsigned)((rows_k * CH + 255) / 256)), dim3(256), 0,
                        stream, p, g);

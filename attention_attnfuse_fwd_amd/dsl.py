@@ -335,18 +335,15 @@ class AttentionProgram:
         runtime = {n: kwargs.pop(n) for n in self._RUNTIME if n in kwargs}
         return run_attention(self.bundle(**kwargs), q, k, v, **runtime)
 
-    def backward(self, q, k, v, out, dout, lse, *, alibi_slopes=None, bias=None, q_pos0: int = 0,
-                 k_pos0: int = 0, workspace=None, **static):
-        """Gradients (dq, dk, dv) of the same program ("4.4 Backward Pass");
-        programs with a block mask are not supported by the backward kernels."""
+    def backward(self, q, k, v, out, dout, lse, *, alibi_slopes=None, bias=None, block_mask=None,
+                 q_pos0: int = 0, k_pos0: int = 0, workspace=None, **static):
+        """Gradients (dq, dk, dv) of the same program ("4.4 Backward Pass")."""
         b = self.bundle(**static)
-        if b.block_sparse:
-            raise UnsupportedVariant("the backward supports rope, causal, sliding_window, full, "
-                                     "alibi and additive_bias programs")
-        _runtime_operands(b, alibi_slopes, bias, None)
+        _runtime_operands(b, alibi_slopes, bias, block_mask)
         return ops.bwd(q, k, v, out, dout, lse, causal=b.causal, window=b.window,
                        rope_theta=b.rope_theta, scale=b.scale, alibi_slopes=alibi_slopes,
-                       bias=bias, q_pos0=q_pos0, k_pos0=k_pos0, workspace=workspace)
+                       bias=bias, block_mask=block_mask, q_pos0=q_pos0, k_pos0=k_pos0,
+                       workspace=workspace)
 
 
 def attention(fn: Callable) -> AttentionProgram:

@@ -297,14 +297,15 @@ def bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, cau
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
         lse: torch.Tensor, *, causal: bool = False, window: int = 0,
         rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
-        alibi_slopes=None, bias=None, scale: Optional[float] = None,
-        workspace: Optional[torch.Tensor] = None):
+        alibi_slopes=None, bias=None, block_mask: Optional[BlockMask] = None,
+        scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
     """Attention backward ("4.4 Backward Pass"): returns (dq, dk, dv), the
     gradients of sum(out * dout) for the forward fwd(q, k, v, ...) computed
     with the same keyword arguments; ``out`` and ``lse`` are that forward's
     output and saved statistic (``fwd(..., return_lse=True)``).  bf16; an
-    additive bias is a constant of the forward (no bias gradient); no block
-    mask.  dq / dk / dv have the strides of q / k / v."""
+    additive bias is a constant of the forward (no bias gradient); a block
+    mask restricts both gradient passes to the listed blocks.  dq / dk / dv
+    have the strides of q / k / v."""
     _check_inputs(q, k, v)
     if dout.shape != out.shape:
         raise ValueError("dout must have the shape of out")
@@ -319,7 +320,8 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, do
     keep = []
     d = _make_desc(q, k, v, out, scale=scale, causal=causal, window=window,
                    rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0,
-                   alibi_slopes=alibi_slopes, bias=bias, block_mask=None, lse=None, keep=keep)
+                   alibi_slopes=alibi_slopes, bias=bias, block_mask=block_mask, lse=None,
+                   keep=keep)
     lib = _abi.load()
     need = int(lib.attnfuse_bwd_workspace_size(ctypes.byref(d)))
     if workspace is None:

@@ -233,8 +233,10 @@ size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc);
  *       attnfuse_bwd_workspace_size bytes, 16-byte aligned (else
  *       ATTNFUSE_ERR_WORKSPACE); its contents on entry do not matter.
  * Supports bf16 with rope (fp32 cos / sin tables required), causal, window,
- * alibi and additive_bias (a constant of the forward: no bias gradient);
- * block_sparse and fp32 return ATTNFUSE_ERR_UNSUPPORTED.
+ * alibi, additive_bias (a constant of the forward: no bias gradient) and
+ * block_sparse (both gradient passes visit only listed blocks; bs_block_m
+ * and bs_block_n multiples of 64, else ATTNFUSE_ERR_UNSUPPORTED); fp32
+ * returns ATTNFUSE_ERR_UNSUPPORTED.
  * All pointers 16-byte aligned.  Runs three to six kernels on `stream` (with
  * rope the two rotations first; with split key blocks a final reduction).  */
 int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,

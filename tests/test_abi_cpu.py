@@ -180,7 +180,8 @@ def test_bwd_validation(lib):
     assert call(d, FAKE, need - 4) == _abi.ERR_WORKSPACE
     assert call(d, None, need) == _abi.ERR_WORKSPACE
     assert call(d, FAKE, need, lse=None) == _abi.ERR_INVALID
-    assert call(_good_desc(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=64, bs_block_n=64,
+    # block masks need 64-aligned blocks
+    assert call(_good_desc(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=64, bs_block_n=32,
                            bs_nnz=1), FAKE, need) == _abi.ERR_UNSUPPORTED
     assert call(_good_desc(dtype=_abi.FP32), FAKE, 10**9) == _abi.ERR_UNSUPPORTED
     # the backward reads the fp32 cos / sin tables

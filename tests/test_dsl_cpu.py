@@ -148,10 +148,10 @@ def test_relu_attention_is_traced_then_rejected():
         af.lower(g)
 
 
-def test_backward_rejects_block_programs_before_any_launch():
+def test_backward_checks_runtime_operands_before_any_launch():
     @af.attention
     def sparse(Q, K, V):
         return af.softmax(af.block_sparse(af.scaled_dot_product(Q, K))) @ V
 
-    with pytest.raises(af.UnsupportedVariant):
+    with pytest.raises(af.DslError, match="block_mask"):
         sparse.backward(None, None, None, None, None, None)

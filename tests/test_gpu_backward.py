@@ -30,7 +30,39 @@ CASES = {
     "bias_d64_gqa": dict(B=2, Hq=4, Hkv=2, Nq=140, Nk=170, D=64, bias="full"),
     "bias_broadcast_rope_causal_alibi_d128": dict(B=1, Hq=2, Hkv=2, Nq=200, Nk=200, D=128, bias="rows",
                                                   rope_theta=1e4, causal=True, alibi=True),
+    # block masks ("4.3 Block-Sparse Attention": the backward visits only listed blocks)
+    "bigbird_rope_d64": dict(B=2, Hq=4, Hkv=4, Nq=512, Nk=512, D=64, rope_theta=1e4,
+                             mask=("bigbird", 64, 64)),
+    "blocks_128x64_causal_gqa_d128": dict(B=1, Hq=4, Hkv=2, Nq=300, Nk=330, D=128, causal=True,
+                                          mask=("random", 128, 64)),
+    "blocks_64x128_per_head_d64": dict(B=1, Hq=2, Hkv=1, Nq=256, Nk=384, D=64, rope_theta=500.0,
+                                       mask=("per_head", 64, 128)),
 }
+
+
+def _mask(kind, bm, bn, Hq, Nq, Nk, rng):
+    """CSR block mask (row_ptr, col_idx): BigBird, random with an empty row,
+    or one random mask per q-head (row_ptr [Hq, nqb + 1])."""
+    nqb, nkb = -(-Nq // bm), -(-Nk // bn)
+    if kind == "bigbird":
+        return workloads.bigbird_csr(nqb, nkb, seed=4)
+
+    def rows():
+        rp, ci = [0], []
+        for qb in range(nqb):
+            cols = [] if qb == 1 else sorted(rng.choice(nkb, size=int(rng.integers(1, nkb + 1)), replace=False))
+            ci.extend(int(c) for c in cols)
+            rp.append(len(ci))
+        return rp, ci
+    if kind == "random":
+        rp, ci = rows()
+        return np.asarray(rp, np.int32), np.asarray(ci, np.int32)
+    rps, cis = [], []
+    for _ in range(Hq):
+        rp, ci = rows()
+        rps.append([r + len(cis) for r in rp])
+        cis.extend(ci)
+    return np.asarray(rps, np.int32), np.asarray(cis, np.int32)
 
 
 def _run(c, seed):
@@ -53,9 +85,15 @@ def _run(c, seed):
         bias = rng.standard_normal((Nq, Nk)).astype(np.float32)
         kw["bias"] = torch.from_numpy(bias).cuda().expand(B, Hq, Nq, Nk)
         okw["bias"] = np.broadcast_to(bias.astype(np.float64), (B, Hq, Nq, Nk))
+    if "mask" in c:
+        kind, bm, bn = c["mask"]
+        rp, ci = _mask(kind, bm, bn, Hq, Nq, Nk, rng)
+        kw["block_mask"] = af.block_mask_from_csr(rp, ci, bm, bn, "cuda")
+        okw["block_mask"] = (rp, ci, bm, bn)
     qd, kd, vd, gd = (to_dev(x, "bf16") for x in (qb, kb, vb, gb))
     out, lse = af.fwd(qd, kd, vd, return_lse=True, decode_fast_path=False, **kw)
-    dq, dk, dv = af.bwd(qd, kd, vd, out, gd, lse, **kw)
+    bkw = {key: val for key, val in kw.items() if key != "block_mask"}
+    dq, dk, dv = af.bwd(qd, kd, vd, out, gd, lse, block_mask=kw.get("block_mask"), **bkw)
     torch.cuda.synchronize()
     ref = oracle.attention_backward(q, k, v, g, **okw)
     return (host(dq), host(dk), host(dv)), ref
