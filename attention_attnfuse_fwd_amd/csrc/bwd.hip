@@ -30,6 +30,7 @@ namespace attnfuse {
 namespace {
 
 constexpr int kBwdThreads = 256;    // default thread count of the row stages
+constexpr int kMaxSparseSteps = 8192;  // dK/dV step masks held in LDS
 constexpr int kKvThreads = 512;     // 8 waves, two per SIMD (dK/dV)
 constexpr int kDqThreads = 512;     // 8 waves, two per SIMD (dQ)
 constexpr int kDqRows = 256;        // query rows per dQ workgroup
@@ -566,18 +567,34 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
   // the workgroup's key blocks (bit 0: the block of key k0, bit 1: the block
   // of the last key; the same block sets both), and a wave computes only when
   // its own key block is listed.  Dense steps are all visited.
+  // The masks of up to kMaxSparseSteps steps are found by all threads at once
+  // (one CSR row scan each) and kept in LDS; longer step ranges scan a row
+  // per step.
   const int kb_lo = SPARSE ? k0 / p.bn : 0, kb_hi = SPARSE ? k_last / p.bn : 0;
   const int wbit = (SPARSE && jw / p.bn != kb_lo) ? 2 : 1;
-  auto vis = [&](int t) -> int {
-    if (!SPARSE) return 3;
+  auto vis_scan = [&](int t) -> int {
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
-    const CsrRow row = csr_row(p, h, q0 / p.bm);
+    const int* rp = p.row_ptr + (p.bs_head_stride ? (long long)h * p.bs_head_stride : 0);
+    const int qb = q0 / p.bm, nkb = (p.Nk + p.bn - 1) / p.bn;
+    const long long a = min(max((long long)rp[qb], 0LL), p.bs_nnz);
+    const long long e = min(max((long long)rp[qb + 1], a), p.bs_nnz);
     int m = 0;
-    for (int e = row.beg; e < row.end; ++e) {
-      const int c = csr_col(p, e);
+    for (long long x = a; x < e; ++x) {
+      const int c = min(max(p.col_idx[x], 0), nkb);
       m |= (c == kb_lo ? 1 : 0) | (c == kb_hi ? 2 : 0);
     }
     return m;
+  };
+  __shared__ uint8_t vis_s[SPARSE ? kMaxSparseSteps : 1];
+  const bool vis_in_lds = SPARSE && t_end - t_begin <= kMaxSparseSteps;
+  if (vis_in_lds) {
+    for (int t = t_begin + (int)threadIdx.x; t < t_end; t += kKvThreads) vis_s[t - t_begin] = (uint8_t)vis_scan(t);
+    __syncthreads();
+  }
+  auto vis = [&](int t) -> int {
+    if (!SPARSE) return 3;
+    if (vis_in_lds) return __builtin_amdgcn_readfirstlane((int)vis_s[t - t_begin]);
+    return __builtin_amdgcn_readfirstlane(vis_scan(t));
   };
   auto next_vis = [&](int t) {
     if (SPARSE)
