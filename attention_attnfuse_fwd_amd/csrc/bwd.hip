@@ -620,18 +620,27 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
     const bool skip = ia >= p.Nq || jw >= p.Nk ||
                       (p.has_band && (jwl - ia < p.band_lo || jw - ib > p.band_hi)) ||
                       (SPARSE && !(vis(t) & wbit));
-    if (!skip) {  // else P = dS = 0
-      const bool full = ia + 31 < p.Nq && jw + 31 < p.Nk &&
-                        (!p.has_band || (jw - (ia + 31) >= p.band_lo && jw + 31 - ia <= p.band_hi));
-      const float slope2 = (SM & kSmAlibi) ? p.alibi[h] * kLog2e : 0.f;
-      const float* bias_bh = (SM & kSmBias) ? p.bias + b * p.bsb + h * p.bsh : nullptr;
-      // S and dP (32 query rows x the wave's 32 keys; lane = key column).
-      f32x16 sa = f32x16{}, da = f32x16{};
+    // S and dP (32 query rows x the wave's 32 keys; lane = key column).
+    f32x16 sa = f32x16{}, da = f32x16{};
+    if (!skip) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         sa = mfma32(row_frag<D>(qs, 32 * st + lq, kk), row_frag<D>(kblk_s, 32 * kw + lq, kk), sa);
         da = mfma32(row_frag<D>(dos, 32 * st + lq, kk), row_frag<D>(vblk_s, 32 * kw + lq, kk), da);
       }
+    }
+    // The next step's tiles go to the other buffer while the products run
+    // (that buffer was last read before the previous barrier).
+    const int nn = nxt < t_end ? next_vis(nxt + 1) : t_end;
+    if (nxt < t_end) {
+      store_step(buf ^ 1);
+      if (nn < t_end) load_step(nn);
+    }
+    if (!skip) {  // else P = dS = 0
+      const bool full = ia + 31 < p.Nq && jw + 31 < p.Nk &&
+                        (!p.has_band || (jw - (ia + 31) >= p.band_lo && jw + 31 - ia <= p.band_hi));
+      const float slope2 = (SM & kSmAlibi) ? p.alibi[h] * kLog2e : 0.f;
+      const float* bias_bh = (SM & kSmBias) ? p.bias + b * p.bsb + h * p.bsh : nullptr;
       // Per 16-row chunk: P and dS (bf16), then dV^T += dO^T P, dK'^T += Q'^T dS.
       auto chunk = [&](auto c_tag) {
         constexpr int c = decltype(c_tag)::value;
@@ -656,11 +665,6 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
       };
       chunk(std::integral_constant<int, 0>{});
       chunk(std::integral_constant<int, 1>{});
-    }
-    const int nn = nxt < t_end ? next_vis(nxt + 1) : t_end;
-    if (nxt < t_end) {  // the other buffer was last read before the previous barrier
-      store_step(buf ^ 1);
-      if (nn < t_end) load_step(nn);
     }
     __syncthreads();
     cur = nxt;
