@@ -25,6 +25,8 @@ def _oracle_kw(w: workloads.Workload, inp: workloads.Inputs):
         kw["alibi_slopes"] = inp.alibi_slopes.astype(np.float64)
     if inp.bs_row_ptr is not None:
         kw["block_mask"] = (inp.bs_row_ptr, inp.bs_col_idx, w.bigbird_block, w.bigbird_block)
+    if inp.bias is not None:
+        kw["bias"] = np.broadcast_to(inp.bias.astype(np.float64), (w.B, w.Hq, w.Nq, w.Nk))
     return kw
 
 
@@ -36,6 +38,8 @@ def _gpu_kw(w: workloads.Workload, inp: workloads.Inputs):
     if inp.bs_row_ptr is not None:
         kw["block_mask"] = af.block_mask_from_csr(inp.bs_row_ptr, inp.bs_col_idx, w.bigbird_block,
                                                   w.bigbird_block, "cuda")
+    if inp.bias is not None:
+        kw["bias"] = torch.from_numpy(inp.bias).cuda().expand(w.B, w.Hq, w.Nq, w.Nk)
     return kw
 
 
@@ -203,7 +207,7 @@ def _sample_rows(N, rng, extra=()):
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_rope_causal_n4096", "alibi_causal_window1024_n8192",
-                                  "bigbird_rope_n4096"])
+                                  "bigbird_rope_n4096", "bias_heads_causal_n2048"])
 def test_full_size_sampled_rows(name):
     w = W[name]
     inp = workloads.make_inputs(w)

@@ -76,6 +76,7 @@ class Workload:
     q_pos0: int = 0
     k_pos0: int = 0
     decode_splits: int = 0     # >0: split-KV decode workload
+    bias_heads: bool = False   # additive fp32 bias, one [Nq, Nk] plane per q-head (shared by batches)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -104,6 +105,13 @@ WORKLOADS = {
         "llama3_70b_decode_32k", "bf16", B=1, Hq=64, Hkv=8, Nq=1, Nk=32768, D=128,
         seed=5, rope_theta=500000.0, q_pos0=32768, k_pos0=0, decode_splits=64),
 }
+
+# Additive-bias workload (the pages' additive_bias combinator, no evaluation
+# geometry given): a relative-position-style bias plane per head, B=2 H=16
+# N=2048 D=128, causal, bias iid N(0,1) float32 drawn after Q, K, V.
+WORKLOADS["bias_heads_causal_n2048"] = Workload(
+    "bias_heads_causal_n2048", "bf16", B=2, Hq=16, Hkv=16, Nq=2048, Nk=2048, D=128, seed=7,
+    causal=True, bias_heads=True)
 
 # Second grid: the GPT-2-small geometry of the pages' head-to-head tables
 # ("6.1 Forward Head-to-Head on Ampere", Table 6: Dense, Causal, SW W=256,
@@ -199,6 +207,7 @@ class Inputs:
     k_dev: np.ndarray
     v_dev: np.ndarray
     alibi_slopes: Optional[np.ndarray] = None
+    bias: Optional[np.ndarray] = None   # float32 [1, Hq, Nq, Nk] (broadcast over batches)
     bs_row_ptr: Optional[np.ndarray] = None
     bs_col_idx: Optional[np.ndarray] = None
 
@@ -221,6 +230,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
         raise ValueError(w.dtype)
     if w.alibi:
         inp.alibi_slopes = alibi_slopes(w.Hq)
+    if w.bias_heads:
+        inp.bias = rng.standard_normal((1, w.Hq, w.Nq, w.Nk), dtype=np.float32)
     if w.bigbird_block:
         nqb = -(-w.Nq // w.bigbird_block)
         nkb = -(-w.Nk // w.bigbird_block)
