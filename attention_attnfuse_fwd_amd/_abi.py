@@ -81,6 +81,9 @@ class VariantDesc(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("tile_waves", ctypes.c_int32),
         ("tile_heads", ctypes.c_int32),
+        ("kv_fp8", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
     @classmethod

@@ -44,6 +44,10 @@ int validate_common(const attnfuse_variant_desc* d) {
       d->k_pos0 + d->Nk >= kMaxLen)
     return ATTNFUSE_ERR_INVALID;
   if (d->causal != 0 && d->causal != 1) return ATTNFUSE_ERR_INVALID;
+  if (d->kv_fp8 != 0 && d->kv_fp8 != 1) return ATTNFUSE_ERR_INVALID;
+  if (d->kv_fp8 && (!(d->k_scale > 0.f) || !isfinite(d->k_scale) || !(d->v_scale > 0.f) ||
+                    !isfinite(d->v_scale)))
+    return ATTNFUSE_ERR_INVALID;
   if (d->window < 0) return ATTNFUSE_ERR_INVALID;
   if (d->rope) {
     if (!(d->rope_theta > 0.0)) return ATTNFUSE_ERR_INVALID;
@@ -97,6 +101,7 @@ AttnParams base_params(const void* q, const void* k, const void* v, void* out,
   p.osb = d->o_stride[0]; p.osh = d->o_stride[1]; p.osn = d->o_stride[2];
   const double scale = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->D);
   p.scale_log2 = (float)(scale * 1.4426950408889634);
+  p.v_scale = 1.f;
   p.rcos = d->rope ? d->rope_cos : nullptr;
   p.rsin = d->rope ? d->rope_sin : nullptr;
   p.rcs = d->rope ? d->rope_cs_f16 : nullptr;
@@ -160,6 +165,7 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
+  if (d->kv_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
   // K and V may be NULL only when there are no keys (an empty tensor).
   if (!q || !out || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
   // fp32 kernels read the fp32 tables; bf16 kernels rotate Q with the fp16
@@ -293,10 +299,15 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
   if (p.chunk < 1) p.chunk = 1;
   p.n_hgrp = (p.G + 31) / 32;
   p.ws = reinterpret_cast<float*>(workspace);
+  if (d->kv_fp8) {  // rows = scale * code: the key scale joins the score scale
+    p.scale_log2 *= d->k_scale;
+    p.v_scale = d->v_scale;
+  }
   const long long U = (long long)d->B * d->Hkv * p.n_hgrp;
   const long long grid = 8 * U * ((num_splits + 7) / 8);
   if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
-  hipError_t e = attnfuse::launch_decode_split(p, d->D, d->rope != 0, (unsigned)grid, s);
+  hipError_t e = attnfuse::launch_decode_split(p, d->D, d->rope != 0, d->kv_fp8 != 0,
+                                               (unsigned)grid, s);
   if (e != hipSuccess) return ATTNFUSE_ERR_HIP;
   return hip_status(attnfuse::launch_decode_combine(p, d->D, s));
 }
@@ -343,7 +354,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
-  if (d->dtype != ATTNFUSE_BF16) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->dtype != ATTNFUSE_BF16 || d->kv_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->bs_row_ptr && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->Nq > 0 && (!q || !out || !dout || !lse || !dq)) return ATTNFUSE_ERR_INVALID;
   if (d->Nk > 0 && (!k || !v || !dk || !dv)) return ATTNFUSE_ERR_INVALID;
@@ -411,6 +422,7 @@ int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* 
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
   if (!x || !x_rot || !d->rope || (which != 0 && which != 1)) return ATTNFUSE_ERR_INVALID;
+  if (d->kv_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
   if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
   const int H = which == 0 ? d->Hq : d->Hkv;
   const int N = which == 0 ? d->Nq : d->Nk;

@@ -67,6 +67,7 @@ struct AttnParams {
   // split-KV decode
   int splits, chunk, n_hgrp;
   float* ws;
+  float v_scale;              // output multiplier (fp8 V cache dequantisation; 1 otherwise)
 };
 
 // Backward pass buffers (the kernels read the forward's q, k, v, out, lse

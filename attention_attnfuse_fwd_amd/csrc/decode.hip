@@ -27,10 +27,11 @@ constexpr int kDecNT = 256;  // 4 waves
 constexpr int kDecSK = 32;   // keys per wave step
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool KV8>
 __global__ void __launch_bounds__(kDecNT, 2) decode_split_kernel(const AttnParams p) {
-  using KS = KStage<D, kDecSK, 64, ROPE>;
-  using VS = VStage<D, kDecSK, 64>;
+  using KS = KStage<D, kDecSK, 64, ROPE, KV8>;
+  using VS = VStage<D, kDecSK, 64, KV8>;
+  using T = typename KS::T;
   constexpr int KSTR = KS::KSTR;
   constexpr int VSTR = VS::VSTR;
   constexpr int WBUF = kDecSK * KSTR + D * VSTR;  // one wave's LDS region (elements)
@@ -56,8 +57,8 @@ __global__ void __launch_bounds__(kDecNT, 2) decode_split_kernel(const AttnParam
   const int c1 = min(p.Nk, c0 + p.chunk);
   const int n_steps = c1 > c0 ? (c1 - c0 + kDecSK - 1) / kDecSK : 0;
 
-  const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ksb + kvh * p.ksh;
-  const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh;
+  const T* kb = reinterpret_cast<const T*>(p.k) + b * p.ksb + kvh * p.ksh;
+  const T* vb = reinterpret_cast<const T*>(p.v) + b * p.vsb + kvh * p.vsh;
   __bf16* const ks = smem + wave * WBUF;
   __bf16* const vs = ks + kDecSK * KSTR;
 
@@ -324,21 +325,26 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const AttnParams p)
   const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
   const int b = bh / p.Hq, h = bh % p.Hq;
   __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh;
-  for (int d = tid; d < D; d += 256) orow[d] = (__bf16)(s_acc[0][d] * inv);
+  const float oscale = inv * p.v_scale;  // v_scale: fp8 V cache dequantisation (else 1)
+  for (int d = tid; d < D; d += 256) orow[d] = (__bf16)(s_acc[0][d] * oscale);
   if (p.lse && tid == 0) p.lse[bh] = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -INFINITY;
 }
 
-hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned grid,
+hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, bool kv8, unsigned grid,
                                hipStream_t stream) {
-#define ATTNFUSE_DEC(DD, R)                                                                  \
-  if (D == DD && rope == R) {                                                                \
-    hipLaunchKernelGGL((decode_split_kernel<DD, R>), dim3(grid), dim3(kDecNT), 0, stream, p); \
-    return hipGetLastError();                                                                \
+#define ATTNFUSE_DEC(DD, R, K8)                                                                   \
+  if (D == DD && rope == R && kv8 == K8) {                                                        \
+    hipLaunchKernelGGL((decode_split_kernel<DD, R, K8>), dim3(grid), dim3(kDecNT), 0, stream, p); \
+    return hipGetLastError();                                                                     \
   }
-  ATTNFUSE_DEC(64, false)
-  ATTNFUSE_DEC(64, true)
-  ATTNFUSE_DEC(128, false)
-  ATTNFUSE_DEC(128, true)
+  ATTNFUSE_DEC(64, false, false)
+  ATTNFUSE_DEC(64, true, false)
+  ATTNFUSE_DEC(128, false, false)
+  ATTNFUSE_DEC(128, true, false)
+  ATTNFUSE_DEC(64, false, true)
+  ATTNFUSE_DEC(64, true, true)
+  ATTNFUSE_DEC(128, false, true)
+  ATTNFUSE_DEC(128, true, true)
 #undef ATTNFUSE_DEC
   return hipErrorInvalidValue;
 }

@@ -23,7 +23,7 @@ constexpr bool fwd_bf16_supported(int D, int NW, bool rope, bool scoremod, bool 
   return !(D == 128 && NW == 8 && scoremod && (rope || sparse));
 }
 
-hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, unsigned grid,
+hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, bool kv8, unsigned grid,
                                hipStream_t stream);
 hipError_t launch_decode_combine(const AttnParams& p, int D, hipStream_t stream);
 

@@ -4,12 +4,28 @@
 // ([BN][D + 8], rotated when ROPE), V goes transposed ([D][BN + 8], key
 // columns permuted by vcol()).  The load*() calls only issue global loads, so
 // a kernel can call them a tile (or two) ahead and hide their latency behind
-// MFMA work; store() then rotates and writes LDS.
+// MFMA work; store() then rotates and writes LDS.  With KV8 the cache holds
+// OCP FP8 E4M3 codes: half the bytes are loaded, and store() converts them
+// to bf16 exactly (every E4M3 value is a bf16 value) before the rotation.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
 namespace attnfuse {
+
+// Eight FP8 E4M3 codes (bytes of x, in order) -> eight bf16 values, exact
+// (gfx950 conversion with a unit scale).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 x) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
 
 // K part: unit = (key j, 8-wide chunk c of the low half) covering d in
 // [8c, 8c + 8) and its RoPE partner [D/2 + 8c, D/2 + 8c + 8).  Consecutive
@@ -17,8 +33,9 @@ namespace attnfuse {
 // within each block of 16 keys is permuted so that the rows a 16-lane group
 // stores together sit CPR rows apart, which puts their 16-byte chunks on
 // disjoint LDS banks (the row stride is D + 8 elements).
-template <int D, int BN, int NT, bool ROPE>
+template <int D, int BN, int NT, bool ROPE, bool KV8 = false>
 struct KStage {
+  using T = typename std::conditional<KV8, uint8_t, __bf16>::type;  // cache element
   static constexpr int KSTR = D + 8;
   static constexpr int CPR = D / 16;                 // chunk pairs per row
   static constexpr int UNITS = BN * CPR;
@@ -31,12 +48,13 @@ struct KStage {
     return (jr & ~15) | ((jl % RPG) * CPR + jl / RPG);
   }
 
-  uint4 lo[U], hi[U];
+  uint4 lo[KV8 ? 1 : U], hi[KV8 ? 1 : U];      // bf16 rows
+  uint2 lo8[KV8 ? U : 1], hi8[KV8 ? U : 1];    // fp8 rows
   uint4 cs[U][2];  // fp16 (cos, sin) pairs for the unit's 8 angles
   int pos[U];
 
   // Raw K rows k0 .. k0+BN-1 (rows at or past key_end are clamped to key_end - 1).
-  __device__ __forceinline__ void load(const AttnParams& p, const __bf16* kb, int k0, int key_end,
+  __device__ __forceinline__ void load(const AttnParams& p, const T* kb, int k0, int key_end,
                                        int tid) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -44,9 +62,14 @@ struct KStage {
       if (UNITS % NT == 0 || unit < UNITS) {
         const int j = row_of(unit), c = unit % CPR;
         const int kj = min(k0 + j, key_end - 1);
-        const __bf16* src = kb + (long long)kj * p.ksn + 8 * c;
-        lo[u] = ld16(src);
-        hi[u] = ld16(src + D / 2);
+        const T* src = kb + (long long)kj * p.ksn + 8 * c;
+        if constexpr (KV8) {
+          lo8[u] = *reinterpret_cast<const uint2*>(src);
+          hi8[u] = *reinterpret_cast<const uint2*>(src + D / 2);
+        } else {
+          lo[u] = ld16(src);
+          hi[u] = ld16(src + D / 2);
+        }
         pos[u] = p.k_pos0 + kj;
       }
     }
@@ -71,7 +94,14 @@ struct KStage {
       const int unit = tid + u * NT;
       if (UNITS % NT == 0 || unit < UNITS) {
         const int j = row_of(unit), c = unit % CPR;
-        uint4 l = lo[u], h = hi[u];
+        uint4 l, h;
+        if constexpr (KV8) {
+          l = e4m3x8_to_bf16x8(lo8[u]);
+          h = e4m3x8_to_bf16x8(hi8[u]);
+        } else {
+          l = lo[u];
+          h = hi[u];
+        }
         if (ROPE) rope_rotate_bf16x8_h(l, h, cs[u][0], cs[u][1]);
         st16(ks + j * KSTR + 8 * c, l);
         st16(ks + j * KSTR + D / 2 + 8 * c, h);
@@ -84,16 +114,18 @@ struct KStage {
 // vary fastest across lanes, so the 8-byte writes a 16-lane group issues for
 // one d row land side by side in that row (no bank conflicts); each load
 // instruction still reads 64-byte pieces of 16 key rows.
-template <int D, int BN, int NT>
+template <int D, int BN, int NT, bool KV8 = false>
 struct VStage {
+  using T = typename std::conditional<KV8, uint8_t, __bf16>::type;  // cache element
   static constexpr int VSTR = BN + 8;
   static constexpr int RUNS = BN / 4;
   static constexpr int UNITS = RUNS * (D / 8);
   static constexpr int U = (UNITS + NT - 1) / NT;
 
-  uint4 v[U][4];
+  uint4 v[KV8 ? 1 : U][4];    // bf16 rows
+  uint2 v8[KV8 ? U : 1][4];   // fp8 rows
 
-  __device__ __forceinline__ void load(const AttnParams& p, const __bf16* vb, int k0, int key_end,
+  __device__ __forceinline__ void load(const AttnParams& p, const T* vb, int k0, int key_end,
                                        int tid) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -103,7 +135,9 @@ struct VStage {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int kj = min(k0 + 4 * run + b, key_end - 1);
-          v[u][b] = ld16(vb + (long long)kj * p.vsn + 8 * dc);
+          const T* src = vb + (long long)kj * p.vsn + 8 * dc;
+          if constexpr (KV8) v8[u][b] = *reinterpret_cast<const uint2*>(src);
+          else v[u][b] = ld16(src);
         }
       }
     }
@@ -114,7 +148,14 @@ struct VStage {
       const int unit = tid + u * NT;
       if (UNITS % NT == 0 || unit < UNITS) {
         const int run = unit % RUNS, dc = unit / RUNS;
-        store_vt_4x8(vs + (8 * dc) * VSTR + vcol(4 * run), VSTR, v[u]);
+        if constexpr (KV8) {
+          uint4 w[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) w[b] = e4m3x8_to_bf16x8(v8[u][b]);
+          store_vt_4x8(vs + (8 * dc) * VSTR + vcol(4 * run), VSTR, w);
+        } else {
+          store_vt_4x8(vs + (8 * dc) * VSTR + vcol(4 * run), VSTR, v[u]);
+        }
       }
     }
   }

@@ -251,13 +251,30 @@ def decode_workspace_size(q, k_cache, num_splits: int) -> int:
     return int(_abi.load().attnfuse_decode_workspace_size(ctypes.byref(d), int(num_splits)))
 
 
+_FP8_DTYPES = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
            num_splits: Optional[int] = None, causal: bool = False, window: int = 0,
            rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
            alibi_slopes=None, scale: Optional[float] = None, return_lse: bool = False,
-           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Split-KV single-query decode (q [B, Hq, 1, D] bf16) with a log-sum-exp combine."""
-    _check_inputs(q, k_cache, v_cache)
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           k_scale: float = 1.0, v_scale: float = 1.0):
+    """Split-KV single-query decode (q [B, Hq, 1, D] bf16) with a log-sum-exp combine.
+
+    The cache is bf16 like q, or FP8 E4M3 codes (``torch.float8_e4m3fn``, or
+    their bytes as ``torch.uint8``) holding rows ``k_scale * code`` and
+    ``v_scale * code``."""
+    kv_fp8 = k_cache.dtype in _FP8_DTYPES
+    if kv_fp8:
+        if v_cache.dtype != k_cache.dtype or q.dtype != torch.bfloat16:
+            raise TypeError("an fp8 cache needs fp8 k_cache and v_cache and a bf16 query")
+        if not (q.is_cuda and k_cache.is_cuda and v_cache.is_cuda):
+            raise ValueError("q, k_cache, v_cache must be GPU tensors")
+        if k_cache.shape != v_cache.shape:
+            raise ValueError("k and v must have the same shape")
+    else:
+        _check_inputs(q, k_cache, v_cache)
     B, Hq, Nq, D = q.shape
     Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
     if num_splits is None:
@@ -269,6 +286,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     d = _make_desc(q, k_cache, v_cache, out, scale=scale, causal=causal, window=window,
                    rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0,
                    alibi_slopes=alibi_slopes, bias=None, block_mask=None, lse=lse, keep=keep)
+    if kv_fp8:
+        d.kv_fp8, d.k_scale, d.v_scale = 1, float(k_scale), float(v_scale)
     lib = _abi.load()
     need = int(lib.attnfuse_decode_workspace_size(ctypes.byref(d), int(num_splits)))
     if workspace is None:

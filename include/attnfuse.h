@@ -160,6 +160,17 @@ typedef struct attnfuse_variant_desc {
    * points and by fp32. */
   int32_t tile_waves;
   int32_t tile_heads;
+
+  /* KV cache in fp8 (attnfuse_decode only): kv_fp8 = 1 means k_cache and
+   * v_cache hold OCP FP8 E4M3 codes (1 byte each: bias 7, largest 448, no
+   * infinities) and the cached rows are k_scale * code and v_scale * code
+   * (per-tensor dequantisation scales, finite and > 0); K/V strides then
+   * count bytes and keep the 8-element alignment of the bf16 layout.  q and
+   * out stay bf16.  0 = K/V have the dtype above.  Any other entry point
+   * returns ATTNFUSE_ERR_UNSUPPORTED when kv_fp8 is set. */
+  int32_t kv_fp8;
+  float k_scale;
+  float v_scale;
 } attnfuse_variant_desc;
 
 /* Fused attention forward: out = attention(q, k, v) under `desc`.
@@ -180,7 +191,8 @@ size_t attnfuse_decode_workspace_size(const attnfuse_variant_desc* desc, int32_t
  * (m, l, acc[D]) per (b, q-head, chunk) into `workspace`; phase 2 merges the
  * partials by log-sum-exp into `out` (and desc->lse when set).  Both kernels
  * run on `stream`.  Supports rope, causal, window, alibi; bias and
- * block_sparse return ATTNFUSE_ERR_UNSUPPORTED.  workspace is caller-owned
+ * block_sparse return ATTNFUSE_ERR_UNSUPPORTED; kv_fp8 reads an fp8 cache.
+ * workspace is caller-owned
  * device memory of at least attnfuse_decode_workspace_size bytes (else
  * ATTNFUSE_ERR_WORKSPACE); its contents on entry do not matter.
  * 1 <= num_splits <= 4096. */

@@ -80,6 +80,14 @@ def _fwd(lib, d):
     return lib.attnfuse_fwd(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), None)
 
 
+def test_fp8_cache_fields_are_validated(lib):
+    # only attnfuse_decode reads an fp8 cache; bad scales are invalid everywhere
+    assert _fwd(lib, _good_desc(kv_fp8=1, k_scale=1.0, v_scale=1.0)) == _abi.ERR_UNSUPPORTED
+    assert _fwd(lib, _good_desc(kv_fp8=2)) == _abi.ERR_INVALID
+    assert _fwd(lib, _good_desc(kv_fp8=1, k_scale=0.0, v_scale=1.0)) == _abi.ERR_INVALID
+    assert _fwd(lib, _good_desc(kv_fp8=1, k_scale=1.0, v_scale=float("inf"))) == _abi.ERR_INVALID
+
+
 @pytest.mark.parametrize("tile", [(3, 1), (8, 3), (2, 4), (16, 1), (4, 4)])
 def test_unsupported_tile_choices_are_rejected_before_launch(lib, tile):
     # the default descriptor has G = Hq / Hkv = 2: tile_heads 4 does not divide it

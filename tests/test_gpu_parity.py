@@ -400,3 +400,83 @@ def test_gqa_matches_repeated_heads():
     a = host(af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), causal=True, rope_theta=1e4))
     b = host(af.fwd(to_dev(qb, "bf16"), to_dev(kr, "bf16"), to_dev(vr, "bf16"), causal=True, rope_theta=1e4))
     assert np.max(np.abs(a - b)) <= 2e-2
+
+
+# ----------------------------------------------------------------------------
+# Decode from an FP8 E4M3 KV cache (per-tensor scales)
+# ----------------------------------------------------------------------------
+
+def _fp8_cache(shape, rng, scale_to=448.0):
+    """float32 N(0,1) draws quantised to E4M3 with a per-tensor scale:
+    (codes uint8, dequantised float64 values, scale)."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    scale = float(np.abs(x).max()) / scale_to
+    codes = workloads.round_to_e4m3(x / scale)
+    return codes, workloads.e4m3_to_f64(codes) * scale, scale
+
+
+def _fp8_dev(codes, as_uint8=False):
+    t = torch.from_numpy(codes).cuda()
+    return t if as_uint8 else t.view(torch.float8_e4m3fn)
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=2, Hq=8, Hkv=2, Nk=3000, D=128, rope_theta=1e4, splits=13),
+    dict(B=1, Hq=40, Hkv=1, Nk=2000, D=128, splits=64, alibi=True, window=700, causal=True),
+    dict(B=2, Hq=16, Hkv=2, Nk=777, D=64, rope_theta=5e5, splits=7, k_pos0=9, uint8=True),
+], ids=["rope_gqa_d128", "alibi_window_gqa40", "rope_offset_d64_uint8"])
+def test_decode_fp8_cache_small(case):
+    c = dict(case)
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, Nk, D = c["B"], c["Hq"], c["Hkv"], c["Nk"], c["D"]
+    qb, q = workloads.normal_bf16((B, Hq, 1, D), rng)
+    kc, k, ks = _fp8_cache((B, Hkv, Nk, D), rng)
+    vc, v, vs = _fp8_cache((B, Hkv, Nk, D), rng)
+    k0 = c.get("k_pos0", 0)
+    okw = dict(q_pos0=Nk + k0, k_pos0=k0, rope_theta=c.get("rope_theta"), causal=c.get("causal", False),
+               window=c.get("window", 0))
+    dkw = dict(okw)
+    if c.get("alibi"):
+        sl = workloads.alibi_slopes(Hq)
+        okw["alibi_slopes"] = sl.astype(np.float64)
+        dkw["alibi_slopes"] = torch.from_numpy(sl).cuda()
+    log(f"case decode fp8 {case}")
+    out, lse = af.decode(to_dev(qb, "bf16"), _fp8_dev(kc, c.get("uint8")), _fp8_dev(vc, c.get("uint8")),
+                         num_splits=c["splits"], k_scale=ks, v_scale=vs, return_lse=True, **dkw)
+    ref, rlse = oracle.attention(q, k, v, **okw)
+    check_close(host(out), ref, "bf16", f"decode fp8 {case}")
+    check_lse(host(lse), rlse, 2e-2, f"decode fp8 {case}")
+
+
+def test_decode_fp8_cache_full_config():
+    """Llama-3-70B decode geometry (B=1, Hq=64, Hkv=8, D=128, 32768 cached keys,
+    RoPE theta=5e5, 64 splits) with the cache in E4M3: every head against the
+    oracle on the dequantised values."""
+    w = W["llama3_70b_decode_32k"]
+    rng = np.random.default_rng(w.seed)
+    qb, q = workloads.normal_bf16((w.B, w.Hq, 1, w.D), rng)
+    kc, k, ks = _fp8_cache((w.B, w.Hkv, w.Nk, w.D), rng)
+    vc, v, vs = _fp8_cache((w.B, w.Hkv, w.Nk, w.D), rng)
+    log("case decode fp8 70b full size")
+    out = af.decode(to_dev(qb, "bf16"), _fp8_dev(kc), _fp8_dev(vc), num_splits=w.decode_splits,
+                    rope_theta=w.rope_theta, q_pos0=w.q_pos0, k_scale=ks, v_scale=vs)
+    ref, _ = oracle.attention(q, k, v, rope_theta=w.rope_theta, q_pos0=w.q_pos0)
+    check_close(host(out), ref, "bf16", "decode fp8 70b")
+
+
+def test_fp8_cache_is_rejected_outside_decode():
+    rng = np.random.default_rng(3)
+    kc, _, _ = _fp8_cache((1, 2, 64, 64), rng)
+    d = af.VariantDesc.new()
+    d.dtype, d.B, d.Hq, d.Hkv, d.Nq, d.Nk, d.D = 0, 1, 2, 2, 64, 64, 64
+    for f in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        arr = getattr(d, f)
+        arr[0], arr[1], arr[2] = 2 * 64 * 64, 64 * 64, 64
+    d.kv_fp8, d.k_scale, d.v_scale = 1, 1.0, 1.0
+    lib = af.load_library()
+    kd = _fp8_dev(kc)
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda")
+    import ctypes
+    st = lib.attnfuse_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kd.data_ptr()),
+                          ctypes.c_void_p(kd.data_ptr()), ctypes.c_void_p(q.data_ptr()), ctypes.byref(d), None)
+    assert st == -2  # ATTNFUSE_ERR_UNSUPPORTED

@@ -53,6 +53,36 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) to float64: sign, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 is subnormal (m * 2^-9); 0x7f / 0xff are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_GRID = e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))  # the 127 finite magnitudes, ascending
+
+
+def round_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """float values to OCP FP8 E4M3 codes, round to nearest (ties to the even
+    code), saturating at +-448.  Finite inputs only."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("round_to_e4m3 expects finite values")
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_GRID, a, side="left"), 0, 0x7E)  # first grid value >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3_GRID[lo], _E4M3_GRID[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(x < 0, code | 0x80, code).astype(np.uint8)
+
+
 # ----------------------------------------------------------------------------
 # Workload descriptions
 # ----------------------------------------------------------------------------
