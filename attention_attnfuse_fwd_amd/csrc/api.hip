@@ -166,8 +166,9 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
   if (d->kv_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
-  // K and V may be NULL only when there are no keys (an empty tensor).
-  if (!q || !out || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
+  // Q / out may be NULL only when there are no queries, K / V only when there
+  // are no keys (empty tensors).
+  if ((d->Nq > 0 && (!q || !out)) || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
   // fp32 kernels read the fp32 tables; bf16 kernels rotate Q with the fp16
   // pairs and K with the bf16 pairs.
   if (d->dtype == ATTNFUSE_FP32 && !fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;

@@ -132,6 +132,9 @@ def create_block_mask(predicate: Callable, n_qblocks: int, n_kblocks: int, block
 def _strides3(t: torch.Tensor, name: str):
     if t.dim() != 4:
         raise ValueError(f"{name} must be 4-D [B, H, N, D]")
+    if t.numel() == 0:  # nothing is read or written: describe it as contiguous
+        _, H, N, D = t.shape
+        return (H * N * D, N * D, D)
     if t.stride(3) != 1:
         raise ValueError(f"{name} must have a contiguous last (head) dimension")
     return (t.stride(0), t.stride(1), t.stride(2))

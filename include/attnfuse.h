@@ -176,7 +176,8 @@ typedef struct attnfuse_variant_desc {
 /* Fused attention forward: out = attention(q, k, v) under `desc`.
  * q, k, v, out: device pointers laid out as described above (dtype from
  * desc->dtype); k and v may be NULL when desc->Nk == 0 (every output row is
- * then zero and its lse -inf).  Returns an attnfuse_status. */
+ * then zero and its lse -inf), q and out when desc->Nq == 0 (nothing to do).
+ * Returns an attnfuse_status. */
 int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
                  const attnfuse_variant_desc* desc, void* stream);
 

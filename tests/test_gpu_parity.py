@@ -480,3 +480,18 @@ def test_fp8_cache_is_rejected_outside_decode():
     st = lib.attnfuse_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kd.data_ptr()),
                           ctypes.c_void_p(kd.data_ptr()), ctypes.c_void_p(q.data_ptr()), ctypes.byref(d), None)
     assert st == -2  # ATTNFUSE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("Nk,splits", [(1, 1), (31, 4), (33, 64), (100, 7)])
+def test_decode_fp8_cache_short(Nk, splits):
+    """Short fp8 caches: fewer keys than one 32-key step, more splits than keys."""
+    rng = np.random.default_rng(Nk)
+    B, Hq, Hkv, D = 1, 8, 2, 128
+    qb, q = workloads.normal_bf16((B, Hq, 1, D), rng)
+    kc, k, ks = _fp8_cache((B, Hkv, Nk, D), rng)
+    vc, v, vs = _fp8_cache((B, Hkv, Nk, D), rng)
+    log(f"case decode fp8 short Nk={Nk} splits={splits}")
+    out = af.decode(to_dev(qb, "bf16"), _fp8_dev(kc), _fp8_dev(vc), num_splits=splits, rope_theta=1e4,
+                    q_pos0=Nk, k_scale=ks, v_scale=vs)
+    ref, _ = oracle.attention(q, k, v, rope_theta=1e4, q_pos0=Nk)
+    check_close(host(out), ref, "bf16", f"decode fp8 Nk={Nk}")
