@@ -306,7 +306,8 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
   }
   const long long U = (long long)d->B * d->Hkv * p.n_hgrp;
   const long long grid = 8 * U * ((num_splits + 7) / 8);
-  if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (grid >= (1LL << 31) || (long long)d->B * d->Hq * (d->D / 32) >= (1LL << 31))
+    return ATTNFUSE_ERR_UNSUPPORTED;
   hipError_t e = attnfuse::launch_decode_split(p, d->D, d->rope != 0, d->kv_fp8 != 0,
                                                (unsigned)grid, s);
   if (e != hipSuccess) return ATTNFUSE_ERR_HIP;

@@ -14,8 +14,10 @@
 // merged in LDS at the end.  Workgroups are ordered so that the kv-heads of
 // one chunk run on the same XCD and share the chunk's RoPE table rows in L2.
 //
-// Partial layout in the workspace (fp32): for (b, h, chunk), D + 2 floats:
-// acc[0..D-1] (un-normalised), then m (exp2 domain, scaled), then l.
+// Partial layout in the workspace (fp32), two arrays: acc [B][Hq][splits][D]
+// (un-normalised output rows, 16-byte aligned), then ml [B][Hq][splits][2]
+// holding m (running maximum, exp2 domain, scaled) and l (the sum of the
+// exponentials) of each chunk.
 #include "common.h"
 #include "launch.h"
 #include "tile_stage.h"
@@ -232,102 +234,83 @@ __global__ void __launch_bounds__(kDecNT, 2) decode_split_kernel(const AttnParam
         L += a * lw[w * 32 + col];
       }
     }
-    const int hh = kvh * p.G + gg;
-    float* dst = p.ws + (((long long)b * p.Hq + hh) * p.splits + split) * (D + 2);
-    dst[d] = acc;
+    const long long rec = ((long long)b * p.Hq + kvh * p.G + gg) * p.splits + split;
+    p.ws[rec * D + d] = acc;
     if (d == 0) {
-      dst[D] = M;
-      dst[D + 1] = L;
+      float* ml = p.ws + (long long)p.B * p.Hq * p.splits * D + 2 * rec;
+      ml[0] = M;
+      ml[1] = L;
     }
   }
 }
 
-// Phase 2: one workgroup of 256 threads per (b, q-head), one memory round
-// trip.  Thread (c, g) owns chunks c, c + NC, ... and the 8-wide d slice g
-// (D / 8 slices); it loads all of its (m, l, acc-slice) records at once, then
-// the log-sum-exp merge runs from registers: M = max m_c (LDS max over the
-// chunk lanes), weights 2^(m_c - M), LDS sums of the weighted acc and l.
+// Phase 2: one wave per (b, q-head, 32-wide slice of d), one memory round
+// trip for up to 64 chunks.  Lane s holds chunk s's (m, l) and its 32 acc
+// values; lanes merge their own chunks first (more than 64 chunks: online, in
+// steps of 64), then the wave takes M = max m, rescales every lane's (l, acc)
+// by 2^(m - M), and sums l with lane shuffles and the 32 acc columns through
+// LDS.
 template <int D>
-__global__ void __launch_bounds__(256) decode_combine_kernel(const AttnParams p) {
-  constexpr int NG = D / 8;          // 8-wide d slices
-  constexpr int NC = 256 / NG;       // chunk lanes (16 for D = 128, 32 for D = 64)
-  constexpr int MAXR = 8;            // records per thread held at once (splits <= NC * MAXR)
-  __shared__ float s_m[256];
-  __shared__ float s_l[NC];
-  __shared__ float s_acc[NC][D + 4];
-  const int bh = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int c = tid / NG, g = tid % NG;
-  const float* base = p.ws + (long long)bh * p.splits * (D + 2);
+__global__ void __launch_bounds__(64) decode_combine_kernel(const AttnParams p) {
+  constexpr int NC = D / 32;  // d slices per head
+  __shared__ float red[64][33];
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x / NC, c = blockIdx.x % NC;
+  const long long n_rec = (long long)p.B * p.Hq * p.splits;
+  const float* accb = p.ws + (long long)bh * p.splits * D + 32 * c;
+  const float* mlb = p.ws + n_rec * D + (long long)bh * p.splits * 2;
 
   float M = -INFINITY, L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.splits; s0 += NC * MAXR) {
-    // Load a batch of records (independent loads, one round trip).
-    float mr[MAXR], lr[MAXR];
-    float2 vr[MAXR][4];
+  float a[32];
 #pragma unroll
-    for (int k = 0; k < MAXR; ++k) {
-      const int s = s0 + c + NC * k;
-      mr[k] = -INFINITY;
-      lr[k] = 0.f;
+  for (int e = 0; e < 32; ++e) a[e] = 0.f;
+  for (int s0 = 0; s0 < p.splits; s0 += 64) {
+    const int s = s0 + lane;
+    float m = -INFINITY, l = 0.f;
+    float4 v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vr[k][e] = make_float2(0.f, 0.f);
-      if (s < p.splits) {
-        const float* part = base + (long long)s * (D + 2);
-        mr[k] = part[D];
-        lr[k] = part[D + 1];
-        // part is 8-byte aligned (D + 2 floats per record).
+    for (int k = 0; k < 8; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s < p.splits) {
+      const float2 ml = *reinterpret_cast<const float2*>(mlb + 2 * s);
+      m = ml.x;
+      l = ml.y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[k][e] = *reinterpret_cast<const float2*>(part + 8 * g + 2 * e);
-      }
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const float4*>(accb + (long long)s * D + 4 * k);
     }
-    // Maximum over this batch and everything before it (all chunk lanes).
-    float mloc = M;
-#pragma unroll
-    for (int k = 0; k < MAXR; ++k) mloc = fmaxf(mloc, mr[k]);
-    s_m[tid] = mloc;
-    __syncthreads();
-    float Mn = -INFINITY;
-    for (int cc = 0; cc < NC; ++cc) Mn = fmaxf(Mn, s_m[cc * NG + g]);
-    __syncthreads();
-    // Rescale what was accumulated against the old maximum, then add the batch.
-    const float a0 = (M == -INFINITY || Mn == -INFINITY) ? 0.f : fast_exp2(M - Mn);
-    L *= a0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= a0;
+    const float Mn = fmaxf(M, m);
+    const float wa = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    const float wb = (m == -INFINITY) ? 0.f : fast_exp2(m - Mn);
     M = Mn;
+    L = L * wa + l * wb;
 #pragma unroll
-    for (int k = 0; k < MAXR; ++k) {
-      const float w = (mr[k] == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(mr[k] - M);
-      L = __builtin_fmaf(w, lr[k], L);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = __builtin_fmaf(w, vr[k][e].x, acc[2 * e]);
-        acc[2 * e + 1] = __builtin_fmaf(w, vr[k][e].y, acc[2 * e + 1]);
-      }
+    for (int k = 0; k < 8; ++k) {
+      a[4 * k + 0] = a[4 * k + 0] * wa + v[k].x * wb;
+      a[4 * k + 1] = a[4 * k + 1] * wa + v[k].y * wb;
+      a[4 * k + 2] = a[4 * k + 2] * wa + v[k].z * wb;
+      a[4 * k + 3] = a[4 * k + 3] * wa + v[k].w * wb;
     }
   }
-  // Sum over the NC chunk lanes (every lane holds the same M).
+  float Mg = M;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s_acc[c][8 * g + e] = acc[e];
-  if (g == 0) s_l[c] = L;
+  for (int off = 32; off >= 1; off /= 2) Mg = fmaxf(Mg, __shfl_xor(Mg, off));
+  const float w = (M == -INFINITY) ? 0.f : fast_exp2(M - Mg);
+  float Lg = L * w;
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) Lg += __shfl_xor(Lg, off);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) red[lane][e] = a[e] * w;
   __syncthreads();
-  for (int w = NC / 2; w >= 1; w /= 2) {
-    if (c < w) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[c][8 * g + e] += s_acc[c + w][8 * g + e];
-      if (g == 0) s_l[c] += s_l[c + w];
-    }
-    __syncthreads();
-  }
-  const float Lt = s_l[0];
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  // lane t sums column t % 32 over rows 32 * (t / 32) .. + 31; the halves meet by a swap
+  const int col = lane & 31, r0 = 32 * (lane >> 5);
+  float acc = 0.f;
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) acc += red[r0 + r][col];
+  acc += partner32(acc);
+  const float inv = Lg > 0.f ? 1.f / Lg : 0.f;
   const int b = bh / p.Hq, h = bh % p.Hq;
   __bf16* orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh;
-  const float oscale = inv * p.v_scale;  // v_scale: fp8 V cache dequantisation (else 1)
-  for (int d = tid; d < D; d += 256) orow[d] = (__bf16)(s_acc[0][d] * oscale);
-  if (p.lse && tid == 0) p.lse[bh] = Lt > 0.f ? (M + __builtin_log2f(Lt)) * kLn2 : -INFINITY;
+  if (lane < 32) orow[32 * c + lane] = (__bf16)(acc * inv * p.v_scale);  // v_scale: fp8 V cache
+  if (p.lse && c == 0 && lane == 0) p.lse[bh] = Lg > 0.f ? (Mg + __builtin_log2f(Lg)) * kLn2 : -INFINITY;
 }
 
 hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, bool kv8, unsigned grid,
@@ -350,11 +333,11 @@ hipError_t launch_decode_split(const AttnParams& p, int D, bool rope, bool kv8, 
 }
 
 hipError_t launch_decode_combine(const AttnParams& p, int D, hipStream_t stream) {
-  const unsigned grid = (unsigned)(p.B * p.Hq);
+  const unsigned grid = (unsigned)(p.B * p.Hq * (D / 32));
   if (D == 64) {
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(grid), dim3(64), 0, stream, p);
   } else if (D == 128) {
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(grid), dim3(64), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
