@@ -508,6 +508,20 @@ fwd_bf16_kernel(const AttnParams p) {
   const float* const brow =
       (SCOREMOD && p.bias) ? p.bias + b * p.bsb + h * p.bsh + (long long)iq * p.bsi : nullptr;
   const long long bsj = p.bsj;
+  // Bias fetched a tile ahead (two-wave-per-SIMD schedule, unit key stride,
+  // Nk a multiple of 4, 16-byte aligned rows): lane (lq, lh) needs, for
+  // g = 0..7, the four keys k0 + 8g + 4lh .. + 3 of its query row (S^T
+  // subtile g / 4, registers 4 (g % 4) .. + 3), one 16-byte load each.  Runs
+  // past the keys are clamped in bounds; those scores are masked.
+  const bool bias_vec = PP && SCOREMOD && brow && bsj == 1 && Nk >= 4 && (Nk & 3) == 0 &&
+                        __builtin_amdgcn_ballot_w64((reinterpret_cast<uintptr_t>(brow) & 15) != 0) == 0;
+  float4 bias4[8];
+  auto bias_fetch = [&](int k0) {
+    if (!bias_vec) return;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      bias4[g] = *reinterpret_cast<const float4*>(brow + min(k0 + 8 * g + 4 * lh, Nk - 4));
+  };
 
   // Dense key lists: tile u starts at key 64 * (t_begin + u), so the tiles
   // that need no mask (inside the key range and, with a band, wholly inside
@@ -571,7 +585,11 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr float kTrig = 15.f;  // largest exp2 argument taken without the exact path
   auto neg_m = [&]() -> float { return (m_run == -INFINITY) ? 0.f : -m_run; };
   // Per-lane, per-tile part of the exp2 argument: score mods' lane offset.
-  auto mod_base = [&](int k0) -> float { return SCOREMOD ? slope2 * (float)(k0 + 4 * lh - i + dpos) : 0.f; };
+  // With score mods the MFMAs start from 0 and minus the running maximum
+  // joins this offset (it saves the 16 registers of the splat below).
+  auto mod_base = [&](int k0) -> float {
+    return SCOREMOD ? __builtin_fmaf(slope2, (float)(k0 + 4 * lh - i + dpos), neg_m()) : 0.f;
+  };
   // The first score MFMA of every tile takes its C operand from minit, a
   // splat of minus the running maximum (updated only when the maximum
   // moves), so the MFMAs leave the exp2 argument itself: the scale is folded
@@ -584,8 +602,15 @@ fwd_bf16_kernel(const AttnParams p) {
     if (SCOREMOD) {
       x += __builtin_fmaf(slope2, (float)kOff(st, r), mod_base(k0));
       if (brow) {
-        const int j = min(k0 + 4 * lh + kOff(st, r), Nk - 1);
-        x = __builtin_fmaf(brow[(long long)j * bsj], kLog2e, x);
+        float bv;
+        if (bias_vec) {
+          const float4 b4 = bias4[4 * st + r / 4];
+          bv = (r % 4 == 0) ? b4.x : (r % 4 == 1) ? b4.y : (r % 4 == 2) ? b4.z : b4.w;
+        } else {
+          const int j = min(k0 + 4 * lh + kOff(st, r), Nk - 1);
+          bv = brow[(long long)j * bsj];
+        }
+        x = __builtin_fmaf(bv, kLog2e, x);
       }
     }
     return x;
@@ -665,7 +690,7 @@ fwd_bf16_kernel(const AttnParams p) {
     f32x16 s0[2];
 #pragma unroll
     for (int k = 0; k < 2 * NKK; ++k)
-      s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], k < 2 ? minit : s0[k & 1]);
+      s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], k < 2 ? (SCOREMOD ? f32x16{} : minit) : s0[k & 1]);
     mask_scores(0, s0);
     uint32_t pw[16];
 #pragma unroll
@@ -703,6 +728,7 @@ fwd_bf16_kernel(const AttnParams p) {
     }
     load_q_issue_staged();
     if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
+    if (n > 0) bias_fetch(tile_k0(0));
     vmcnt_wait<0>();
     // Q rows leave their staging area (K slot 3, V slots 2-3, ...) before
     // the barrier, after which those slots are refilled.  K(0) and K(1),
@@ -716,10 +742,13 @@ fwd_bf16_kernel(const AttnParams p) {
     __syncthreads();
     load_q_finish();
     if (n > 0) first_tile();
+    if (n > 1) bias_fetch(tile_k0(1));  // waited for by the next vector cluster
 
     constexpr int NST = 2 * NKK;  // MFMA pairs per cluster (S step + PV step)
     static_assert(NST == 4 * NDT, "one S and one PV MFMA per step");
-    constexpr int PF = 2;         // fragment prefetch distance
+    // Fragment prefetch distance (1 with score mods: their bias registers
+    // stay live through the MFMA cluster).
+    constexpr int PF = SCOREMOD ? 1 : 2;
     f32x16 sn[2];                 // S(t+1) from an MFMA cluster to the next vector cluster
     // The MFMA cluster runs at raised wave priority: when both waves of a SIMD
     // can issue, the matrix core is fed first (otherwise the older wave wins
@@ -757,7 +786,7 @@ fwd_bf16_kernel(const AttnParams p) {
           afr[(k + PF) % (PF + 1)] = kf((k + PF) & 1, (k + PF) >> 1);
           vfr[(k + PF) % (PF + 1)] = vf((k + PF) / NDT, (k + PF) % NDT);
         }
-        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? minit : sn[k & 1]);
+        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? (SCOREMOD ? f32x16{} : minit) : sn[k & 1]);
         o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
         if (k % NDT == NDT - 1) ol = mfma32(ones8, pf[k / NDT], ol);
         __builtin_amdgcn_sched_barrier(0);
@@ -804,6 +833,7 @@ fwd_bf16_kernel(const AttnParams p) {
         for (int x = 0; x < 16; ++x) pw[x] = exp_pair(sn, x, k0s);
         finish_tile(sn, -neg_m(), pw);
         to_frags(pw, pf_next);
+        if (st + 1 < n) bias_fetch(tile_k0(st + 1));
       }
       if (ROPE) {
         // Table entries of K(t+3) go into the slot read above: those reads
@@ -954,7 +984,7 @@ fwd_bf16_kernel(const AttnParams p) {
   #pragma unroll
       for (int k = 0; k < NSA; ++k) {
         if (k + PF < NSA) afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
-        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? minit : sn[k & 1]);
+        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? (SCOREMOD ? f32x16{} : minit) : sn[k & 1]);
         if (k & 1) dma_slot_a(g, k / 2);
         if (ROPE) {
           // Item ri runs at step 2 + ri / AIPS; its half's operands two steps earlier.

@@ -495,3 +495,54 @@ def test_decode_fp8_cache_short(Nk, splits):
                     q_pos0=Nk, k_scale=ks, v_scale=vs)
     ref, _ = oracle.attention(q, k, v, rope_theta=1e4, q_pos0=Nk)
     check_close(host(out), ref, "bf16", f"decode fp8 Nk={Nk}")
+
+
+BIAS_LAYOUTS = {
+    # name: (B, Hq, Hkv, Nq, Nk, D, layout, extra variant keywords)
+    "aligned_gqa_causal_d128": (2, 4, 2, 300, 332, 128, "full", dict(causal=True)),
+    "ragged_keys_d128": (1, 2, 2, 200, 330, 128, "full", dict()),
+    "broadcast_rows_window_rope_d64": (2, 4, 4, 260, 260, 64, "rows",
+                                       dict(window=90, causal=True, rope_theta=1e4)),
+    "key_major_view_d128": (1, 2, 1, 180, 200, 128, "transposed", dict(alibi=True)),
+    "misaligned_rows_d64": (1, 2, 2, 140, 192, 64, "offset", dict(causal=True)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BIAS_LAYOUTS))
+def test_additive_bias_layouts_eight_wave_tiles(name):
+    """The 8-wave prefill tile reads the bias of a key tile one step ahead as
+    16-byte runs when the key stride is 1, Nk is a multiple of 4 and every row
+    is 16-byte aligned, else element by element: both routes, with broadcast
+    (zero) strides, a key-major view and rows shifted by one element."""
+    B, Hq, Hkv, Nq, Nk, D, layout, extra = BIAS_LAYOUTS[name]
+    rng = np.random.default_rng(len(name))
+    (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16(s, rng) for s in
+                                 ((B, Hq, Nq, D), (B, Hkv, Nk, D), (B, Hkv, Nk, D)))
+    if layout == "full":
+        host_bias = rng.standard_normal((B, Hq, Nq, Nk)).astype(np.float32)
+        dev_bias = torch.from_numpy(host_bias).cuda()
+    elif layout == "rows":  # one plane for every (b, h)
+        plane = rng.standard_normal((Nq, Nk)).astype(np.float32)
+        host_bias = np.broadcast_to(plane, (B, Hq, Nq, Nk))
+        dev_bias = torch.from_numpy(plane).cuda().expand(B, Hq, Nq, Nk)
+    elif layout == "transposed":  # stored [B, Hq, Nk, Nq]: unit stride along queries
+        stored = rng.standard_normal((B, Hq, Nk, Nq)).astype(np.float32)
+        host_bias = np.swapaxes(stored, 2, 3)
+        dev_bias = torch.from_numpy(stored).cuda().transpose(2, 3)
+    else:  # rows of Nk + 1 floats, starting one element in
+        stored = rng.standard_normal((B, Hq, Nq, Nk + 1)).astype(np.float32)
+        host_bias = stored[..., 1:]
+        dev_bias = torch.from_numpy(stored).cuda()[..., 1:]
+    kw = {key: val for key, val in extra.items() if key != "alibi"}
+    okw = dict(kw)
+    if extra.get("alibi"):
+        sl = workloads.alibi_slopes(Hq)
+        kw["alibi_slopes"] = torch.from_numpy(sl).cuda()
+        okw["alibi_slopes"] = sl.astype(np.float64)
+    log(f"case bias layout {name} tile (8, 1)")
+    out, lse = af.fwd(to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), bias=dev_bias,
+                      return_lse=True, tile=(8, 1), **kw)
+    torch.cuda.synchronize()
+    ref, rlse = oracle.attention(q, k, v, bias=host_bias.astype(np.float64), **okw)
+    check_close(host(out), ref, "bf16", f"bias layout {name}")
+    check_lse(host(lse), rlse, 2e-2, f"bias layout {name}")
