@@ -69,13 +69,10 @@ int validate_common(const attnfuse_variant_desc* d) {
 }
 
 // RoPE tables each entry point reads: fp32 cos / sin for the fp32 prefill
-// and the pre-rotation pass; fp16 pairs for the bf16 prefill's Q and for
-// decode; bf16 pairs for the bf16 prefill's K.
+// and the pre-rotation pass; fp16 pairs for the bf16 prefill (Q and K) and
+// for decode.
 bool fp32_tables_ok(const attnfuse_variant_desc* d) {
   return !d->rope || (d->rope_cos && d->rope_sin && aligned16(d->rope_cos) && aligned16(d->rope_sin));
-}
-bool bf16_table_ok(const attnfuse_variant_desc* d) {
-  return !d->rope || (d->rope_cs_bf16 && aligned16(d->rope_cs_bf16));
 }
 bool f16_table_ok(const attnfuse_variant_desc* d) {
   return !d->rope || (d->rope_cs_f16 && aligned16(d->rope_cs_f16));
@@ -105,7 +102,6 @@ AttnParams base_params(const void* q, const void* k, const void* v, void* out,
   p.rcos = d->rope ? d->rope_cos : nullptr;
   p.rsin = d->rope ? d->rope_sin : nullptr;
   p.rcs = d->rope ? d->rope_cs_f16 : nullptr;
-  p.rcsb = d->rope ? d->rope_cs_bf16 : nullptr;
   p.rope_len = d->rope ? (int)(d->rope_table_len < kMaxLen ? d->rope_table_len : kMaxLen) : 0;
   p.q_pos0 = (int)d->q_pos0;
   p.k_pos0 = (int)d->k_pos0;
@@ -169,10 +165,10 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   // Q / out may be NULL only when there are no queries, K / V only when there
   // are no keys (empty tensors).
   if ((d->Nq > 0 && (!q || !out)) || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
-  // fp32 kernels read the fp32 tables; bf16 kernels rotate Q with the fp16
-  // pairs and K with the bf16 pairs.
+  // fp32 kernels read the fp32 tables; bf16 kernels rotate Q and K with the
+  // fp16 pairs.
   if (d->dtype == ATTNFUSE_FP32 && !fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
-  if (d->dtype == ATTNFUSE_BF16 && (!bf16_table_ok(d) || !f16_table_ok(d))) return ATTNFUSE_ERR_INVALID;
+  if (d->dtype == ATTNFUSE_BF16 && !f16_table_ok(d)) return ATTNFUSE_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return ATTNFUSE_ERR_UNSUPPORTED;
   const bool sparse = d->bs_row_ptr != nullptr;

@@ -44,7 +44,6 @@ struct AttnParams {
   const float* rcos;          // fp32 RoPE tables [len][D/2] (fp32 kernels) or nullptr
   const float* rsin;
   const uint32_t* rcs;        // fp16 (cos, sin) pairs [len][D/2] (decode) or nullptr
-  const uint32_t* rcsb;       // bf16 (cos, sin) pairs [len][D/2] (bf16 prefill K) or nullptr
   int rope_len;               // rows in the RoPE tables
   int q_pos0, k_pos0;
   // Allowed iff band_lo <= j - i <= band_hi (row/column index space; the
@@ -165,21 +164,27 @@ __device__ __forceinline__ uint4 scale_bf16x8(const uint4& x, float k) {
 }
 
 // NeoX rotation of element e (0 or 1) of a bf16 word pair, with the angle
-// given as a bf16 (cos, sin) word t (cos in the low half):
+// given as an fp16 (cos, sin) word t (cos in the low half):
 //   rl = l c - h s,  rh = h c + l s   (fp32 arithmetic on the exact bf16
-// values).  wl / wh hold elements (2w, 2w+1) of the low / high half.  Plain
+// values).  wl / wh hold elements (2w, 2w+1) of the low / high half.  Each
+// product reads its fp16 factor straight from a half of t (v_fma_mix_f32:
+// the products are written as FMAs with a +0 addend, which the compiler
+// cannot turn into plain multiplies), so the table needs no unpacking.  Plain
 // VALU arithmetic: the bf16 dot-product instructions would queue behind the
 // matrix core, which the partner wave keeps busy.
 __device__ __forceinline__ void rope_elem(uint32_t wl, uint32_t wh, int e, uint32_t t, float& rl,
                                           float& rh) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
   const float l = e ? bf16hi(wl) : bf16lo(wl);
   const float h = e ? bf16hi(wh) : bf16lo(wh);
-  const float c = bf16lo(t), s = bf16hi(t);
-  rl = __builtin_fmaf(l, c, -h * s);
-  rh = __builtin_fmaf(h, c, l * s);
+  const h2_t a = __builtin_bit_cast(h2_t, t);
+  const float c = (float)a[0], s = (float)a[1];
+  const float hs = __builtin_fmaf(h, s, 0.0f), ls = __builtin_fmaf(l, s, 0.0f);
+  rl = __builtin_fmaf(l, c, -hs);
+  rh = __builtin_fmaf(h, c, ls);
 }
 
-// Rotation of one (low, high) pair of 8-element bf16 chunks with bf16
+// Rotation of one (low, high) pair of 8-element bf16 chunks with fp16
 // (cos, sin) words t0 (elements 0-3) and t1 (elements 4-7).
 __device__ __forceinline__ void rope_rotate_bf16x8_t(uint4& lo, uint4& hi, const uint4& t0,
                                                      const uint4& t1) {

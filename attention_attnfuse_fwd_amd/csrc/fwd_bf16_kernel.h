@@ -8,7 +8,7 @@
 //   registers held) ->
 //   K rotated in place in LDS two tiles ahead ("4.1 Fused RoPE": each key is
 //   rotated once per workgroup by the thread that loaded it, in fp32 on the
-//   exact bf16 values, against a precomputed bf16 (cos, sin) table whose
+//   exact bf16 values, against a precomputed fp16 (cos, sin) table whose
 //   entries the thread fetched into a private LDS slot) ->
 //   MFMA operands (K row fragments; V read transposed by ds_read_b64_tr_b16).
 // Per tile and wave:  S^T = K' Q'^T (bf16 MFMA, fp32 acc), score mods and
@@ -40,7 +40,7 @@ namespace attnfuse {
 // LDS layout for head dim D (bytes): a ring of 4 K slots, a ring of 4 V
 // slots and (RoPE) one table slot.  A K slot holds the tile's RoPE halves,
 // each [64 rows][D/2]; a V slot is [64 rows][D]; the table slot holds, per K
-// instruction pair, 2 KiB of bf16 (cos, sin) words: 32 bytes per thread, the
+// instruction pair, 2 KiB of fp16 (cos, sin) words: 32 bytes per thread, the
 // 8 angles of the 8-element chunk it rotates, read back only by that thread.  Every 16-byte chunk
 // sits at an XOR-swizzled position inside its row so that the MFMA operand
 // reads are free of bank conflicts; a DMA instruction fills 1 KiB of
@@ -302,7 +302,7 @@ fwd_bf16_kernel(const AttnParams p) {
       const int prow = k_pos0 + g.k0t + L::KROWS_I * kp;
       const int row0 = min(prow, rope_last);
       const uint32_t off = min(toff, (uint32_t)min(rope_last - row0, 63) * (uint32_t)L::ROWB + tcol);
-      dma16_off(tslot + (uint32_t)kp * L::TPAIR + 1024u * x, p.rcsb + (long long)row0 * (D / 2),
+      dma16_off(tslot + (uint32_t)kp * L::TPAIR + 1024u * x, p.rcs + (long long)row0 * (D / 2),
                 off + 16u * x);
     } else {
       const int j = i - (2 + TPK) * nkw;
@@ -336,7 +336,7 @@ fwd_bf16_kernel(const AttnParams p) {
       if (m < nkw) {
         const int kp = wave + NW * m;
         const int row = min(k_pos0 + k0u + L::KROWS_I * kp + kjr, rope_last);
-        const uint32_t* tr = p.rcsb + (long long)row * (D / 2) + 8 * kc;
+        const uint32_t* tr = p.rcs + (long long)row * (D / 2) + 8 * kc;
         ptab[u][m][0] = ld16(tr);
         ptab[u][m][1] = ld16(tr + 4);
       }

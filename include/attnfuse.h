@@ -91,12 +91,11 @@ typedef struct attnfuse_variant_desc {
    *   rope_cs_f16: one 32-bit word per entry holding the fp16 pair (cos in
    *     bits 0-15, sin in bits 16-31; rounding at most 2^-12, well below the
    *     bf16 rounding of the rotated vectors).  Read by attnfuse_fwd with
-   *     dtype ATTNFUSE_BF16 (the Q rotation, in fp32 arithmetic) and by
-   *     attnfuse_decode.
-   *   rope_cs_bf16: the same pairs rounded to bf16 (at most 2^-9 relative,
-   *     the order of the bf16 rounding of the rotated keys themselves).  Read
-   *     by attnfuse_fwd with dtype ATTNFUSE_BF16 (the K rotation, fp32
-   *     arithmetic on the exact bf16 values).
+   *     dtype ATTNFUSE_BF16 (the Q and K rotations, fp32 arithmetic on the
+   *     exact bf16 values) and by attnfuse_decode.
+   *   rope_cs_bf16: the same pairs rounded to bf16, as attnfuse_rope_table
+   *     writes them.  No entry point reads it (the field keeps the
+   *     descriptor's layout); it may be NULL.
    * Build them with attnfuse_rope_table.  Every position used
    * (q_pos0 + Nq - 1, k_pos0 + Nk - 1) must be below rope_table_len.
    * rope_theta records the base the tables were built with.  A table an

@@ -115,8 +115,6 @@ def test_empty_query_is_ok_without_work(lib):
     (dict(window=-3), _abi.ERR_INVALID),
     (dict(q_pos0=-1), _abi.ERR_INVALID),
     (dict(rope=1), _abi.ERR_INVALID),                        # no tables
-    (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_table_len=100),
-     _abi.ERR_INVALID),                                      # bf16 prefill also reads the bf16 pairs (K)
     (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=10),
      _abi.ERR_INVALID),                                      # table shorter than the positions
     (dict(rope=1, rope_theta=1e4, rope_cos=0x1004, rope_sin=0x2000, rope_table_len=100,
@@ -125,8 +123,8 @@ def test_empty_query_is_ok_without_work(lib):
      _abi.ERR_INVALID),                                      # sin table missing
     (dict(rope=1, rope_theta=1e4, rope_cos=0x1000, rope_sin=0x2000, rope_table_len=100),
      _abi.ERR_INVALID),                                      # bf16 prefill reads the packed pairs, not fp32
-    (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_cs_bf16=0x3008,
-          rope_table_len=100), _abi.ERR_INVALID),            # misaligned bf16 pair table
+    (dict(rope=1, rope_theta=1e4, rope_cs_bf16=0x3000, rope_table_len=100),
+     _abi.ERR_INVALID),                                      # fp16 pair table missing (bf16 one is not read)
     (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1004, rope_cs_bf16=0x3000,
           rope_table_len=100), _abi.ERR_INVALID),            # misaligned fp16 pair table
     (dict(bs_row_ptr=0x1000, bs_block_m=0, bs_block_n=64), _abi.ERR_INVALID),
