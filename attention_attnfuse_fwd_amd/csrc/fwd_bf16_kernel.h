@@ -188,13 +188,20 @@ fwd_bf16_kernel(const AttnParams p) {
   // the keys) lands at k0 >= Nk, is loaded clamped and masked out entirely.
   // The list is read with scalar loads, which do not count against vmcnt.
   const int nkb = SPARSE ? (p.Nk + p.bn - 1) / p.bn : 0;
+  // With ALiBi slopes (positive: the bias grows towards the diagonal) a dense
+  // key list is visited from its last tile to its first, so the running
+  // maximum is set by the first tile and later tiles rarely move it (visited
+  // the other way, the maximum climbs by up to slope * 64 * log2(e) per tile
+  // and almost every tile takes the exact rescaling path).  The softmax does
+  // not depend on the order; masks and positions follow the tile's keys.
+  const bool rev = !SPARSE && SCOREMOD && p.alibi != nullptr;
   typedef __attribute__((address_space(4))) const int* cidx_t;
   auto tile_k0 = [&](int t) -> int {
     if (SPARSE) {
       const int col = min(max(((cidx_t)p.col_idx)[s_begin + t / tpb], 0), nkb);
       return col * p.bn + (t % tpb) * 64;
     }
-    return (t_begin + t) * 64;
+    return (t_begin + (rev ? n_tiles - 1 - t : t)) * 64;
   };
 
   const int Nk = p.Nk, band_lo = p.band_lo, band_hi = p.band_hi;
@@ -554,7 +561,8 @@ fwd_bf16_kernel(const AttnParams p) {
         need_mask |= (dmin < band_lo) | (dmax > band_hi);
       }
     } else {
-      need_mask = (u < mlo) | (u > mhi);
+      const int pu = rev ? n_tiles - 1 - u : u;  // tile's place in key order (< 0 past the list)
+      need_mask = (pu < mlo) | (pu > mhi);
     }
     if (need_mask) {
       const int k0 = tile_k0(min(u, n_tiles - 1));
