@@ -134,6 +134,12 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr int NKW_LO = L::NKP / NW;
   constexpr int TPK = ROPE ? 2 : 0;  // table instructions per K pair
   constexpr bool PP = NW == 8;       // ping-pong schedule (two waves per SIMD)
+  // Score mods: the first score MFMAs of a tile start from a splat of the
+  // lane's offset (ALiBi at the register's base key, minus the running
+  // maximum), leaving one FMA per score for the ALiBi step; the D = 128
+  // eight-wave instance has no 16 registers to spare (it holds the bias tile
+  // fetched ahead) and starts from 0, adding the offset per score.
+  constexpr bool CSPLAT = SCOREMOD && !(D == 128 && NW == 8);
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -593,8 +599,8 @@ fwd_bf16_kernel(const AttnParams p) {
   constexpr float kTrig = 15.f;  // largest exp2 argument taken without the exact path
   auto neg_m = [&]() -> float { return (m_run == -INFINITY) ? 0.f : -m_run; };
   // Per-lane, per-tile part of the exp2 argument: score mods' lane offset.
-  // With score mods the MFMAs start from 0 and minus the running maximum
-  // joins this offset (it saves the 16 registers of the splat below).
+  // With score mods minus the running maximum joins this offset (the MFMAs
+  // start from it, or from 0 in the instance without the registers).
   auto mod_base = [&](int k0) -> float {
     return SCOREMOD ? __builtin_fmaf(slope2, (float)(k0 + 4 * lh - i + dpos), neg_m()) : 0.f;
   };
@@ -608,7 +614,8 @@ fwd_bf16_kernel(const AttnParams p) {
   auto arg = [&](const f32x16 (&s)[2], int st, int r, int k0) -> float {
     float x = s[st][r];
     if (SCOREMOD) {
-      x += __builtin_fmaf(slope2, (float)kOff(st, r), mod_base(k0));
+      if (CSPLAT) x = __builtin_fmaf(slope2, (float)kOff(st, r), x);
+      else x += __builtin_fmaf(slope2, (float)kOff(st, r), mod_base(k0));
       if (brow) {
         float bv;
         if (bias_vec) {
@@ -698,7 +705,7 @@ fwd_bf16_kernel(const AttnParams p) {
     f32x16 s0[2];
 #pragma unroll
     for (int k = 0; k < 2 * NKK; ++k)
-      s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], k < 2 ? (SCOREMOD ? f32x16{} : minit) : s0[k & 1]);
+      s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], k < 2 ? (SCOREMOD ? (CSPLAT ? f32x16{} + mod_base(k00) : f32x16{}) : minit) : s0[k & 1]);
     mask_scores(0, s0);
     uint32_t pw[16];
 #pragma unroll
@@ -763,6 +770,7 @@ fwd_bf16_kernel(const AttnParams p) {
     // and the second half's MFMA clusters stretch).
     auto mcluster = [&](int t, const bf16x8 (&pf)[4]) {
       __builtin_amdgcn_s_setprio(1);
+      const float cb = CSPLAT ? mod_base(tile_k0(min(t + 1, n - 1))) : 0.f;
       // One VGPR base per K chunk column and per V d tile for this step's
       // slots; the rest of every operand address is an instruction offset.
       const uint32_t ks = lds0 + (uint32_t)((t + 1) % RING) * L::KSLOT;
@@ -794,7 +802,7 @@ fwd_bf16_kernel(const AttnParams p) {
           afr[(k + PF) % (PF + 1)] = kf((k + PF) & 1, (k + PF) >> 1);
           vfr[(k + PF) % (PF + 1)] = vf((k + PF) / NDT, (k + PF) % NDT);
         }
-        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? (SCOREMOD ? f32x16{} : minit) : sn[k & 1]);
+        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? (SCOREMOD ? (CSPLAT ? f32x16{} + cb : f32x16{}) : minit) : sn[k & 1]);
         o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
         if (k % NDT == NDT - 1) ol = mfma32(ones8, pf[k / NDT], ol);
         __builtin_amdgcn_sched_barrier(0);
@@ -992,7 +1000,7 @@ fwd_bf16_kernel(const AttnParams p) {
   #pragma unroll
       for (int k = 0; k < NSA; ++k) {
         if (k + PF < NSA) afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
-        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? (SCOREMOD ? f32x16{} : minit) : sn[k & 1]);
+        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? (SCOREMOD ? (CSPLAT ? f32x16{} + mod_base(k0n) : f32x16{}) : minit) : sn[k & 1]);
         if (k & 1) dma_slot_a(g, k / 2);
         if (ROPE) {
           // Item ri runs at step 2 + ri / AIPS; its half's operands two steps earlier.
