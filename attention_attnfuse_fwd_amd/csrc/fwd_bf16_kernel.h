@@ -114,7 +114,9 @@ __device__ __forceinline__ float tree_max32(const f32x16& a, const f32x16& b) {
 // r, by a lane in half lh: 32*st + 8*(r/4) + 4*lh + r%4.  kOff omits 4*lh.
 __device__ __forceinline__ constexpr int kOff(int st, int r) { return 32 * st + 8 * (r / 4) + (r % 4); }
 
-template <int D, int NW, bool ROPE, bool SCOREMOD, bool SPARSE>
+// BIAS: an additive bias may be present (else only ALiBi slopes, with
+// SCOREMOD); the instances without it keep the registers of the bias tile.
+template <int D, int NW, bool ROPE, bool SCOREMOD, bool SPARSE, bool BIAS>
 __global__ void __launch_bounds__(NW * 64)
 fwd_bf16_kernel(const AttnParams p) {
   using L = TileLds<D>;
@@ -139,7 +141,7 @@ fwd_bf16_kernel(const AttnParams p) {
   // maximum), leaving one FMA per score for the ALiBi step; the D = 128
   // eight-wave instance has no 16 registers to spare (it holds the bias tile
   // fetched ahead) and starts from 0, adding the offset per score.
-  constexpr bool CSPLAT = SCOREMOD && !(D == 128 && NW == 8);
+  constexpr bool CSPLAT = SCOREMOD && !(D == 128 && NW == 8 && BIAS);
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -519,7 +521,7 @@ fwd_bf16_kernel(const AttnParams p) {
   float slope2 = 0.f;  // ALiBi slope times log2(e), loaded in the prologue
   const int dpos = p.k_pos0 - p.q_pos0;
   const float* const brow =
-      (SCOREMOD && p.bias) ? p.bias + b * p.bsb + h * p.bsh + (long long)iq * p.bsi : nullptr;
+      (SCOREMOD && BIAS && p.bias) ? p.bias + b * p.bsb + h * p.bsh + (long long)iq * p.bsi : nullptr;
   const long long bsj = p.bsj;
   // Bias fetched a tile ahead (two-wave-per-SIMD schedule, unit key stride,
   // Nk a multiple of 4, 16-byte aligned rows): lane (lq, lh) needs, for
