@@ -5,7 +5,7 @@ a split-KV decode with a log-sum-exp combine, and the attention backward.
 The compute lives in ``libattnfuse.so`` (C ABI in ``include/attnfuse.h``);
 this package only marshals PyTorch tensors and streams into it.
 """
-from ._abi import LIB_PATH, LibraryNotBuilt, VariantDesc, load as load_library  # noqa: F401
+from ._abi import LIB_PATH, LibraryNotBuilt, VariantDesc, library_identity, load as load_library  # noqa: F401
 from .ops import (AttnfuseError, BlockMask, block_mask_from_csr, bwd, bwd_workspace_size,  # noqa: F401
                   create_block_mask,
                   decode, decode_workspace_size, default_num_splits, fwd, prerotate,
@@ -14,5 +14,5 @@ from .ops import (AttnfuseError, BlockMask, block_mask_from_csr, bwd, bwd_worksp
 __all__ = [
     "fwd", "bwd", "bwd_workspace_size", "decode", "decode_workspace_size", "default_num_splits", "prerotate",
     "rope_tables", "create_block_mask", "block_mask_from_csr", "BlockMask", "AttnfuseError",
-    "load_library", "LIB_PATH", "LibraryNotBuilt", "VariantDesc",
+    "load_library", "library_identity", "LIB_PATH", "LibraryNotBuilt", "VariantDesc",
 ]

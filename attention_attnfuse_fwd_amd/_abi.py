@@ -8,10 +8,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-# ATTNFUSE_LIB may point at another build of the same library (A/B timing of
-# kernel versions); by default the in-tree build next to this file is used.
-LIB_PATH = os.environ.get("ATTNFUSE_LIB") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libattnfuse.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattnfuse.so")
 
 OK = 0
 ERR_INVALID = -1
@@ -24,7 +21,7 @@ FP32 = 1
 NORM_SOFTMAX = 0
 NORM_RELU = 1
 
-# Every function the header declares (checked against the header by the tests).
+# Every function the headers declare (checked against include/*.h by the tests).
 EXPORTS = (
     "attnfuse_fwd",
     "attnfuse_decode_workspace_size",
@@ -34,6 +31,10 @@ EXPORTS = (
     "attnfuse_bwd_workspace_size",
     "attnfuse_bwd",
     "attnfuse_status_string",
+    # include/attnfuse_microbench.h
+    "attnfuse_mb_mfma_bf16",
+    "attnfuse_mb_hbm_read",
+    "attnfuse_mb_host_cost",
 )
 
 
@@ -124,8 +125,26 @@ def load() -> ctypes.CDLL:
     lib.attnfuse_bwd.restype = ctypes.c_int
     lib.attnfuse_status_string.argtypes = [ctypes.c_int]
     lib.attnfuse_status_string.restype = ctypes.c_char_p
+    lib.attnfuse_mb_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.attnfuse_mb_mfma_bf16.restype = ctypes.c_int
+    lib.attnfuse_mb_hbm_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int32, P, P, P]
+    lib.attnfuse_mb_hbm_read.restype = ctypes.c_int
+    lib.attnfuse_mb_host_cost.argtypes = [ctypes.c_int32, P, P, P, P, D, ctypes.c_int32, P, ctypes.c_size_t,
+                                          ctypes.c_int32, ctypes.POINTER(ctypes.c_double), P]
+    lib.attnfuse_mb_host_cost.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def library_identity() -> dict:
+    """Path and sha256 of the library file this process loads."""
+    import hashlib
+    h = hashlib.sha256()
+    with open(LIB_PATH, "rb") as fh:
+        for chunk in iter(lambda: fh.read(1 << 20), b""):
+            h.update(chunk)
+    return {"path": os.path.relpath(LIB_PATH, os.path.dirname(os.path.dirname(LIB_PATH))),
+            "sha256": h.hexdigest()}
 
 
 def status_string(status: int) -> str:

@@ -2,9 +2,11 @@
 // cos / sin table; NeoX half-split pairs (r, r + D/2)).
 //
 //  * rope_table: cos / sin of p * theta^(-2r/D), angle formed in fp64 (an fp32
-//    angle at p ~ 3e4 would carry ~2e-3 rad of error), rounded to fp32, and
-//    packed as fp16 pairs (decode kernel) and bf16 pairs (the bf16 prefill
-//    kernel rotates K with bf16 dot products).
+//    angle at p ~ 3e4 would carry ~2e-3 rad of error), rounded to fp32 (fp32
+//    prefill, pre-rotation pass), packed as fp16 (cos, sin) pairs (the bf16
+//    prefill's Q and K rotations and the decode's K rotation, fp32 arithmetic
+//    with the fp16 factors) and, on request, as bf16 pairs (no kernel of this
+//    library reads those).
 //  * prerotate: the separate rotation pass that the fused kernel replaces
 //    ("1 Introduction": the pre-rotation workaround costs two extra memory
 //    round trips; "5.3 The Rotation Calculus" weighs the two).  Rotates a

@@ -16,13 +16,12 @@ libattnfuse.so, so "compiling" a program means validating it and fixing its
 descriptor constants.  Tensors flow straight to ``ops.fwd`` / ``ops.bwd``.
 
     @attention
-    def llama_attn(Q, K, V, theta=500000.0):
-        s = rope(Q, K, theta=theta)
-        s = causal(s)
-        return softmax(s) @ V
+    def local_alibi(Q, K, V, w=1024):
+        banded = sliding_window(causal(scaled_dot_product(Q, K)), w)
+        return softmax(alibi(banded)) @ V
 
-    out = llama_attn(q, k, v)                      # traced on the first call
-    out = llama_attn(q, k, v, theta=10000.0)       # another configuration
+    out = local_alibi(q, k, v, alibi_slopes=slopes)          # traced on the first call
+    out = local_alibi(q, k, v, w=256, alibi_slopes=slopes)   # another configuration
 """
 from __future__ import annotations
 

@@ -37,8 +37,26 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _raw_stream(device: torch.device) -> int:
+    """Handle of the current stream of ``device`` as an int."""
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# Prepared descriptors of calls whose descriptor holds no per-call pointer
+# (no lse output, ALiBi slopes, bias or block mask): keyed by everything the
+# descriptor is built from, so a repeated call skips the marshalling.  A
+# cached descriptor is never modified after it is stored.
+_FWD_DESCS: dict = {}
+_DECODE_DESCS: dict = {}
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -53,28 +71,69 @@ def _dtype_code(t: torch.Tensor) -> int:
 # RoPE tables
 # ----------------------------------------------------------------------------
 
+class _RopeEntry:
+    """One cached table set: fp32 cos, fp32 sin and packed fp16 (cos, sin)
+    words, built asynchronously on ``stream``; ``ready`` marks the end of the
+    build on that stream."""
+    __slots__ = ("cos", "sin", "cs16", "ready", "stream", "done")
+
+    def __init__(self, cos, sin, cs16, ready, stream):
+        self.cos, self.sin, self.cs16 = cos, sin, cs16
+        self.ready, self.stream, self.done = ready, stream, False
+
+
 _ROPE_CACHE: dict = {}
+# Tables replaced by longer ones stay alive until the process ends: kernels
+# already queued on any stream may still read them.
+_ROPE_RETIRED: list = []
 
 
-def rope_tables(theta: float, D: int, length: int, device) -> tuple:
-    """(cos, sin, cs_f16, cs_bf16) tables [L][D/2] with L >= length, built on the device
-    and cached: fp32 cos and sin, and the packed fp16 and bf16 (cos, sin) pairs."""
-    device = torch.device(device)
-    key = (float(theta), int(D), device.index if device.index is not None else torch.cuda.current_device())
+def _rope_entry(theta: float, D: int, length: int, device: torch.device) -> _RopeEntry:
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (float(theta), int(D), index)
     hit = _ROPE_CACHE.get(key)
-    if hit is not None and hit[0].shape[0] >= length:
+    if hit is not None and hit.cos.shape[0] >= length:
         return hit
     L = max(int(length), 1)
     if hit is not None:
-        L = max(L, 2 * hit[0].shape[0])
+        L = max(L, 2 * hit.cos.shape[0])
+        _ROPE_RETIRED.append(hit)
     cos = torch.empty((L, D // 2), dtype=torch.float32, device=device)
     sin = torch.empty_like(cos)
     cs16 = torch.empty((L, D // 2), dtype=torch.int32, device=device)
-    csb16 = torch.empty((L, D // 2), dtype=torch.int32, device=device)
+    stream = torch.cuda.current_stream(device)
     _check(_abi.load().attnfuse_rope_table(float(theta), int(D), int(L), _ptr(cos), _ptr(sin),
-                                           _ptr(cs16), _ptr(csb16), _stream(device)), "rope_table")
-    _ROPE_CACHE[key] = (cos, sin, cs16, csb16)
-    return cos, sin, cs16, csb16
+                                           _ptr(cs16), None, ctypes.c_void_p(stream.cuda_stream)),
+           "rope_table")
+    ready = torch.cuda.Event()
+    ready.record(stream)
+    entry = _RopeEntry(cos, sin, cs16, ready, stream.cuda_stream)
+    _ROPE_CACHE[key] = entry
+    return entry
+
+
+def _rope_ready_on(entry: _RopeEntry, device: torch.device):
+    """Order the current stream after the table's build (once the build is
+    known to be complete, no further waits are issued)."""
+    if entry.done:
+        return
+    if entry.ready.query():
+        entry.done = True
+        return
+    cur = torch.cuda.current_stream(device)
+    if cur.cuda_stream != entry.stream:
+        cur.wait_event(entry.ready)
+
+
+def rope_tables(theta: float, D: int, length: int, device) -> tuple:
+    """(cos, sin, cs_f16) tables [L][D/2] with L >= length, built on the device
+    and cached per (theta, D, device): fp32 cos and sin (fp32 kernels, the
+    pre-rotation pass) and the packed fp16 (cos, sin) words the bf16 kernels
+    read.  The current stream is ordered after the build."""
+    device = torch.device(device)
+    entry = _rope_entry(theta, D, length, device)
+    _rope_ready_on(entry, device)
+    return entry.cos, entry.sin, entry.cs16
 
 
 # ----------------------------------------------------------------------------
@@ -159,13 +218,12 @@ def _make_desc(q, k, v, out, *, scale, causal, window, rope_theta, q_pos0, k_pos
     d.window = int(window or 0)
     if rope_theta is not None:
         need = max(int(q_pos0) + Nq, int(k_pos0) + Nk)
-        cos, sin, cs16, csb16 = rope_tables(rope_theta, D, need, q.device)
-        keep.extend([cos, sin, cs16, csb16])
+        cos, sin, cs16 = rope_tables(rope_theta, D, need, q.device)
+        keep.extend([cos, sin, cs16])
         d.rope = 1
         d.rope_theta = float(rope_theta)
         d.rope_cos, d.rope_sin = cos.data_ptr(), sin.data_ptr()
         d.rope_cs_f16 = cs16.data_ptr()
-        d.rope_cs_bf16 = csb16.data_ptr()
         d.rope_table_len = cos.shape[0]
     if alibi_slopes is not None:
         a = torch.as_tensor(alibi_slopes, dtype=torch.float32).to(q.device).contiguous()
@@ -222,6 +280,20 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     decode path, as the pages' runtime dispatch does.  ``tile = (waves, heads)``
     overrides the library's tile table for the bf16 prefill kernel.
     """
+    cacheable = (out is not None and not return_lse and alibi_slopes is None and bias is None
+                 and block_mask is None and tile is None)
+    if cacheable:
+        key = (q.shape, q.stride(), k.shape, k.stride(), v.shape, v.stride(), out.shape, out.stride(),
+               q.dtype, k.dtype, v.dtype, out.dtype, q.device, k.device, v.device, out.device,
+               causal, window, rope_theta, q_pos0, k_pos0, scale, decode_fast_path)
+        hit = _FWD_DESCS.get(key)
+        if hit is not None:
+            dref, entry = hit
+            if entry is not None:
+                _rope_ready_on(entry, q.device)
+            _check(_abi.load().attnfuse_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                            dref, _raw_stream(q.device)), "fwd")
+            return out
     _check_inputs(q, k, v)
     if (decode_fast_path and q.shape[2] == 1 and q.dtype == torch.bfloat16 and bias is None
             and block_mask is None and k.shape[2] > 0):
@@ -240,6 +312,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
     _check(_abi.load().attnfuse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(d),
                                     _stream(q.device)), "fwd")
+    if cacheable:
+        entry = (_ROPE_CACHE.get((float(rope_theta), int(q.shape[3]), q.device.index))
+                 if rope_theta is not None else None)
+        if entry is None or entry.cos.data_ptr() == d.rope_cos:
+            _FWD_DESCS[key] = (ctypes.byref(d), entry)
     return (out, lse) if return_lse else out
 
 
@@ -268,6 +345,23 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     The cache is bf16 like q, or FP8 E4M3 codes (``torch.float8_e4m3fn``, or
     their bytes as ``torch.uint8``) holding rows ``k_scale * code`` and
     ``v_scale * code``."""
+    cacheable = (out is not None and workspace is not None and not return_lse and alibi_slopes is None
+                 and num_splits is not None)
+    if cacheable:
+        key = (q.shape, q.stride(), k_cache.shape, k_cache.stride(), v_cache.shape, v_cache.stride(),
+               out.shape, out.stride(), q.dtype, k_cache.dtype, v_cache.dtype, out.dtype, q.device,
+               k_cache.device, v_cache.device, out.device, num_splits, causal, window, rope_theta,
+               q_pos0, k_pos0, scale, k_scale, v_scale, workspace.device)
+        hit = _DECODE_DESCS.get(key)
+        nbytes = workspace.numel() * workspace.element_size()
+        if hit is not None and nbytes >= hit[2]:
+            dref, entry, _ = hit
+            if entry is not None:
+                _rope_ready_on(entry, q.device)
+            _check(_abi.load().attnfuse_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                               out.data_ptr(), dref, int(num_splits), workspace.data_ptr(),
+                                               nbytes, _raw_stream(q.device)), "decode")
+            return out
     kv_fp8 = k_cache.dtype in _FP8_DTYPES
     if kv_fp8:
         if v_cache.dtype != k_cache.dtype or q.dtype != torch.bfloat16:
@@ -299,6 +393,11 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     _check(lib.attnfuse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), ctypes.byref(d),
                                int(num_splits), _ptr(workspace), nbytes, _stream(q.device)),
            "decode")
+    if cacheable:
+        entry = (_ROPE_CACHE.get((float(rope_theta), int(D), q.device.index))
+                 if rope_theta is not None else None)
+        if entry is None or entry.cos.data_ptr() == d.rope_cos:
+            _DECODE_DESCS[key] = (ctypes.byref(d), entry, need)
     return (out, lse) if return_lse else out
 
 

@@ -14,6 +14,8 @@ from attention_attnfuse_fwd_amd import _abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attnfuse.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced (validation fails first)
 
 
@@ -23,9 +25,12 @@ def lib():
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(attnfuse_[a-z_0-9]+)\s*\(", src)))
+    names = set()
+    for path in HEADERS:
+        src = open(path).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(attnfuse_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_exactly_the_binding_exports():
@@ -230,3 +235,22 @@ def test_product_does_not_import_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", txt, flags=re.M), f
                 assert "oracle/" not in txt, f
+
+
+def test_microbench_entry_points_reject_bad_arguments(lib):
+    """The machine-peak probes validate on the host and launch nothing on error."""
+    P = ctypes.c_void_p
+    sink, stamps = P(0x100000), P(0x200000)
+    assert lib.attnfuse_mb_mfma_bf16(0, 10, sink, stamps, None) == -1
+    assert lib.attnfuse_mb_mfma_bf16(1, 0, sink, stamps, None) == -1
+    assert lib.attnfuse_mb_mfma_bf16(1, 10, None, stamps, None) == -1
+    assert lib.attnfuse_mb_hbm_read(P(0x100000), 15, 1, sink, stamps, None) == -1
+    assert lib.attnfuse_mb_hbm_read(P(0x100008), 1024, 1, sink, stamps, None) == -1
+    assert lib.attnfuse_mb_hbm_read(None, 1024, 1, sink, stamps, None) == -1
+    ns = ctypes.c_double(0)
+    assert lib.attnfuse_mb_host_cost(3, None, None, None, None, None, 0, None, 0, 10, ctypes.byref(ns),
+                                     None) == -1
+    assert lib.attnfuse_mb_host_cost(0, None, None, None, None, None, 0, None, 0, 10, ctypes.byref(ns),
+                                     None) == -1
+    assert lib.attnfuse_mb_host_cost(2, None, None, None, None, None, 0, None, 0, 0, ctypes.byref(ns),
+                                     None) == -1
