@@ -16,6 +16,9 @@ ERR_UNSUPPORTED = -2
 ERR_WORKSPACE = -3
 ERR_HIP = -4
 
+# attnfuse_decode_noalloc's static partials buffer (ATTNFUSE_DECODE_NOALLOC_MAX_BYTES)
+DECODE_NOALLOC_MAX_BYTES = 8 << 20
+
 BF16 = 0
 FP32 = 1
 NORM_SOFTMAX = 0
@@ -26,6 +29,7 @@ EXPORTS = (
     "attnfuse_fwd",
     "attnfuse_decode_workspace_size",
     "attnfuse_decode",
+    "attnfuse_decode_noalloc",
     "attnfuse_rope_table",
     "attnfuse_prerotate",
     "attnfuse_bwd_workspace_size",
@@ -115,6 +119,8 @@ def load() -> ctypes.CDLL:
     lib.attnfuse_decode_workspace_size.restype = ctypes.c_size_t
     lib.attnfuse_decode.argtypes = [P, P, P, P, D, ctypes.c_int32, P, ctypes.c_size_t, P]
     lib.attnfuse_decode.restype = ctypes.c_int
+    lib.attnfuse_decode_noalloc.argtypes = [P, P, P, P, D, ctypes.c_int32, P]
+    lib.attnfuse_decode_noalloc.restype = ctypes.c_int
     lib.attnfuse_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int64, P, P, P, P, P]
     lib.attnfuse_rope_table.restype = ctypes.c_int
     lib.attnfuse_prerotate.argtypes = [P, P, D, ctypes.c_int32, P]

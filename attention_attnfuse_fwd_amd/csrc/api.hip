@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/attnfuse.h"
@@ -275,9 +277,14 @@ size_t attnfuse_decode_workspace_size(const attnfuse_variant_desc* desc, int32_t
   return (size_t)desc->B * desc->Hq * num_splits * (desc->D + 2) * sizeof(float);
 }
 
-int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
-                    const attnfuse_variant_desc* desc, int32_t num_splits, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Split-KV decode on a partials buffer `workspace` of `workspace_bytes`.
+int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* out,
+                const attnfuse_variant_desc* desc, int32_t num_splits, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
@@ -308,6 +315,58 @@ int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, voi
                                                (unsigned)grid, s);
   if (e != hipSuccess) return ATTNFUSE_ERR_HIP;
   return hip_status(attnfuse::launch_decode_combine(p, d->D, s));
+}
+
+constexpr size_t kScratchBytes = ATTNFUSE_DECODE_NOALLOC_MAX_BYTES;
+
+}  // namespace
+
+namespace attnfuse {
+// Partials buffer of attnfuse_decode_noalloc: one static array per GPU (the
+// code object's copy on that device), never allocated at run time.  In host
+// code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+}  // namespace attnfuse
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure).
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(attnfuse::scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                    const attnfuse_variant_desc* desc, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, out, desc, num_splits, workspace, workspace_bytes, stream);
+}
+
+int attnfuse_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out,
+                            const attnfuse_variant_desc* desc, int32_t num_splits, void* stream) {
+  int st = validate_common(desc);
+  if (st != ATTNFUSE_OK) return st;
+  if (num_splits < 1 || num_splits > 4096) return ATTNFUSE_ERR_INVALID;
+  if (attnfuse_decode_workspace_size(desc, num_splits) > kScratchBytes) return ATTNFUSE_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return ATTNFUSE_ERR_HIP;
+  return decode_impl(q, k_cache, v_cache, out, desc, num_splits, ws, kScratchBytes, stream);
 }
 
 namespace {

@@ -401,6 +401,36 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     return (out, lse) if return_lse else out
 
 
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, out: torch.Tensor, *,
+                   num_splits: int, causal: bool = False, window: int = 0,
+                   rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
+                   alibi_slopes: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                   lse: Optional[torch.Tensor] = None, k_scale: float = 1.0, v_scale: float = 1.0):
+    """``decode`` without a workspace (``attnfuse_decode_noalloc``): the
+    partials go to the library's static per-GPU buffer, so neither this call
+    nor the library allocates device memory (``out``, and ``lse`` [B, Hq, 1]
+    fp32 when wanted, are the caller's; the RoPE table must already be built,
+    e.g. by ``rope_tables``, or it is built and cached on first use).  Calls
+    that may overlap on one GPU race on that buffer.  Returns ``out``."""
+    kv_fp8 = k_cache.dtype in _FP8_DTYPES
+    if not kv_fp8:
+        _check_inputs(q, k_cache, v_cache)
+    elif not (q.is_cuda and k_cache.is_cuda and v_cache.is_cuda) or k_cache.shape != v_cache.shape:
+        raise ValueError("q, k_cache, v_cache must be GPU tensors, k and v of one shape")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, 1] tensor")
+    keep = []
+    d = _make_desc(q, k_cache, v_cache, out, scale=scale, causal=causal, window=window,
+                   rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0, alibi_slopes=alibi_slopes,
+                   bias=None, block_mask=None, lse=lse, keep=keep)
+    if kv_fp8:
+        d.kv_fp8, d.k_scale, d.v_scale = 1, float(k_scale), float(v_scale)
+    _check(_abi.load().attnfuse_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                               ctypes.byref(d), int(num_splits), _stream(q.device)),
+           "decode_noalloc")
+    return out
+
+
 def bwd_workspace_size(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
                        window: int = 0, rope_theta: Optional[float] = None, q_pos0: int = 0,
                        k_pos0: int = 0) -> int:

@@ -28,7 +28,9 @@
  *  * Every pointer argument is caller-owned DEVICE memory (except `desc`,
  *    which is host memory read during the call only).  The library
  *    allocates nothing, keeps no pointer after returning, and holds no mutable
- *    global state, so calls from several host threads are safe.
+ *    global state, so calls from several host threads are safe.  (The one
+ *    exception is attnfuse_decode_noalloc, which writes a static per-GPU
+ *    buffer of the library instead of a caller workspace; see there.)
  *  * `stream` is a hipStream_t (NULL = the default stream).  All GPU work is
  *    enqueued asynchronously on it; the caller keeps buffers alive until the
  *    stream has completed the work.  No call synchronises.
@@ -199,6 +201,28 @@ size_t attnfuse_decode_workspace_size(const attnfuse_variant_desc* desc, int32_t
 int attnfuse_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
                     const attnfuse_variant_desc* desc, int32_t num_splits,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Largest partials buffer attnfuse_decode_noalloc can use (8 MiB). */
+#define ATTNFUSE_DECODE_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+
+/* attnfuse_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same two kernels and results as attnfuse_decode with the same
+ * arguments, but the partials go to a static buffer of
+ * ATTNFUSE_DECODE_NOALLOC_MAX_BYTES that the library holds on each GPU it
+ * runs on (until the process ends) instead of a caller workspace.  The call
+ * itself allocates nothing; the first call on a device looks up that
+ * device's buffer address once.  A call whose partials would exceed the
+ * buffer (attnfuse_decode_workspace_size(desc, num_splits) >
+ * ATTNFUSE_DECODE_NOALLOC_MAX_BYTES, e.g. B * Hq * num_splits > 16,131 at
+ * D = 128) returns ATTNFUSE_ERR_WORKSPACE with nothing enqueued; other errors
+ * as attnfuse_decode.  Every call on one GPU shares that GPU's buffer: calls
+ * that may overlap in time on one GPU (different streams, or different host
+ * threads without ordering) race on it and must be serialised by the
+ * caller; calls on one stream are ordered and safe.  The buffer's contents
+ * on entry do not matter (phase 1 writes every partial phase 2 reads). */
+int attnfuse_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out,
+                            const attnfuse_variant_desc* desc, int32_t num_splits, void* stream);
 
 /* RoPE tables ("4.1 Fused RoPE": a precomputed cos / sin table):
  * cos_out[p][r] = cos(p * theta^(-2r/D)), sin_out likewise, for

@@ -254,3 +254,27 @@ def test_microbench_entry_points_reject_bad_arguments(lib):
                                      None) == -1
     assert lib.attnfuse_mb_host_cost(2, None, None, None, None, None, 0, None, 0, 0, ctypes.byref(ns),
                                      None) == -1
+
+
+def test_decode_noalloc_rejects_oversized_partials_before_any_hip_call(lib):
+    """attnfuse_decode_noalloc checks the partials size against its static
+    buffer on the host: too many (batch, head, split) records -> WORKSPACE."""
+    d = _abi.VariantDesc.new()
+    d.dtype, d.B, d.Hq, d.Hkv, d.Nq, d.Nk, d.D = _abi.BF16, 1, 64, 8, 1, 32768, 128
+    for f in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        arr = getattr(d, f)
+        arr[0], arr[1], arr[2] = 64 * 128, 128, 128
+    splits_max = _abi.DECODE_NOALLOC_MAX_BYTES // (d.B * d.Hq * (d.D + 2) * 4)
+    assert lib.attnfuse_decode_workspace_size(ctypes.byref(d), splits_max + 1) > _abi.DECODE_NOALLOC_MAX_BYTES
+    assert lib.attnfuse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), splits_max + 1,
+                                       None) == _abi.ERR_WORKSPACE
+    assert lib.attnfuse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 0, None) == _abi.ERR_INVALID
+    assert lib.attnfuse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, None, 4, None) == _abi.ERR_INVALID
+    d.Hq = 7  # not a multiple of Hkv
+    assert lib.attnfuse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 4, None) == _abi.ERR_INVALID
+
+
+def test_decode_noalloc_limit_matches_header():
+    src = open(HEADER).read()
+    assert "#define ATTNFUSE_DECODE_NOALLOC_MAX_BYTES ((size_t)8 << 20)" in src
+    assert _abi.DECODE_NOALLOC_MAX_BYTES == 8 << 20
