@@ -118,12 +118,17 @@ int attnfuse_mb_hbm_read(const void* src, size_t bytes, int32_t workgroups, floa
 int attnfuse_mb_host_cost(int32_t which, const void* q, const void* k, const void* v, void* out,
                           const attnfuse_variant_desc* desc, int32_t num_splits, void* workspace,
                           size_t workspace_bytes, int32_t calls, double* ns_per_call, void* stream) {
-  if (which < 0 || which > 2 || calls < 1 || calls > (1 << 20) || !ns_per_call)
+  if (which < 0 || which > 3 || calls < 1 || calls > (1 << 20) || !ns_per_call)
     return ATTNFUSE_MB_ERR_INVALID;
   if (which != 2 && !desc) return ATTNFUSE_MB_ERR_INVALID;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   attnfuse::AttnParams p{};
   p.B = 1;
+  attnfuse_variant_desc dz{};
+  if (which == 3) {  // no queries: attnfuse_fwd validates everything, then returns
+    dz = *desc;
+    dz.Nq = 0;
+  }
   const auto t0 = std::chrono::steady_clock::now();
   int st = ATTNFUSE_OK;
   for (int i = 0; i < calls && st == ATTNFUSE_OK; ++i) {
@@ -131,6 +136,8 @@ int attnfuse_mb_host_cost(int32_t which, const void* q, const void* k, const voi
       st = attnfuse_fwd(q, k, v, out, desc, stream);
     } else if (which == 1) {
       st = attnfuse_decode(q, k, v, out, desc, num_splits, workspace, workspace_bytes, stream);
+    } else if (which == 3) {
+      st = attnfuse_fwd(q, k, v, out, &dz, stream);
     } else {
       hipLaunchKernelGGL(attnfuse::mb_empty_kernel, dim3(1), dim3(64), 0, s, p);
       st = hipGetLastError() == hipSuccess ? ATTNFUSE_OK : ATTNFUSE_ERR_HIP;

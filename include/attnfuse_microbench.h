@@ -56,7 +56,9 @@ int attnfuse_mb_hbm_read(const void* src, size_t bytes, int32_t workgroups, floa
  * which = 1: attnfuse_decode(q, k, v, out, desc, num_splits, workspace,
  * workspace_bytes, stream); which = 2: a launch of an empty kernel that takes
  * the same kernel-argument block as the attention kernels (HIP's own launch
- * cost; the tensor arguments are ignored).  The calls enqueue real work on
+ * cost; the tensor arguments are ignored); which = 3: attnfuse_fwd on a copy
+ * of *desc with Nq = 0, which runs the whole argument validation and returns
+ * before any launch (the library's own host cost).  The calls enqueue real work on
  * `stream`: keep `calls` small enough for the queue not to fill (a full queue
  * makes the host wait for the GPU).  Returns the first failing call's status
  * (the entry point's own codes) or ATTNFUSE_MB_OK; 1 <= calls <= 2^20. */

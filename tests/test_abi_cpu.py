@@ -248,6 +248,8 @@ def test_microbench_entry_points_reject_bad_arguments(lib):
     assert lib.attnfuse_mb_hbm_read(P(0x100008), 1024, 1, sink, stamps, None) == -1
     assert lib.attnfuse_mb_hbm_read(None, 1024, 1, sink, stamps, None) == -1
     ns = ctypes.c_double(0)
+    assert lib.attnfuse_mb_host_cost(4, None, None, None, None, None, 0, None, 0, 10, ctypes.byref(ns),
+                                     None) == -1
     assert lib.attnfuse_mb_host_cost(3, None, None, None, None, None, 0, None, 0, 10, ctypes.byref(ns),
                                      None) == -1
     assert lib.attnfuse_mb_host_cost(0, None, None, None, None, None, 0, None, 0, 10, ctypes.byref(ns),
