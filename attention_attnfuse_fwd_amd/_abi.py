@@ -89,6 +89,8 @@ class VariantDesc(ctypes.Structure):
         ("kv_fp8", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("q_fp8", ctypes.c_int32),
+        ("q_scale", ctypes.c_float),
     ]
 
     @classmethod

@@ -50,6 +50,8 @@ int validate_common(const attnfuse_variant_desc* d) {
   if (d->kv_fp8 && (!(d->k_scale > 0.f) || !isfinite(d->k_scale) || !(d->v_scale > 0.f) ||
                     !isfinite(d->v_scale)))
     return ATTNFUSE_ERR_INVALID;
+  if (d->q_fp8 != 0 && d->q_fp8 != 1) return ATTNFUSE_ERR_INVALID;
+  if (d->q_fp8 && (!(d->q_scale > 0.f) || !isfinite(d->q_scale))) return ATTNFUSE_ERR_INVALID;
   if (d->window < 0) return ATTNFUSE_ERR_INVALID;
   if (d->rope) {
     if (!(d->rope_theta > 0.0)) return ATTNFUSE_ERR_INVALID;
@@ -163,7 +165,17 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
-  if (d->kv_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
+  // fp8 inputs: Q, K and V together, with neither RoPE nor an additive bias.
+  const bool fp8 = d->kv_fp8 || d->q_fp8;
+  if (fp8) {
+    if (!d->kv_fp8 || !d->q_fp8 || d->dtype != ATTNFUSE_BF16 || d->rope || d->bias)
+      return ATTNFUSE_ERR_UNSUPPORTED;
+    const int64_t* in_strides[3] = {d->q_stride, d->k_stride, d->v_stride};
+    for (const int64_t* st : in_strides)
+      for (int a = 0; a < 3; ++a)
+        if (st[a] % 16) return ATTNFUSE_ERR_UNSUPPORTED;
+    if (d->tile_waves != 0 && d->tile_waves != 8) return ATTNFUSE_ERR_UNSUPPORTED;
+  }
   // Q / out may be NULL only when there are no queries, K / V only when there
   // are no keys (empty tensors).
   if ((d->Nq > 0 && (!q || !out)) || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
@@ -195,6 +207,36 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
     const long long grid = (long long)d->B * d->Hq * p.n_qblk;
     if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
     return hip_status(attnfuse::launch_fwd_fp32(p, d->D, (unsigned)grid, s));
+  }
+
+  if (fp8) {
+    // Eight waves (the fp8 schedule), as many q-heads of a group as fit.
+    int hp = largest_pow2_divisor(p.G, 8);
+    if (d->tile_heads != 0) {
+      const int h2 = d->tile_heads;
+      if (!(h2 == 1 || h2 == 2 || h2 == 4 || h2 == 8) || p.G % h2) return ATTNFUSE_ERR_UNSUPPORTED;
+      hp = h2;
+    }
+    if (use_sparse) {
+      if (d->bs_head_stride > 0) {
+        if (d->tile_heads > 1) return ATTNFUSE_ERR_UNSUPPORTED;
+        hp = 1;
+      }
+      if (d->bs_block_m % (32 * (8 / hp))) return ATTNFUSE_ERR_UNSUPPORTED;
+    }
+    p.hp = hp;
+    p.n_units = d->B * d->Hkv * (p.G / hp);
+    p.n_qblk = (d->Nq + 32 * (8 / hp) - 1) / (32 * (8 / hp));
+    const long long grid = (long long)p.n_units * p.n_qblk;
+    if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+    // Products of codes: both dequantisation scales join the score scale.
+    const double sc = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->D);
+    p.scale_log2 = (float)(sc * 1.4426950408889634 * (double)d->q_scale * (double)d->k_scale);
+    p.v_scale = d->v_scale;
+    const bool alibi = d->alibi_slopes != nullptr;
+    hipError_t e = d->D == 128 ? attnfuse::launch_fwd_fp8<128>(p, alibi, use_sparse, (unsigned)grid, s)
+                               : attnfuse::launch_fwd_fp8<64>(p, alibi, use_sparse, (unsigned)grid, s);
+    return hip_status(e);
   }
 
   // bf16 MFMA kernel: choose waves per workgroup (NW) and q-heads per
@@ -291,7 +333,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o
   if (!q || !k_cache || !v_cache || !out) return ATTNFUSE_ERR_INVALID;
   if (d->Nq != 1 || num_splits < 1 || num_splits > 4096) return ATTNFUSE_ERR_INVALID;
   if (!f16_table_ok(d)) return ATTNFUSE_ERR_INVALID;
-  if (d->dtype != ATTNFUSE_BF16 || d->bias || d->bs_row_ptr) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->dtype != ATTNFUSE_BF16 || d->bias || d->bs_row_ptr || d->q_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return ATTNFUSE_ERR_UNSUPPORTED;
   const size_t need = attnfuse_decode_workspace_size(d, num_splits);
   if (!workspace || workspace_bytes < need) return ATTNFUSE_ERR_WORKSPACE;
@@ -411,7 +453,7 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
-  if (d->dtype != ATTNFUSE_BF16 || d->kv_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->dtype != ATTNFUSE_BF16 || d->kv_fp8 || d->q_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->bs_row_ptr && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->Nq > 0 && (!q || !out || !dout || !lse || !dq)) return ATTNFUSE_ERR_INVALID;
   if (d->Nk > 0 && (!k || !v || !dk || !dv)) return ATTNFUSE_ERR_INVALID;
@@ -479,7 +521,7 @@ int attnfuse_prerotate(const void* x, void* x_rot, const attnfuse_variant_desc* 
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
   if (!x || !x_rot || !d->rope || (which != 0 && which != 1)) return ATTNFUSE_ERR_INVALID;
-  if (d->kv_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (d->kv_fp8 || d->q_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
   if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
   const int H = which == 0 ? d->Hq : d->Hkv;
   const int N = which == 0 ? d->Nq : d->Nk;

@@ -113,6 +113,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Eight FP8 E4M3 codes (bytes of x, in order) -> eight bf16 values, exact
+// (every E4M3 value is a bf16 value; gfx950 conversion with a unit scale).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 x) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// S += A B on the fp8 matrix core (v_mfma_f32_32x32x64_f8f6f4, both operands
+// OCP E4M3, unit block scales, fp32 accumulate).  Lane l holds row (A) /
+// column (B) l % 32 and 32 of the 64 k values; the k values of lane-half g
+// of A meet those of lane-half g of B, so any split of k into the two
+// halves' 32 bytes gives the product as long as both operands use it.
+__device__ __forceinline__ f32x16 mfma32_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 

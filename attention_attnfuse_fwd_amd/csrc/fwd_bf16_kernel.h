@@ -114,19 +114,52 @@ __device__ __forceinline__ float tree_max32(const f32x16& a, const f32x16& b) {
 // r, by a lane in half lh: 32*st + 8*(r/4) + 4*lh + r%4.  kOff omits 4*lh.
 __device__ __forceinline__ constexpr int kOff(int st, int r) { return 32 * st + 8 * (r / 4) + (r % 4); }
 
+// LDS layout of the FP8 instances (bytes): Q and K stay OCP E4M3 codes and
+// meet on the fp8 matrix core, so a K slot holds the tile's codes [64 rows][D]
+// (16-byte chunks XOR-swizzled by row, k8swz); V is converted once per
+// workgroup to bf16 into the same V slots as the bf16 instances, from a
+// two-deep staging ring where each thread finds the 16 codes it loaded itself.
+template <int D>
+struct Fp8Lds {
+  static constexpr int KSLOT = 64 * D;
+  static constexpr int V_OFF = 4 * KSLOT;
+  static constexpr int VSLOT = 128 * D;
+  static constexpr int S_OFF = V_OFF + 4 * VSLOT;
+  static constexpr int SSLOT = 64 * D;
+  static constexpr int BYTES = S_OFF + 2 * SSLOT;
+  static constexpr int NI = D / 16;          // DMA instructions per K (or V) tile
+  static constexpr int ROWS_I = 1024 / D;    // rows per DMA instruction
+  static constexpr int CPR = D / 16;         // 16-byte chunks per row
+};
+// Swizzle of fp8 K row j: the 16 rows a 16-lane group reads at one chunk
+// column land on distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ constexpr int k8swz(int j) {
+  return D == 128 ? (j >> 1) & 7 : (j >> 2) & 3;
+}
+
 // BIAS: an additive bias may be present (else only ALiBi slopes, with
 // SCOREMOD); the instances without it keep the registers of the bias tile.
-template <int D, int NW, bool ROPE, bool SCOREMOD, bool SPARSE, bool BIAS>
+// FP8: Q, K, V are OCP E4M3 codes with per-tensor scales (folded into
+// p.scale_log2 and p.v_scale); S = K Q^T runs on the fp8 matrix core, P V on
+// bf16 (eight waves, no RoPE, no bias).
+template <int D, int NW, bool ROPE, bool SCOREMOD, bool SPARSE, bool BIAS, bool FP8 = false>
 __global__ void __launch_bounds__(NW * 64)
 fwd_bf16_kernel(const AttnParams p) {
   using L = TileLds<D>;
+  using L8 = Fp8Lds<D>;
+  static_assert(!FP8 || (NW == 8 && !ROPE && !BIAS), "fp8 instances: eight waves, no RoPE, no bias");
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
+  constexpr int NK8 = D / 64;  // fp8 MFMA k-steps over the head dim
   constexpr int NDT = D / 32;  // 32-row tiles of O^T
   constexpr int RING = L::RING;
   constexpr int LDS_RING = L::T_OFF + (ROPE ? L::TSLOT : 0);
   // The ping-pong prologue stages each wave's Q rows (32 rows of 2*D bytes)
   // in K slot 3, V slots 2 and 3 and one more area of the same size.
-  constexpr int LDS_BYTES = LDS_RING + (NW == 8 ? 128 * D : 0);
+  constexpr int LDS_BF16 = LDS_RING + (NW == 8 ? 128 * D : 0);
+  // The epilogue stages 32 rows of 2 * D + 16 bytes per wave.
+  constexpr int LDS_EPI = NW * 32 * (2 * D + 16);
+  constexpr int LDS_BYTES = FP8 ? (L8::BYTES > LDS_EPI ? L8::BYTES : LDS_EPI) : LDS_BF16;
   // DMA instructions per wave and tile.  V is spread evenly; K pairs may not
   // be (D = 64 with 8 waves: waves 0..3 take one pair each).
   static_assert(L::NVI % NW == 0, "V instructions must spread evenly over the waves");
@@ -615,6 +648,12 @@ fwd_bf16_kernel(const AttnParams p) {
   // score mods, the lane's offset, the register's ALiBi step and the bias.
   auto arg = [&](const f32x16 (&s)[2], int st, int r, int k0) -> float {
     float x = s[st][r];
+    if constexpr (FP8) {
+      // The fp8 products are unscaled code dot products: one FMA applies the
+      // folded scales (and joins the ALiBi step and minus the running maximum).
+      const float base = SCOREMOD ? __builtin_fmaf(slope2, (float)kOff(st, r), mod_base(k0)) : neg_m();
+      return __builtin_fmaf(p.scale_log2, x, base);
+    }
     if (SCOREMOD) {
       if (CSPLAT) x = __builtin_fmaf(slope2, (float)kOff(st, r), x);
       else x += __builtin_fmaf(slope2, (float)kOff(st, r), mod_base(k0));
@@ -715,7 +754,173 @@ fwd_bf16_kernel(const AttnParams p) {
     finish_tile(s0, -neg_m(), pw);
     to_frags(pw, pfa);
   };
-  if constexpr (PP) {
+  if constexpr (FP8) {
+    // ---- fp8 ping-pong schedule ----
+    // The two-waves-per-SIMD alternation of the bf16 schedule below, with
+    // S(t+1) = K(t+1) Q^T on the fp8 matrix core (Q codes in registers, K
+    // codes in LDS) and P V on bf16.  Vector cluster of step t: DMA of K(t+3)
+    // and of V(t+2) into the staging ring, conversion of the thread's own codes
+    // of V(t+1) (landed by the wait that opens the cluster) into bf16 V slot
+    // (t+1) % 4, softmax of S(t+1).  The waves with a DMA role issue one K and
+    // one V instruction per tile (D = 128: all eight; D = 64: waves 0-3).
+    const bool m_first = wave < NW / 2;
+    const bool dma_wave = wave < L8::NI;
+    const uint8_t* const kb8 = reinterpret_cast<const uint8_t*>(p.k) + b * p.ksb + kvh * p.ksh;
+    const uint8_t* const vb8 = reinterpret_cast<const uint8_t*>(p.v) + b * p.vsb + kvh * p.vsh;
+    // Instruction `wave` of a tile covers rows ROWS_I * wave ..; lane: row
+    // row8, 16-byte chunk position pos8 (K: global chunk pos8 ^ k8swz(row8)).
+    const int row8 = L8::ROWS_I * wave + lane / L8::CPR;
+    const int pos8 = lane % L8::CPR;
+    const uint32_t kcol8 = 16u * (uint32_t)(pos8 ^ k8swz<D>(row8));
+    const uint32_t vcol8 = 16u * (uint32_t)pos8;
+    const uint32_t ksnb = (uint32_t)ksn, vsnb = (uint32_t)vsn;  // row strides in bytes (< 2^24)
+    auto dma_k8 = [&](int u) {
+      int k0, rmax;
+      const int kc0 = tile_base(u, k0, rmax);
+      const uint32_t off = (uint32_t)min(row8, min(rmax, 63)) * ksnb + kcol8;
+      dma16_off(lds0 + (uint32_t)(u % RING) * L8::KSLOT + 1024u * (uint32_t)wave, kb8 + (long long)kc0 * ksn,
+                off);
+    };
+    auto dma_v8 = [&](int u) {
+      int k0, rmax;
+      const int kc0 = tile_base(u, k0, rmax);
+      const uint32_t off = (uint32_t)min(row8, min(rmax, 63)) * vsnb + vcol8;
+      dma16_off(lds0 + L8::S_OFF + (uint32_t)(u % 2) * L8::SSLOT + 1024u * (uint32_t)wave,
+                vb8 + (long long)kc0 * vsn, off);
+    };
+    // This thread's 16 codes of V tile u (row row8, columns 16 * pos8 ..) ->
+    // two bf16 chunks of V slot u % 4 at their swizzled places.
+    auto convert_v8 = [&](int u) {
+      const uint4 c = ld16(smem + L8::S_OFF + (u % 2) * L8::SSLOT + 1024 * wave + 16 * lane);
+      char* const dst = smem + L8::V_OFF + (u % RING) * L8::VSLOT + row8 * 2 * D;
+      st16(dst + 16 * ((2 * pos8) ^ vswz<D>(row8)), e4m3x8_to_bf16x8(make_uint2(c.x, c.y)));
+      st16(dst + 16 * ((2 * pos8 + 1) ^ vswz<D>(row8)), e4m3x8_to_bf16x8(make_uint2(c.z, c.w)));
+    };
+    // Q codes as B operands: lane (lq, lh) holds bytes 64 kk + 32 lh .. + 31
+    // of its query row (K fragments split k the same way).
+    i32x8 qf8[NK8];
+    auto load_q8 = [&]() {
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + b * p.qsb + h * p.qsh + (long long)iq * p.qsn;
+#pragma unroll
+      for (int kk = 0; kk < NK8; ++kk) {
+        const uint4 a = ld16(qrow + 64 * kk + 32 * lh), c = ld16(qrow + 64 * kk + 32 * lh + 16);
+        qf8[kk] = i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+      }
+    };
+    // K fragment (A operand): row 32 st + lq, bytes 64 kk + 32 lh .. + 31.
+    const int k8s = k8swz<D>(lq);  // = k8swz(32 st + lq) for both subtiles
+    auto kf8 = [&](uint32_t ks, int st, int kk) -> i32x8 {
+      const uint32_t rowb = ks + (uint32_t)(32 * st + lq) * D;
+      const uint4 a = __builtin_bit_cast(uint4, lds_read16(rowb + 16 * ((4 * kk + 2 * lh) ^ k8s)));
+      const uint4 c = __builtin_bit_cast(uint4, lds_read16(rowb + 16 * ((4 * kk + 2 * lh + 1) ^ k8s)));
+      return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+    };
+    constexpr int NS8 = 2 * NK8;     // fp8 S MFMAs per tile: (subtile, k step)
+    constexpr int NPV = 4 * NDT;     // P V MFMAs per tile
+    constexpr int EVERY = NPV / NS8;
+    static_assert(NPV % NS8 == 0, "S MFMAs spread evenly over the P V steps");
+    if (n > 0) {
+      if (dma_wave) {
+        dma_k8(0);
+        dma_v8(0);
+        if (n > 1) {
+          dma_k8(1);
+          dma_v8(1);
+        }
+        if (n > 2) dma_k8(2);
+      }
+    }
+    load_q8();
+    if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
+    vmcnt_wait<0>();
+    if (n > 0 && dma_wave) {
+      convert_v8(0);
+      if (n > 1) convert_v8(1);
+    }
+    __syncthreads();
+    if (n > 0) {
+      const int k00 = tile_k0(0);
+      f32x16 s0[2];
+#pragma unroll
+      for (int j = 0; j < NS8; ++j)
+        s0[j & 1] = mfma32_f8(kf8(lds0, j & 1, j >> 1), qf8[j >> 1], j < 2 ? f32x16{} : s0[j & 1]);
+      mask_scores(0, s0);
+      uint32_t pw[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00);
+      finish_tile(s0, -neg_m(), pw);
+      to_frags(pw, pfa);
+    }
+    constexpr int PF = 2;
+    f32x16 sn[2];
+    auto mcluster8 = [&](int t, const bf16x8 (&pf)[4]) {
+      __builtin_amdgcn_s_setprio(1);
+      const uint32_t ks = lds0 + (uint32_t)((t + 1) % RING) * L8::KSLOT;
+      const uint32_t vs = lds0 + L8::V_OFF + (uint32_t)(t % RING) * L8::VSLOT;
+      uint32_t vbase[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vbase[dt] = vs + voff[dt];
+      auto vf = [&](int c, int dt) -> bf16x8 {
+        const i16x4 r0 = lds_read_tr4(vbase[dt] + c * 32 * D);
+        const i16x4 r1 = lds_read_tr4(vbase[dt] + c * 32 * D + 16 * D);
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 a = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+        return __builtin_bit_cast(bf16x8, a);
+      };
+      bf16x8 vfr[PF + 1];
+#pragma unroll
+      for (int k = 0; k < PF; ++k) vfr[k] = vf(k / NDT, k % NDT);
+      i32x8 a8 = kf8(ks, 0, 0);
+#pragma unroll
+      for (int k = 0; k < NPV; ++k) {
+        if (k + PF < NPV) vfr[(k + PF) % (PF + 1)] = vf((k + PF) / NDT, (k + PF) % NDT);
+        if (k % EVERY == 0) {
+          const int j = k / EVERY;
+          sn[j & 1] = mfma32_f8(a8, qf8[j >> 1], j < 2 ? f32x16{} : sn[j & 1]);
+          if (j + 1 < NS8) a8 = kf8(ks, (j + 1) & 1, (j + 1) >> 1);
+        }
+        o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
+        if (k % NDT == NDT - 1) ol = mfma32(ones8, pf[k / NDT], ol);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    auto vcluster8 = [&](int t, int st, bool has_s, bf16x8 (&pf_next)[4]) {
+      vmcnt_wait<0>();
+      if (dma_wave) {
+        if (t + 3 < n) dma_k8(t + 3);
+        if (t + 2 < n) dma_v8(t + 2);
+        if (t >= 1 && t + 1 < n) convert_v8(t + 1);
+      }
+      if (has_s) {
+        const int k0s = tile_k0(min(st, n - 1));
+        mask_scores(st, sn);
+        uint32_t pw[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) pw[x] = exp_pair(sn, x, k0s);
+        finish_tile(sn, -neg_m(), pw);
+        to_frags(pw, pf_next);
+      }
+    };
+    const int dstep = m_first ? 0 : 1;
+    if (n > 0 && !m_first) {
+      vcluster8(0, 0, false, pfb);
+      __syncthreads();
+    }
+    auto step8 = [&](int t, const bf16x8 (&pf_cur)[4], bf16x8 (&pf_nxt)[4]) {
+      mcluster8(t, pf_cur);
+      __syncthreads();
+      vcluster8(t + dstep, t + 1, true, pf_nxt);
+      __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < n; t += 2) {
+      step8(t, pfa, pfb);
+      step8(t + 1, pfb, pfa);
+    }
+    if (t < n) step8(t, pfa, pfb);
+    if (n > 0 && m_first) __syncthreads();
+  } else if constexpr (PP) {
     // ---- ping-pong schedule (two waves per SIMD) ----
     // Waves w and w + NW/2 share a SIMD.  Each wave alternates an MFMA
     // cluster M(t) (S(t+1) = K'(t+1) Q'^T and O^T += V(t)^T P(t)^T, 32 MFMAs,
@@ -1081,7 +1286,7 @@ fwd_bf16_kernel(const AttnParams p) {
   // as whole 16-byte chunks of consecutive rows, so each store instruction
   // writes a few complete rows.
   const float l_tot = ol[0];
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? p.v_scale / l_tot : 0.f;  // v_scale: fp8 V dequantisation (else 1)
   constexpr int OROW = 2 * D + 16;  // bytes per staged row
   char* const ost = smem + wave * 32 * OROW;
 #pragma unroll

@@ -13,6 +13,11 @@ template <int D, int NW>
 hipError_t launch_fwd_bf16(const AttnParams& p, bool rope, bool scoremod, bool sparse,
                            unsigned grid, hipStream_t stream);
 
+// fp8 prefill (Q, K, V OCP E4M3 codes, bf16 out; eight waves, no RoPE / bias).
+template <int D>
+hipError_t launch_fwd_fp8(const AttnParams& p, bool scoremod, bool sparse, unsigned grid,
+                          hipStream_t stream);
+
 // fp32 prefill kernel (64 query rows per workgroup).
 hipError_t launch_fwd_fp32(const AttnParams& p, int D, unsigned grid, hipStream_t stream);
 

@@ -15,18 +15,6 @@
 
 namespace attnfuse {
 
-// Eight FP8 E4M3 codes (bytes of x, in order) -> eight bf16 values, exact
-// (gfx950 conversion with a unit scale).
-__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 x) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
-  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
-  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
-}
-
 // K part: unit = (key j, 8-wide chunk c of the low half) covering d in
 // [8c, 8c + 8) and its RoPE partner [D/2 + 8c, D/2 + 8c + 8).  Consecutive
 // units walk the chunks of one row (coalesced 16-byte loads); the row order

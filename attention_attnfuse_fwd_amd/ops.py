@@ -59,12 +59,15 @@ _FWD_DESCS: dict = {}
 _DECODE_DESCS: dict = {}
 
 
+_E4M3 = getattr(torch, "float8_e4m3fn", None)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
-        return _abi.BF16
+    if t.dtype == torch.bfloat16 or (_E4M3 is not None and t.dtype == _E4M3):
+        return _abi.BF16  # fp8 inputs produce a bf16 output
     if t.dtype == torch.float32:
         return _abi.FP32
-    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16, float32 or float8_e4m3fn")
 
 
 # ----------------------------------------------------------------------------
@@ -273,19 +276,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         alibi_slopes=None, bias=None, block_mask: Optional[BlockMask] = None,
         scale: Optional[float] = None, return_lse: bool = False,
         out: Optional[torch.Tensor] = None, decode_fast_path: bool = True,
-        tile: Optional[tuple] = None):
+        tile: Optional[tuple] = None, q_scale: float = 1.0, k_scale: float = 1.0,
+        v_scale: float = 1.0):
     """Fused attention forward; q [B, Hq, Nq, D], k / v [B, Hkv, Nk, D] on the GPU.
 
     A single query row (Nq == 1, bf16, no bias or block mask) takes the split-KV
     decode path, as the pages' runtime dispatch does.  ``tile = (waves, heads)``
-    overrides the library's tile table for the bf16 prefill kernel.
+    overrides the library's tile table for the bf16 prefill kernel.  With
+    ``torch.float8_e4m3fn`` q, k and v (E4M3 codes whose rows are
+    ``q_scale * code`` etc.) the fp8 prefill runs and the output is bf16.
     """
     cacheable = (out is not None and not return_lse and alibi_slopes is None and bias is None
                  and block_mask is None and tile is None)
     if cacheable:
         key = (q.shape, q.stride(), k.shape, k.stride(), v.shape, v.stride(), out.shape, out.stride(),
                q.dtype, k.dtype, v.dtype, out.dtype, q.device, k.device, v.device, out.device,
-               causal, window, rope_theta, q_pos0, k_pos0, scale, decode_fast_path)
+               causal, window, rope_theta, q_pos0, k_pos0, scale, decode_fast_path, q_scale, k_scale,
+               v_scale)
         hit = _FWD_DESCS.get(key)
         if hit is not None:
             dref, entry = hit
@@ -300,14 +307,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         return decode(q, k, v, causal=causal, window=window, rope_theta=rope_theta,
                       q_pos0=q_pos0, k_pos0=k_pos0, alibi_slopes=alibi_slopes, scale=scale,
                       return_lse=return_lse, out=out)
+    fp8 = _E4M3 is not None and q.dtype == _E4M3
     if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if fp8 else q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     keep = []
     d = _make_desc(q, k, v, out, scale=scale, causal=causal, window=window,
                    rope_theta=rope_theta, q_pos0=q_pos0, k_pos0=k_pos0,
                    alibi_slopes=alibi_slopes, bias=bias, block_mask=block_mask, lse=lse,
                    keep=keep)
+    if fp8:
+        d.kv_fp8, d.q_fp8 = 1, 1
+        d.q_scale, d.k_scale, d.v_scale = float(q_scale), float(k_scale), float(v_scale)
     if tile is not None:
         d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
     _check(_abi.load().attnfuse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(d),

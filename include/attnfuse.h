@@ -167,11 +167,31 @@ typedef struct attnfuse_variant_desc {
    * infinities) and the cached rows are k_scale * code and v_scale * code
    * (per-tensor dequantisation scales, finite and > 0); K/V strides then
    * count bytes and keep the 8-element alignment of the bf16 layout.  q and
-   * out stay bf16.  0 = K/V have the dtype above.  Any other entry point
-   * returns ATTNFUSE_ERR_UNSUPPORTED when kv_fp8 is set. */
+   * out stay bf16.  0 = K/V have the dtype above.  attnfuse_fwd takes
+   * kv_fp8 = 1 only together with q_fp8 = 1 (below); the other entry points
+   * return ATTNFUSE_ERR_UNSUPPORTED when kv_fp8 is set. */
   int32_t kv_fp8;
   float k_scale;
   float v_scale;
+
+  /* fp8 prefill inputs (attnfuse_fwd; "9.1 Limitations and Future
+   * Directions" names fp8 as future work): q_fp8 = 1 together with kv_fp8 = 1
+   * means q, k and v all hold OCP FP8 E4M3 codes, the rows being
+   * q_scale * code, k_scale * code and v_scale * code (per-tensor
+   * dequantisation scales, finite and > 0).  Q and K then meet on the fp8
+   * matrix core (products of codes, fp32 accumulate; the scales multiply the
+   * fp32 score) and P V runs in bf16 on V codes converted exactly, so the
+   * result matches attention on the dequantised values to the bf16 bar.
+   * Strides count bytes and must be multiples of 16, base pointers 16-byte
+   * aligned; out stays bf16 (dtype ATTNFUSE_BF16).  Supports causal, window,
+   * alibi and block_sparse (bs_block_m a multiple of the workgroup's 32 * 8 /
+   * tile_heads rows); rope and additive_bias return ATTNFUSE_ERR_UNSUPPORTED
+   * (rotated or biased values are not fp8 codes; rotate before quantising),
+   * and so do tile_waves other than 0 or 8.  q_fp8 = 1 without kv_fp8 = 1,
+   * or on any other entry point, returns ATTNFUSE_ERR_UNSUPPORTED.
+   * 0 = q has desc->dtype. */
+  int32_t q_fp8;
+  float q_scale;
 } attnfuse_variant_desc;
 
 /* Fused attention forward: out = attention(q, k, v) under `desc`.

@@ -280,3 +280,41 @@ def test_decode_noalloc_limit_matches_header():
     src = open(HEADER).read()
     assert "#define ATTNFUSE_DECODE_NOALLOC_MAX_BYTES ((size_t)8 << 20)" in src
     assert _abi.DECODE_NOALLOC_MAX_BYTES == 8 << 20
+
+
+def _fp8_desc(**kw):
+    """A valid all-fp8 prefill descriptor (byte strides, multiples of 16)."""
+    base = dict(kv_fp8=1, q_fp8=1, q_scale=0.5, k_scale=0.25, v_scale=2.0)
+    base.update(kw)
+    return _good_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_fp8=0), _abi.ERR_UNSUPPORTED),                   # fp8 K / V with a bf16 Q
+    (dict(kv_fp8=0, k_scale=0.0, v_scale=0.0), _abi.ERR_UNSUPPORTED),  # fp8 Q alone
+    (dict(q_fp8=3), _abi.ERR_INVALID),
+    (dict(q_scale=0.0), _abi.ERR_INVALID),
+    (dict(q_scale=float("nan")), _abi.ERR_INVALID),
+    (dict(dtype=_abi.FP32), _abi.ERR_UNSUPPORTED),
+    (dict(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_table_len=100), _abi.ERR_UNSUPPORTED),
+    (dict(bias=0x1000), _abi.ERR_UNSUPPORTED),
+    (dict(tile_waves=4), _abi.ERR_UNSUPPORTED),
+    (dict(tile_heads=4), _abi.ERR_UNSUPPORTED),              # does not divide G = 2
+    (dict(Nq=0), _abi.OK),                                   # nothing to do, validated
+])
+def test_fp8_prefill_descriptor_rules(lib, kw, status):
+    assert _fwd(lib, _fp8_desc(**kw)) == status
+
+
+def test_fp8_prefill_byte_strides_must_be_16_aligned(lib):
+    d = _fp8_desc(Nq=0)
+    d.k_stride[2] = 136  # bytes: a multiple of 8 (bf16 rule) but not of 16
+    assert _fwd(lib, d) == _abi.ERR_UNSUPPORTED
+
+
+def test_fp8_query_is_rejected_by_the_other_entry_points(lib):
+    d = _fp8_desc(Nq=1)
+    assert lib.attnfuse_decode(FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), 4, FAKE, 1 << 20,
+                               None) == _abi.ERR_UNSUPPORTED
+    assert lib.attnfuse_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), FAKE,
+                            1 << 20, None) == _abi.ERR_UNSUPPORTED

@@ -269,6 +269,16 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
     return inp
 
 
+def normal_e4m3(shape, rng: np.random.Generator):
+    """N(0,1) float32 draws quantised to OCP E4M3 with a per-tensor scale
+    (largest magnitude -> 448): (codes uint8, dequantised float64 values
+    code * scale, scale)."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    scale = float(np.abs(x).max()) / 448.0
+    codes = round_to_e4m3(x / scale)
+    return codes, e4m3_to_f64(codes) * scale, scale
+
+
 def normal_bf16(shape, rng: np.random.Generator, scale: float = 1.0):
     """(bits uint16, float64 values) of scaled N(0,1) draws rounded to bf16."""
     x = (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)).astype(np.float32)
