@@ -107,6 +107,7 @@ AttnParams base_params(const void* q, const void* k, const void* v, void* out,
   p.rsin = d->rope ? d->rope_sin : nullptr;
   p.rcs = d->rope ? d->rope_cs_f16 : nullptr;
   p.rope_len = d->rope ? (int)(d->rope_table_len < kMaxLen ? d->rope_table_len : kMaxLen) : 0;
+  p.rope_log2_theta = d->rope ? (float)log2(d->rope_theta) : 0.f;
   p.q_pos0 = (int)d->q_pos0;
   p.k_pos0 = (int)d->k_pos0;
   // Band in position space: lo <= p_k - p_q <= hi; then shifted to index space.

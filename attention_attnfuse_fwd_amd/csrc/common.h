@@ -45,6 +45,7 @@ struct AttnParams {
   const float* rsin;
   const uint32_t* rcs;        // fp16 (cos, sin) pairs [len][D/2] (decode) or nullptr
   int rope_len;               // rows in the RoPE tables
+  float rope_log2_theta;      // log2 of the RoPE base (decode's small angles)
   int q_pos0, k_pos0;
   // Allowed iff band_lo <= j - i <= band_hi (row/column index space; the
   // position offset k_pos0 - q_pos0 is already folded in).  has_band = 0
@@ -247,6 +248,46 @@ __device__ __forceinline__ void rope_rotate_bf16x8_h(uint4& lo, uint4& hi, const
     const float c0 = (float)a[0] * k, s0 = (float)a[1] * k, c1 = (float)b[0] * k, s1 = (float)b[1] * k;
     ol[w] = pack_bf16x2(l0 * c0 - h0 * s0, l1 * c1 - h1 * s1);
     oh[w] = pack_bf16x2(h0 * c0 + l0 * s0, h1 * c1 + l1 * s1);
+  }
+  lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+  hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+}
+
+// NeoX rotation of one (low, high) pair of 8-element bf16 chunks by the
+// angles a_e + j * w_e, e = 0..7: fp16 (cos, sin) words of a_e (b0, b1),
+// w_e / (2 pi) = wrev0 * ratio^e, and j small (|j * w_e| / (2 pi) a few
+// revolutions: the hardware sine and cosine take revolutions).  cos(a + b) =
+// cos a cos b - sin a sin b, sin(a + b) = sin a cos b + cos a sin b, all in
+// fp32, then the rotation and one bf16 rounding.
+__device__ __forceinline__ void rope_rotate_bf16x8_step(uint4& lo, uint4& hi, const uint4& b0,
+                                                        const uint4& b1, float wrev0, float ratio,
+                                                        float j) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  const uint32_t* wl = reinterpret_cast<const uint32_t*>(&lo);
+  const uint32_t* wh = reinterpret_cast<const uint32_t*>(&hi);
+  uint32_t ol[4], oh[4];
+  float x = j * wrev0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float c[2], s[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * w + q;
+      const h2_t a = __builtin_bit_cast(h2_t, bw[e]);
+      const float ca = (float)a[0], sa = (float)a[1];
+      if (e > 0) x *= ratio;
+      // Loop-invariant across steps: keep the compiler from hoisting (and
+      // holding) every step's sines and cosines in registers.
+      asm volatile("" : "+v"(x));
+      const float cbv = __builtin_amdgcn_cosf(x), sbv = __builtin_amdgcn_sinf(x);
+      c[q] = __builtin_fmaf(ca, cbv, -sa * sbv);
+      s[q] = __builtin_fmaf(sa, cbv, ca * sbv);
+    }
+    const float l0 = bf16lo(wl[w]), l1 = bf16hi(wl[w]);
+    const float h0 = bf16lo(wh[w]), h1 = bf16hi(wh[w]);
+    ol[w] = pack_bf16x2(__builtin_fmaf(l0, c[0], -h0 * s[0]), __builtin_fmaf(l1, c[1], -h1 * s[1]));
+    oh[w] = pack_bf16x2(__builtin_fmaf(h0, c[0], l0 * s[0]), __builtin_fmaf(h1, c[1], l1 * s[1]));
   }
   lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
   hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);

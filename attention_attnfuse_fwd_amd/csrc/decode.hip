@@ -77,6 +77,7 @@ __global__ void __launch_bounds__(kDecNT, 2) decode_split_kernel(const AttnParam
   // Start streaming before touching the query.
   KS kst;
   VS vst;
+  kst.init(p, lane);
   int st = wave;  // this wave's current step
   if (st < n_steps) {
     kst.load(p, kb, step_k0(st), c1, lane);

@@ -36,14 +36,33 @@ struct KStage {
     return (jr & ~15) | ((jl % RPG) * CPR + jl / RPG);
   }
 
+  static_assert(NT % CPR == 0, "a lane keeps one chunk column for all its units");
+
   uint4 lo[KV8 ? 1 : U], hi[KV8 ? 1 : U];      // bf16 rows
   uint2 lo8[KV8 ? U : 1], hi8[KV8 ? U : 1];    // fp8 rows
-  uint4 cs[U][2];  // fp16 (cos, sin) pairs for the unit's 8 angles
-  int pos[U];
+  // Angles by addition: the key at position base + j (base = the step's
+  // first key, 0 <= j < BN) is rotated by base * w + j * w, so only the
+  // step's base row of the table is read (fp16 (cos, sin) pairs of the
+  // lane's 8 angles); the small angles j * w come from the hardware sine and
+  // cosine (|j * w| / 2 pi < BN / 2 pi revolutions) with w computed once.
+  uint4 cb[2];     // table row `base`
+  float wrev0;     // w / (2 pi) of the lane's first frequency, r = 8 * (tid % CPR)
+  float ratio;     // w_{r+1} / w_r = theta^(-2/D) (the same for every lane)
+  int base;
+
+  // The lane's frequencies w_r = theta^(-2r/D), r = 8 * (tid % CPR) + e,
+  // as wrev0 * ratio^e.
+  __device__ __forceinline__ void init(const AttnParams& p, int tid) {
+    if (!ROPE) return;
+    const int c = tid % CPR;
+    wrev0 = exp2f(-2.0f * (float)(8 * c) / (float)D * p.rope_log2_theta) * 0.15915494309189535f;
+    ratio = exp2f(-2.0f / (float)D * p.rope_log2_theta);
+  }
 
   // Raw K rows k0 .. k0+BN-1 (rows at or past key_end are clamped to key_end - 1).
   __device__ __forceinline__ void load(const AttnParams& p, const T* kb, int k0, int key_end,
                                        int tid) {
+    base = p.k_pos0 + k0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int unit = tid + u * NT;
@@ -58,23 +77,16 @@ struct KStage {
           lo[u] = ld16(src);
           hi[u] = ld16(src + D / 2);
         }
-        pos[u] = p.k_pos0 + kj;
       }
     }
   }
-  // (cos, sin) table entries for the positions load() recorded.
+  // (cos, sin) table entries of the step's base row (rows clamped at the end
+  // of the keys are masked out, so they take angle base + j as well).
   __device__ __forceinline__ void load_tables(const AttnParams& p, int tid) {
     if (!ROPE) return;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int unit = tid + u * NT;
-      if (UNITS % NT == 0 || unit < UNITS) {
-        const int c = unit % CPR;
-        const uint32_t* row = p.rcs + (long long)pos[u] * (D / 2) + 8 * c;
-        cs[u][0] = ld16(row);
-        cs[u][1] = ld16(row + 4);
-      }
-    }
+    const uint32_t* brow = p.rcs + (long long)base * (D / 2) + 8 * (tid % CPR);
+    cb[0] = ld16(brow);
+    cb[1] = ld16(brow + 4);
   }
   __device__ __forceinline__ void store(__bf16* ks, int tid) {
 #pragma unroll
@@ -90,7 +102,7 @@ struct KStage {
           l = lo[u];
           h = hi[u];
         }
-        if (ROPE) rope_rotate_bf16x8_h(l, h, cs[u][0], cs[u][1]);
+        if (ROPE) rope_rotate_bf16x8_step(l, h, cb[0], cb[1], wrev0, ratio, (float)j);
         st16(ks + j * KSTR + 8 * c, l);
         st16(ks + j * KSTR + D / 2 + 8 * c, h);
       }
