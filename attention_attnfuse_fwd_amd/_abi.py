@@ -27,6 +27,7 @@ NORM_RELU = 1
 # Every function the headers declare (checked against include/*.h by the tests).
 EXPORTS = (
     "attnfuse_fwd",
+    "attnfuse_fwd_plan",
     "attnfuse_decode_workspace_size",
     "attnfuse_decode",
     "attnfuse_decode_noalloc",
@@ -40,6 +41,22 @@ EXPORTS = (
     "attnfuse_mb_hbm_read",
     "attnfuse_mb_host_cost",
 )
+
+
+PLAN_KERNELS = {0: "none", 1: "fp32", 2: "bf16", 3: "fp8"}
+
+
+class FwdPlanInfo(ctypes.Structure):
+    """Mirror of ``attnfuse_fwd_plan_info``."""
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("waves", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("query_blocks", ctypes.c_int32),
+        ("paired", ctypes.c_int32),
+        ("workgroups", ctypes.c_int64),
+    ]
 
 
 class LibraryNotBuilt(ImportError):
@@ -117,6 +134,8 @@ def load() -> ctypes.CDLL:
     D = ctypes.POINTER(VariantDesc)
     lib.attnfuse_fwd.argtypes = [P, P, P, P, D, P]
     lib.attnfuse_fwd.restype = ctypes.c_int
+    lib.attnfuse_fwd_plan.argtypes = [D, ctypes.POINTER(FwdPlanInfo)]
+    lib.attnfuse_fwd_plan.restype = ctypes.c_int
     lib.attnfuse_decode_workspace_size.argtypes = [D, ctypes.c_int32]
     lib.attnfuse_decode_workspace_size.restype = ctypes.c_size_t
     lib.attnfuse_decode.argtypes = [P, P, P, P, D, ctypes.c_int32, P, ctypes.c_size_t, P]

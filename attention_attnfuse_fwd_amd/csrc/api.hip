@@ -146,23 +146,19 @@ int largest_pow2_divisor(int g, int cap) {
   return hp;
 }
 
-}  // namespace
+// Launch choice of attnfuse_fwd.
+struct FwdPlan {
+  int kind = ATTNFUSE_PLAN_NONE;
+  int NW = 0, hp = 0, rows = 0;  // waves and q-heads per workgroup, query rows per block
+  long long grid = 0;
+};
 
-extern "C" {
-
-const char* attnfuse_status_string(int status) {
-  switch (status) {
-    case ATTNFUSE_OK: return "ok";
-    case ATTNFUSE_ERR_INVALID: return "invalid argument or descriptor";
-    case ATTNFUSE_ERR_UNSUPPORTED: return "unsupported variant or shape";
-    case ATTNFUSE_ERR_WORKSPACE: return "workspace missing or too small";
-    case ATTNFUSE_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
-                 const attnfuse_variant_desc* desc, void* stream) {
+// Validation and launch choice of attnfuse_fwd (kernel, tile, grid), shared
+// with attnfuse_fwd_plan.  With have_ptrs false the data pointers are not
+// examined.
+int plan_fwd(const void* q, const void* k, const void* v, const void* out,
+             const attnfuse_variant_desc* desc, bool have_ptrs, AttnParams& p, FwdPlan& f) {
+  f = FwdPlan{};
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
@@ -179,12 +175,13 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   }
   // Q / out may be NULL only when there are no queries, K / V only when there
   // are no keys (empty tensors).
-  if ((d->Nq > 0 && (!q || !out)) || (d->Nk > 0 && (!k || !v))) return ATTNFUSE_ERR_INVALID;
+  if (have_ptrs && ((d->Nq > 0 && (!q || !out)) || (d->Nk > 0 && (!k || !v))))
+    return ATTNFUSE_ERR_INVALID;
   // fp32 kernels read the fp32 tables; bf16 kernels rotate Q and K with the
   // fp16 pairs.
   if (d->dtype == ATTNFUSE_FP32 && !fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;
   if (d->dtype == ATTNFUSE_BF16 && !f16_table_ok(d)) return ATTNFUSE_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+  if (have_ptrs && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)))
     return ATTNFUSE_ERR_UNSUPPORTED;
   const bool sparse = d->bs_row_ptr != nullptr;
   const bool bf16 = d->dtype == ATTNFUSE_BF16;
@@ -196,9 +193,8 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
     if (bf16 && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;
     if (!bf16 && (d->bs_block_m % 64 || d->bs_block_n % 32)) return ATTNFUSE_ERR_UNSUPPORTED;
   }
-  if (d->Nq == 0) return ATTNFUSE_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  AttnParams p = base_params(q, k, v, out, d);
+  if (d->Nq == 0) return ATTNFUSE_OK;  // plan: nothing to launch
+  p = base_params(q, k, v, const_cast<void*>(out), d);
   if (d->Nk == 0) p.row_ptr = nullptr;  // nothing to visit: every row is empty
   const bool use_sparse = p.row_ptr != nullptr;
   p.longest_first = (d->causal && d->window == 0 && !use_sparse) ? 1 : 0;
@@ -207,7 +203,8 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
     p.n_qblk = (d->Nq + 63) / 64;
     const long long grid = (long long)d->B * d->Hq * p.n_qblk;
     if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
-    return hip_status(attnfuse::launch_fwd_fp32(p, d->D, (unsigned)grid, s));
+    f = FwdPlan{ATTNFUSE_PLAN_FP32, 1, 1, 64, grid};
+    return ATTNFUSE_OK;
   }
 
   if (fp8) {
@@ -234,10 +231,8 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
     const double sc = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->D);
     p.scale_log2 = (float)(sc * 1.4426950408889634 * (double)d->q_scale * (double)d->k_scale);
     p.v_scale = d->v_scale;
-    const bool alibi = d->alibi_slopes != nullptr;
-    hipError_t e = d->D == 128 ? attnfuse::launch_fwd_fp8<128>(p, alibi, use_sparse, (unsigned)grid, s)
-                               : attnfuse::launch_fwd_fp8<64>(p, alibi, use_sparse, (unsigned)grid, s);
-    return hip_status(e);
+    f = FwdPlan{ATTNFUSE_PLAN_FP8, 8, hp, 32 * (8 / hp), grid};
+    return ATTNFUSE_OK;
   }
 
   // bf16 MFMA kernel: choose waves per workgroup (NW) and q-heads per
@@ -299,20 +294,86 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
   const int RB = NW / hp;
   p.n_units = d->B * d->Hkv * (p.G / hp);
   p.n_qblk = (d->Nq + 32 * RB - 1) / (32 * RB);
-  const long long grid = (long long)p.n_units * p.n_qblk;
+  long long grid = (long long)p.n_units * p.n_qblk;
   if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
-  const unsigned g = (unsigned)grid;
+  // Causal dense attention without a window: workgroup j of a unit runs
+  // query block n_qblk - 1 - j and then block j, so every workgroup streams
+  // about n_qblk + 1 key tiles and half as many workgroups pay the start-up
+  // and drain of a block.  Needs the eight-wave schedule without a score
+  // modifier, keys for every row (band_hi >= 0) and enough pairs to keep one
+  // workgroup on each of the 256 CUs.
+  const long long pairs = (long long)p.n_units * (p.n_qblk / 2);
+  if (NW == 8 && !scoremod && p.longest_first && d->Nk > 0 && p.band_hi >= 0 && pairs >= 256) {
+    p.pair = 1;
+    grid = (long long)p.n_units * ((p.n_qblk + 1) / 2);
+  }
+  f = FwdPlan{ATTNFUSE_PLAN_BF16, NW, hp, 32 * RB, grid};
+  return ATTNFUSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attnfuse_status_string(int status) {
+  switch (status) {
+    case ATTNFUSE_OK: return "ok";
+    case ATTNFUSE_ERR_INVALID: return "invalid argument or descriptor";
+    case ATTNFUSE_ERR_UNSUPPORTED: return "unsupported variant or shape";
+    case ATTNFUSE_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTNFUSE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
+                 const attnfuse_variant_desc* desc, void* stream) {
+  AttnParams p;
+  FwdPlan f;
+  const int st = plan_fwd(q, k, v, out, desc, true, p, f);
+  if (st != ATTNFUSE_OK || f.kind == ATTNFUSE_PLAN_NONE) return st;
+  const attnfuse_variant_desc* d = desc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const unsigned g = (unsigned)f.grid;
+  const bool use_sparse = p.row_ptr != nullptr;
+  const bool scoremod = d->alibi_slopes != nullptr || d->bias != nullptr;
+  if (f.kind == ATTNFUSE_PLAN_FP32) return hip_status(attnfuse::launch_fwd_fp32(p, d->D, g, s));
+  if (f.kind == ATTNFUSE_PLAN_FP8) {
+    const bool alibi = d->alibi_slopes != nullptr;
+    return hip_status(d->D == 128 ? attnfuse::launch_fwd_fp8<128>(p, alibi, use_sparse, g, s)
+                                  : attnfuse::launch_fwd_fp8<64>(p, alibi, use_sparse, g, s));
+  }
+  const bool rope = d->rope != 0;
   hipError_t e;
   if (d->D == 128) {
-    if (NW == 8) e = attnfuse::launch_fwd_bf16<128, 8>(p, rope, scoremod, use_sparse, g, s);
-    else if (NW == 4) e = attnfuse::launch_fwd_bf16<128, 4>(p, rope, scoremod, use_sparse, g, s);
+    if (f.NW == 8) e = attnfuse::launch_fwd_bf16<128, 8>(p, rope, scoremod, use_sparse, g, s);
+    else if (f.NW == 4) e = attnfuse::launch_fwd_bf16<128, 4>(p, rope, scoremod, use_sparse, g, s);
     else e = attnfuse::launch_fwd_bf16<128, 2>(p, rope, scoremod, use_sparse, g, s);
   } else {
-    if (NW == 8) e = attnfuse::launch_fwd_bf16<64, 8>(p, rope, scoremod, use_sparse, g, s);
-    else if (NW == 4) e = attnfuse::launch_fwd_bf16<64, 4>(p, rope, scoremod, use_sparse, g, s);
+    if (f.NW == 8) e = attnfuse::launch_fwd_bf16<64, 8>(p, rope, scoremod, use_sparse, g, s);
+    else if (f.NW == 4) e = attnfuse::launch_fwd_bf16<64, 4>(p, rope, scoremod, use_sparse, g, s);
     else e = attnfuse::launch_fwd_bf16<64, 2>(p, rope, scoremod, use_sparse, g, s);
   }
   return hip_status(e);
+}
+
+int attnfuse_fwd_plan(const attnfuse_variant_desc* desc, attnfuse_fwd_plan_info* info) {
+  if (!info) return ATTNFUSE_ERR_INVALID;
+  AttnParams p;
+  FwdPlan f;
+  const int st = plan_fwd(nullptr, nullptr, nullptr, nullptr, desc, false, p, f);
+  if (st != ATTNFUSE_OK) return st;
+  *info = attnfuse_fwd_plan_info{};
+  info->kernel = f.kind;
+  if (f.kind != ATTNFUSE_PLAN_NONE) {
+    info->waves = f.NW;
+    info->heads = f.hp;
+    info->rows = f.rows;
+    info->query_blocks = p.n_qblk;
+    info->paired = p.pair;
+    info->workgroups = f.grid;
+  }
+  return ATTNFUSE_OK;
 }
 
 size_t attnfuse_decode_workspace_size(const attnfuse_variant_desc* desc, int32_t num_splits) {

@@ -64,6 +64,9 @@ struct AttnParams {
   int n_units;                // B * Hkv * (G / hp)
   int n_qblk;                 // query blocks per unit
   int longest_first;          // schedule later (longer) query blocks first
+  // Paired workgroups (causal, dense, eight waves): workgroup j of a unit runs
+  // query block n_qblk - 1 - j and then block j, as one stream of key tiles.
+  int pair;
   // split-KV decode
   int splits, chunk, n_hgrp;
   float* ws;
@@ -314,9 +317,16 @@ __device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
 // Same, with the global address split into a wave-uniform 64-bit base and a
 // per-lane unsigned 32-bit byte offset (one VGPR instead of two).
 __device__ __forceinline__ void dma16_off(uint32_t lds_base, const void* base, uint32_t off) {
+  // base is wave-uniform by construction; readfirstlane keeps it in SGPRs
+  // where the compiler cannot prove that itself.  (readfirstlane returns an
+  // int: each half goes through uint32_t so that widening never sign-extends.)
+  const uint64_t b64 = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(off), "s"(base)
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(off), "s"(reinterpret_cast<const void*>(bs))
                : "memory", "m0");
 }
 

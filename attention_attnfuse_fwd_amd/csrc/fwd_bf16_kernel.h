@@ -189,17 +189,27 @@ fwd_bf16_kernel(const AttnParams p) {
   const int unit = blockIdx.x % p.n_units;
   const int qrank = blockIdx.x / p.n_units;
   const int qblk = p.longest_first ? (p.n_qblk - 1 - qrank) : qrank;
+  // A paired workgroup (see AttnParams::pair) runs a second query block,
+  // qrank, after qblk (-1: none).
+  constexpr bool PAIRABLE = PP && !FP8 && !SCOREMOD && !SPARSE;
+  const int qblk2 = (PAIRABLE && p.pair && qrank < qblk) ? qrank : -1;
   const int n_hg = p.G / hp;
   const int hg = unit % n_hg;
   const int kvh = (unit / n_hg) % p.Hkv;
   const int b = unit / (n_hg * p.Hkv);
   const int h = kvh * p.G + hg * hp + (wave % hp);
-  const int r0_wg = qblk * rows_wg;
-  const int w0 = r0_wg + 32 * (wave / hp);  // first row of this wave
-  const int i = w0 + lq;                    // this lane's query row
-  const int iq = min(i, p.Nq - 1);
-  const int wg_last = min(r0_wg + rows_wg, p.Nq) - 1;
-  const int w_last = min(w0 + 31, p.Nq - 1);
+  // Rows of the query block being processed (switched between the blocks of
+  // a paired workgroup).
+  int r0_wg, w0, i, iq, wg_last, w_last;
+  auto set_rows = [&](int qb) {
+    r0_wg = qb * rows_wg;
+    w0 = r0_wg + 32 * (wave / hp);  // first row of this wave
+    i = w0 + lq;                    // this lane's query row
+    iq = min(i, p.Nq - 1);
+    wg_last = min(r0_wg + rows_wg, p.Nq) - 1;
+    w_last = min(w0 + 31, p.Nq - 1);
+  };
+  set_rows(qblk);
 
   const __bf16* qb = reinterpret_cast<const __bf16*>(p.q) + b * p.qsb + h * p.qsh;
   const __bf16* kb = reinterpret_cast<const __bf16*>(p.k) + b * p.ksb + kvh * p.ksh;
@@ -225,6 +235,17 @@ fwd_bf16_kernel(const AttnParams p) {
     t_begin = j_lo / 64;
     n_tiles = (j_hi >= j_lo) ? (j_hi / 64 - t_begin + 1) : 0;
   }
+  // Paired: the second block's tiles follow the first block's in one stream
+  // (both start at key 0: a causal band with no window); stream tile u >=
+  // seg_split is tile u - seg_split of the second block.
+  int seg_split = 1 << 30, n_first = n_tiles, n_second = 0;
+  if (qblk2 >= 0) {
+    const int wg_last2 = min((qblk2 + 1) * rows_wg, p.Nq) - 1;
+    const int j_hi2 = min(p.Nk - 1, (int)min((long long)wg_last2 + p.band_hi, (long long)kBandInf));
+    n_second = j_hi2 >= 0 ? j_hi2 / 64 + 1 : 0;
+    seg_split = n_tiles;
+    n_tiles += n_second;
+  }
   // Column indices are clamped into [0, nkb]; column nkb (or anything past
   // the keys) lands at k0 >= Nk, is loaded clamped and masked out entirely.
   // The list is read with scalar loads, which do not count against vmcnt.
@@ -242,7 +263,7 @@ fwd_bf16_kernel(const AttnParams p) {
       const int col = min(max(((cidx_t)p.col_idx)[s_begin + t / tpb], 0), nkb);
       return col * p.bn + (t % tpb) * 64;
     }
-    return (t_begin + (rev ? n_tiles - 1 - t : t)) * 64;
+    return (t_begin + (rev ? n_tiles - 1 - t : (t >= seg_split ? t - seg_split : t))) * 64;
   };
 
   const int Nk = p.Nk, band_lo = p.band_lo, band_hi = p.band_hi;
@@ -576,18 +597,24 @@ fwd_bf16_kernel(const AttnParams p) {
   // it for every row of this wave) form one interval [mlo, mhi], computed
   // once here instead of per tile.
   int mlo = 0, mhi = -1;
-  if (!SPARSE) {
-    auto fdiv = [](long long a) -> long long { return a >= 0 ? a / 64 : -((-a + 63) / 64); };
-    long long lo = 0, hi = min((long long)n_tiles - 1, fdiv((long long)Nk - 64) - t_begin);
-    if (has_band) {
-      lo = max(lo, -fdiv(-((long long)band_lo + w_last)) - t_begin);          // k0 - w_last >= band_lo
-      hi = min(hi, fdiv((long long)band_hi + w0 - 63) - t_begin);             // k0 + 63 - w0 <= band_hi
+  // (n_seg: tiles of the query block being processed.)
+  auto set_masks = [&](int n_seg) {
+    mlo = 0;
+    mhi = -1;
+    if (!SPARSE) {
+      auto fdiv = [](long long a) -> long long { return a >= 0 ? a / 64 : -((-a + 63) / 64); };
+      long long lo = 0, hi = min((long long)n_seg - 1, fdiv((long long)Nk - 64) - t_begin);
+      if (has_band) {
+        lo = max(lo, -fdiv(-((long long)band_lo + w_last)) - t_begin);          // k0 - w_last >= band_lo
+        hi = min(hi, fdiv((long long)band_hi + w0 - 63) - t_begin);             // k0 + 63 - w0 <= band_hi
+      }
+      if (lo <= hi) {
+        mlo = (int)lo;
+        mhi = (int)hi;
+      }
     }
-    if (lo <= hi) {
-      mlo = (int)lo;
-      mhi = (int)hi;
-    }
-  }
+  };
+  set_masks(n_first);
   // Masks of S^T tile u in place (only where the tile needs them: the key
   // tail, or the band edge crossing this wave's rows).  A tile past the list
   // (the last iteration's look-ahead) is masked out entirely.
@@ -602,13 +629,14 @@ fwd_bf16_kernel(const AttnParams p) {
         need_mask |= (dmin < band_lo) | (dmax > band_hi);
       }
     } else {
-      const int pu = rev ? n_tiles - 1 - u : u;  // tile's place in key order (< 0 past the list)
+      // tile's place in its block's key order (< 0 past the list)
+      const int pu = rev ? n_tiles - 1 - u : (u >= seg_split ? u - seg_split : u);
       need_mask = (pu < mlo) | (pu > mhi);
     }
     if (need_mask) {
       const int k0 = tile_k0(min(u, n_tiles - 1));
       // Allowed register offsets form one interval [lo_off, hi_off].
-      const int jd = k0 + 4 * lh - i;  // j - i at register offset 0
+      const int jd = (k0 - w0) + (4 * lh - lq);  // j - i at register offset 0 (i = w0 + lq)
       int lo_off = -kBandInf, hi_off = Nk - 1 - (k0 + 4 * lh);
       if (has_band) {
         lo_off = band_lo - jd;
@@ -741,19 +769,26 @@ fwd_bf16_kernel(const AttnParams p) {
   const int n = n_tiles;
   bf16x8 pfa[4], pfb[4];  // P^T of the tile the next iteration multiplies with V (ping-pong)
   // S(0) -> P(0) in the prologue, shared by both schedules.
-  auto first_tile = [&]() {
-    const int k00 = tile_k0(0);
+  // S(u0) -> P(u0) into pf (u0 = 0, or the first tile of a paired
+  // workgroup's second block), K'(u0) read from its ring slot.
+  auto first_tile_at = [&](int u0, bf16x8 (&pf)[4]) {
+    const int k00 = tile_k0(u0);
+    const uint32_t ks0 = lds0 + (uint32_t)(u0 % RING) * L::KSLOT;
+    auto kf0 = [&](int st, int kk) -> bf16x8 {  // k_frag, addressed through klane
+      return lds_read16(ks0 + klane[kk % (NKK / 2)] + (kk / (NKK / 2)) * L::KHI + 32 * st * D);
+    };
     f32x16 s0[2];
 #pragma unroll
     for (int k = 0; k < 2 * NKK; ++k)
-      s0[k & 1] = mfma32(k_frag(smem, k & 1, k >> 1), qf[k >> 1], k < 2 ? (SCOREMOD ? (CSPLAT ? f32x16{} + mod_base(k00) : f32x16{}) : minit) : s0[k & 1]);
-    mask_scores(0, s0);
+      s0[k & 1] = mfma32(kf0(k & 1, k >> 1), qf[k >> 1], k < 2 ? (SCOREMOD ? (CSPLAT ? f32x16{} + mod_base(k00) : f32x16{}) : minit) : s0[k & 1]);
+    mask_scores(u0, s0);
     uint32_t pw[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00);
     finish_tile(s0, -neg_m(), pw);
-    to_frags(pw, pfa);
+    to_frags(pw, pf);
   };
+  auto first_tile = [&]() { first_tile_at(0, pfa); };
   if constexpr (FP8) {
     // ---- fp8 ping-pong schedule ----
     // The two-waves-per-SIMD alternation of the bf16 schedule below, with
@@ -1085,18 +1120,74 @@ fwd_bf16_kernel(const AttnParams p) {
       vcluster(0, 0, false, pfb);
       __syncthreads();
     }
-    auto step = [&](int t, const bf16x8 (&pf_cur)[4], bf16x8 (&pf_nxt)[4]) {
+    auto step = [&](int t, const bf16x8 (&pf_cur)[4], bf16x8 (&pf_nxt)[4], bool has_s)
+        __attribute__((always_inline)) {
       mcluster(t, pf_cur);
       __syncthreads();
-      vcluster(t + dstep, t + 1, true, pf_nxt);
+      vcluster(t + dstep, t + 1, has_s, pf_nxt);
       __syncthreads();
     };
-    int t = 0;
-    for (; t + 1 < n; t += 2) {
-      step(t, pfa, pfb);
-      step(t + 1, pfb, pfa);
+    // Steps T0 .. T1-1 (P(t) sits in pfa for even t - T0); the last step
+    // takes the softmax of S(T1) only if LAST.  (A macro: the two loops are
+    // separate copies, so neither keeps the other's state live.)
+#define ATTNFUSE_RUN_STEPS(T0, T1, LAST)                          \
+  {                                                               \
+    int t_ = (T0);                                                \
+    const int t1_ = (T1);                                         \
+    const bool last_ = (LAST);                                    \
+    for (; t_ + 1 < t1_; t_ += 2) {                               \
+      step(t_, pfa, pfb, true);                                   \
+      step(t_ + 1, pfb, pfa, last_ || t_ + 2 < t1_);              \
+    }                                                             \
+    if (t_ < t1_) step(t_, pfa, pfb, last_);                      \
+  }
+    // A paired workgroup runs two query blocks over one stream of key tiles.
+    // The first block's last step computes S(seg_split) with its own Q, so
+    // that tile's softmax waits for the second block's Q.
+    const bool paired = PAIRABLE && qblk2 >= 0 && n_first > 0 && n_second > 0;
+    ATTNFUSE_RUN_STEPS(0, paired ? seg_split : n, !paired)
+    if (paired) {
+      // Both halves are past step seg_split - 1 here (the second half has
+      // also run its vector cluster of step seg_split).  K'(seg_split),
+      // K'(seg_split + 1), V(seg_split), V(seg_split + 1) are in their
+      // slots; the next tiles' loads are in flight.
+      if (m_first) __syncthreads();
+      const int i_a = i;
+      const float l_a = ol[0], m_a = m_run;
+      // The first block's output, O^T / l from registers in 8-byte pieces.
+      {
+        const float inv = l_a > 0.f ? p.v_scale / l_a : 0.f;
+        __bf16* const orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh + (long long)i_a * p.osn;
+        if (i_a < p.Nq) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint2 w;
+              w.x = pack_bf16x2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
+              w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+              *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * g + 4 * lh) = w;
+            }
+        }
+        if (i_a < p.Nq && p.lse && lh == 0)
+          p.lse[((long long)b * p.Hq + h) * p.Nq + i_a] =
+              l_a > 0.f ? (m_a + __builtin_log2f(l_a)) * kLn2 : -INFINITY;
+      }
+      set_rows(qblk2);
+      load_q_issue();  // the second block's Q rows and angles (direct loads: every slot is busy)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+      ol = f32x16{};
+      m_run = -INFINITY;
+      minit = f32x16{};
+      set_masks(n_second);
+      load_q_finish();
+      first_tile_at(seg_split, pfa);
+      // The second half sits out one slot, restoring the alternation.
+      if (!m_first) __syncthreads();
+      ATTNFUSE_RUN_STEPS(seg_split, n, true)
     }
-    if (t < n) step(t, pfa, pfb);
+#undef ATTNFUSE_RUN_STEPS
     // Same barrier count in both halves: the first half's closing barrier
     // matches the second half's extra vector cluster.
     if (n > 0 && m_first) __syncthreads();

@@ -331,6 +331,29 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     return (out, lse) if return_lse else out
 
 
+def fwd_plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             window: int = 0, rope_theta: Optional[float] = None, q_pos0: int = 0, k_pos0: int = 0,
+             alibi_slopes=None, bias=None, block_mask: Optional[BlockMask] = None,
+             scale: Optional[float] = None, tile: Optional[tuple] = None) -> dict:
+    """The launch ``fwd`` would make for these arguments (prefill kernels; the
+    single-query decode path is not considered): kernel, waves and q-heads per
+    workgroup, query rows per block, blocks per unit, pairing and grid."""
+    _check_inputs(q, k, v)
+    keep = []
+    d = _make_desc(q, k, v, q, scale=scale, causal=causal, window=window, rope_theta=rope_theta,
+                   q_pos0=q_pos0, k_pos0=k_pos0, alibi_slopes=alibi_slopes, bias=bias,
+                   block_mask=block_mask, lse=None, keep=keep)
+    if _E4M3 is not None and q.dtype == _E4M3:
+        d.kv_fp8, d.q_fp8 = 1, 1
+    if tile is not None:
+        d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
+    info = _abi.FwdPlanInfo()
+    _check(_abi.load().attnfuse_fwd_plan(ctypes.byref(d), ctypes.byref(info)), "fwd_plan")
+    out = {f: getattr(info, f) for f, _ in _abi.FwdPlanInfo._fields_}
+    out["kernel"] = _abi.PLAN_KERNELS[info.kernel]
+    return out
+
+
 def decode_workspace_size(q, k_cache, num_splits: int) -> int:
     d = _abi.VariantDesc.new()
     d.dtype = _dtype_code(q)

@@ -202,6 +202,35 @@ typedef struct attnfuse_variant_desc {
 int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
                  const attnfuse_variant_desc* desc, void* stream);
 
+/* Which kernel attnfuse_fwd launches for a descriptor, and how ("3.2 From
+ * DSL to Kernel": one fused kernel per variant, its tile chosen per shape).
+ * kernel: ATTNFUSE_PLAN_NONE (Nq == 0: nothing is launched), _FP32, _BF16
+ * (the MFMA kernel) or _FP8.  waves and heads: waves and q-heads per
+ * workgroup; rows: query rows of one head per query block; query_blocks:
+ * blocks per (batch, kv-head, head group) unit; paired: 1 when every
+ * workgroup of a causal dense launch runs two query blocks, block
+ * query_blocks - 1 - j and block j, so that all workgroups stream about the
+ * same number of key tiles; workgroups: the grid.  Validates `desc` exactly
+ * as attnfuse_fwd does, except for the data pointers, which are not
+ * examined; returns the status attnfuse_fwd would return for valid
+ * pointers.  `info` is host memory owned by the caller; on an error it is
+ * left unchanged. */
+#define ATTNFUSE_PLAN_NONE 0
+#define ATTNFUSE_PLAN_FP32 1
+#define ATTNFUSE_PLAN_BF16 2
+#define ATTNFUSE_PLAN_FP8 3
+typedef struct attnfuse_fwd_plan_info {
+  int32_t kernel;
+  int32_t waves;
+  int32_t heads;
+  int32_t rows;
+  int32_t query_blocks;
+  int32_t paired;
+  int64_t workgroups;
+} attnfuse_fwd_plan_info;
+
+int attnfuse_fwd_plan(const attnfuse_variant_desc* desc, attnfuse_fwd_plan_info* info);
+
 /* Bytes of workspace attnfuse_decode needs for `desc` and `num_splits`
  * (B * Hq * num_splits * (D + 2) * 4).  Returns 0 for an invalid descriptor. */
 size_t attnfuse_decode_workspace_size(const attnfuse_variant_desc* desc, int32_t num_splits);

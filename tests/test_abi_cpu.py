@@ -318,3 +318,92 @@ def test_fp8_query_is_rejected_by_the_other_entry_points(lib):
                                None) == _abi.ERR_UNSUPPORTED
     assert lib.attnfuse_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(d), FAKE,
                             1 << 20, None) == _abi.ERR_UNSUPPORTED
+
+
+def _shape_desc(B, Hq, Hkv, N, D, rope=True, dtype=_abi.BF16, **kw):
+    d = _abi.VariantDesc.new()
+    d.dtype = dtype
+    d.B, d.Hq, d.Hkv, d.Nq, d.Nk, d.D = B, Hq, Hkv, N, N, D
+    for f, H in (("q_stride", Hq), ("k_stride", Hkv), ("v_stride", Hkv), ("o_stride", Hq)):
+        arr = getattr(d, f)
+        arr[0], arr[1], arr[2] = H * N * D, N * D, D
+    if rope:
+        d.rope, d.rope_theta, d.rope_table_len = 1, 5e5, 2 * N + 1
+        d.rope_cs_f16 = d.rope_cos = d.rope_sin = FAKE.value
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _plan(lib, d):
+    info = _abi.FwdPlanInfo()
+    st = lib.attnfuse_fwd_plan(ctypes.byref(d), ctypes.byref(info))
+    return st, {f: getattr(info, f) for f, _ in _abi.FwdPlanInfo._fields_}
+
+
+def test_plan_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in _abi.FwdPlanInfo._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){",
+            'printf("size %zu\\n", sizeof(attnfuse_fwd_plan_info));']
+    prog += [f'printf("{f} %zu\\n", offsetof(attnfuse_fwd_plan_info, {f}));' for f in fields]
+    prog += ['printf("kinds %d %d %d %d\\n", ATTNFUSE_PLAN_NONE, ATTNFUSE_PLAN_FP32, ATTNFUSE_PLAN_BF16,'
+             ' ATTNFUSE_PLAN_FP8);', "return 0;}"]
+    c = tmp_path / "plan.c"
+    c.write_text("\n".join(prog))
+    exe = tmp_path / "plan"
+    subprocess.run(["gcc", "-std=c99", str(c), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines()
+    out = {ln.split()[0]: ln.split()[1:] for ln in lines}
+    assert int(out["size"][0]) == ctypes.sizeof(_abi.FwdPlanInfo)
+    for f in fields:
+        assert int(out[f][0]) == getattr(_abi.FwdPlanInfo, f).offset, f
+    assert {int(x): _abi.PLAN_KERNELS[int(x)] for x in out["kinds"]} == _abi.PLAN_KERNELS
+
+
+# (desc kwargs, expected plan fields).  The Llama-3-8B prefill (B=1, Hq=32,
+# Hkv=8, N=4096, d=128): four q-heads of a group per eight-wave workgroup,
+# 64-row blocks, 8 units x 64 blocks; causal without a window pairs block
+# 63 - j with block j in 256 workgroups.
+PLAN_CASES = [
+    ("llama8b_causal", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1),
+     dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=64, paired=1, workgroups=256)),
+    ("llama8b_full", dict(B=1, Hq=32, Hkv=8, N=4096, D=128),
+     dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=64, paired=0, workgroups=512)),
+    ("llama8b_causal_window", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, window=1024),
+     dict(paired=0, workgroups=512)),
+    # odd block count: the middle block runs alone
+    ("odd_blocks", dict(B=2, Hq=64, Hkv=16, N=1200, D=128, causal=1),
+     dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=19, paired=1, workgroups=32 * 10)),
+    # too few pairs to fill the chip
+    ("small_grid", dict(B=1, Hq=8, Hkv=2, N=1024, D=128, causal=1), dict(paired=0)),
+    # a score modifier keeps one block per workgroup
+    ("alibi", dict(B=1, Hq=32, Hkv=32, N=4096, D=128, rope=False, causal=1, alibi_slopes=FAKE.value),
+     dict(paired=0)),
+    # queries before the keys: early rows have no keys, no pairing
+    ("rows_without_keys", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, k_pos0=64), dict(paired=0)),
+    ("fp32", dict(B=1, Hq=4, Hkv=4, N=256, D=64, dtype=_abi.FP32, causal=1),
+     dict(kernel=1, waves=1, heads=1, rows=64, query_blocks=4, paired=0, workgroups=16)),
+    ("no_queries", dict(B=1, Hq=4, Hkv=4, N=256, D=64, Nq=0),
+     dict(kernel=0, waves=0, workgroups=0)),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_fwd_plan(lib, name, kw, want):
+    kw = dict(kw)
+    d = _shape_desc(kw.pop("B"), kw.pop("Hq"), kw.pop("Hkv"), kw.pop("N"), kw.pop("D"), **kw)
+    st, info = _plan(lib, d)
+    assert st == _abi.OK
+    for f, v in want.items():
+        assert info[f] == v, (f, info)
+
+
+def test_fwd_plan_status_matches_fwd(lib):
+    for kw in (dict(tile_waves=3), dict(struct_size=8), dict(window=-1), dict(kv_fp8=2)):
+        d = _good_desc(**kw)
+        st, _ = _plan(lib, d)
+        assert st == _fwd(lib, d) != _abi.OK, kw
+    info = _abi.FwdPlanInfo(kernel=7)
+    assert lib.attnfuse_fwd_plan(ctypes.byref(_good_desc(tile_waves=3)), ctypes.byref(info)) != _abi.OK
+    assert info.kernel == 7  # left unchanged on an error
+    assert lib.attnfuse_fwd_plan(ctypes.byref(_good_desc()), None) == _abi.ERR_INVALID

@@ -208,6 +208,9 @@ def test_full_size_elementwise(name):
     w = W[name]
     inp = workloads.make_inputs(w)
     log(f"case {name} full size, seed {w.seed}")
+    q, k, v = dev_inputs(inp)
+    log(f"plan {af.fwd_plan(q, k, v, **_gpu_kw(w, inp))}")
+    del q, k, v
     out, lse = _run(w, inp)
     ref, rlse = oracle_all_heads(inp.q, inp.k, inp.v, w.B, w.Hq, **_oracle_kw(w, inp))
     check_close(out, ref, w.dtype, f"{name} (all {out.size} elements)")
@@ -217,6 +220,34 @@ def test_full_size_elementwise(name):
         G = w.Hq // w.Hkv
         v0 = inp.v[:, np.arange(w.Hq) // G, 0, :]
         np.testing.assert_array_equal(out[:, :, 0, :], v0)
+
+
+# Paired workgroups: causal dense launches with enough query blocks run block
+# n_qblk - 1 - j and block j in one workgroup, as one stream of key tiles.
+PAIRED = [
+    # odd block count (19: the middle block runs alone) and a ragged last block
+    ("paired_odd_ragged_rope", dict(B=2, Hq=64, Hkv=16, Nq=1200, Nk=1200)),
+    # one q-head per workgroup (no GQA), 256-row blocks, d = 64, no RoPE
+    ("paired_mha_d64", dict(B=4, Hq=32, Hkv=32, Nq=1024, Nk=1024, D=64, rope_theta=None)),
+    # queries after the keys: every block sees 200 keys beyond its diagonal
+    ("paired_queries_after_keys", dict(B=2, Hq=64, Hkv=16, Nq=1000, Nk=1200, q_pos0=200,
+                                       rope_theta=1e4)),
+]
+
+
+@pytest.mark.parametrize("name,over", PAIRED, ids=[c[0] for c in PAIRED])
+def test_paired_workgroups_elementwise(name, over):
+    w = W["llama3_8b_rope_causal_n4096"].with_(**over)
+    inp = workloads.make_inputs(w)
+    log(f"case {name}: {w}")
+    q, k, v = dev_inputs(inp)
+    plan = af.fwd_plan(q, k, v, **_gpu_kw(w, inp))
+    log(f"plan {plan}")
+    assert plan["kernel"] == "bf16" and plan["paired"] == 1, plan
+    out, lse = _run(w, inp)
+    ref, rlse = oracle_all_heads(inp.q, inp.k, inp.v, w.B, w.Hq, **_oracle_kw(w, inp))
+    check_close(out, ref, w.dtype, f"{name} (all {out.size} elements)")
+    check_lse(lse, rlse, 2e-2, f"{name} (all {lse.size} rows)")
 
 
 # ----------------------------------------------------------------------------
