@@ -38,6 +38,7 @@ EXPORTS = (
     "attnfuse_status_string",
     # include/attnfuse_microbench.h
     "attnfuse_mb_mfma_bf16",
+    "attnfuse_mb_mfma_bf16_ops",
     "attnfuse_mb_hbm_read",
     "attnfuse_mb_host_cost",
 )
@@ -154,6 +155,8 @@ def load() -> ctypes.CDLL:
     lib.attnfuse_status_string.restype = ctypes.c_char_p
     lib.attnfuse_mb_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P]
     lib.attnfuse_mb_mfma_bf16.restype = ctypes.c_int
+    lib.attnfuse_mb_mfma_bf16_ops.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+    lib.attnfuse_mb_mfma_bf16_ops.restype = ctypes.c_int
     lib.attnfuse_mb_hbm_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int32, P, P, P]
     lib.attnfuse_mb_hbm_read.restype = ctypes.c_int
     lib.attnfuse_mb_host_cost.argtypes = [ctypes.c_int32, P, P, P, P, D, ctypes.c_int32, P, ctypes.c_size_t,

@@ -51,6 +51,39 @@ __global__ __launch_bounds__(256) void mb_mfma_bf16_kernel(int iters, float* sin
   }
 }
 
+// Same loop with operands read once from `ops` (four bf16x8 per lane: a0,
+// b0, a1, b1) and alternated between consecutive MFMAs, so the matrix core's
+// inputs change every instruction as they do in a real product (the loop
+// above feeds it the same small integers throughout).
+__global__ __launch_bounds__(256) void mb_mfma_bf16_ops_kernel(int iters, const uint4* __restrict__ ops,
+                                                               float* sink, unsigned long long* stamps) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const bf16x8 a0 = __builtin_bit_cast(bf16x8, ops[4 * t + 0]);
+  const bf16x8 b0 = __builtin_bit_cast(bf16x8, ops[4 * t + 1]);
+  const bf16x8 a1 = __builtin_bit_cast(bf16x8, ops[4 * t + 2]);
+  const bf16x8 b1 = __builtin_bit_cast(bf16x8, ops[4 * t + 3]);
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const bool stamp = blockIdx.x == 0 && threadIdx.x == 0;
+  unsigned long long t0 = 0, r0 = 0;
+  if (stamp) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  for (int i = 0; i < iters; ++i) {
+    c0 = mfma32(a0, b0, c0);
+    c1 = mfma32(a1, b1, c1);
+    c2 = mfma32(a0, b1, c2);
+    c3 = mfma32(a1, b0, c3);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  sink[t] = s;
+  if (stamp) {
+    stamps[0] = __builtin_amdgcn_s_memtime() - t0;
+    stamps[1] = __builtin_amdgcn_s_memrealtime() - r0;
+  }
+}
+
 // Grid-stride read of n16 16-byte words, four loads in flight per thread; the
 // XOR of everything read goes to sink so that no load can be dropped.
 __global__ __launch_bounds__(256) void mb_read_kernel(const uint4* __restrict__ src,
@@ -101,6 +134,17 @@ int attnfuse_mb_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, unsign
     return ATTNFUSE_MB_ERR_INVALID;
   hipLaunchKernelGGL(attnfuse::mb_mfma_bf16_kernel, dim3(workgroups), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), iters, sink, stamps);
+  return hipGetLastError() == hipSuccess ? ATTNFUSE_MB_OK : ATTNFUSE_MB_ERR_HIP;
+}
+
+int attnfuse_mb_mfma_bf16_ops(int32_t workgroups, int32_t iters, const void* operands, float* sink,
+                              unsigned long long* stamps, void* stream) {
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24) || !operands ||
+      !attnfuse::aligned16(operands) || !sink || !stamps)
+    return ATTNFUSE_MB_ERR_INVALID;
+  hipLaunchKernelGGL(attnfuse::mb_mfma_bf16_ops_kernel, dim3(workgroups), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), iters, reinterpret_cast<const uint4*>(operands),
+                     sink, stamps);
   return hipGetLastError() == hipSuccess ? ATTNFUSE_MB_OK : ATTNFUSE_MB_ERR_HIP;
 }
 

@@ -42,6 +42,15 @@ enum {
 int attnfuse_mb_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, unsigned long long* stamps,
                           void* stream);
 
+/* The same matrix-core loop on caller-given operands: `operands` holds
+ * workgroups * 256 * 64 bytes of device memory (16-byte aligned), four
+ * bf16x8 values per thread (a0, b0, a1, b1); consecutive MFMAs alternate
+ * them (a0 b0, a1 b1, a0 b1, a1 b0), so with random values the matrix
+ * core's inputs change every instruction.  Same work, sink and stamps as
+ * attnfuse_mb_mfma_bf16. */
+int attnfuse_mb_mfma_bf16_ops(int32_t workgroups, int32_t iters, const void* operands, float* sink,
+                              unsigned long long* stamps, void* stream);
+
 /* Streaming read of `bytes` bytes at `src` (16-byte aligned, bytes a multiple
  * of 16) by `workgroups` workgroups of 256 threads, 16-byte loads, grid-stride
  * with four loads in flight per thread.  sink: workgroups * 256 floats;

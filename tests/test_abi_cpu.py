@@ -244,6 +244,10 @@ def test_microbench_entry_points_reject_bad_arguments(lib):
     assert lib.attnfuse_mb_mfma_bf16(0, 10, sink, stamps, None) == -1
     assert lib.attnfuse_mb_mfma_bf16(1, 0, sink, stamps, None) == -1
     assert lib.attnfuse_mb_mfma_bf16(1, 10, None, stamps, None) == -1
+    assert lib.attnfuse_mb_mfma_bf16_ops(1, 10, None, sink, stamps, None) == -1
+    assert lib.attnfuse_mb_mfma_bf16_ops(1, 10, P(0x300008), sink, stamps, None) == -1
+    assert lib.attnfuse_mb_mfma_bf16_ops(0, 10, P(0x300000), sink, stamps, None) == -1
+    assert lib.attnfuse_mb_mfma_bf16_ops(1, 0, P(0x300000), sink, stamps, None) == -1
     assert lib.attnfuse_mb_hbm_read(P(0x100000), 15, 1, sink, stamps, None) == -1
     assert lib.attnfuse_mb_hbm_read(P(0x100008), 1024, 1, sink, stamps, None) == -1
     assert lib.attnfuse_mb_hbm_read(None, 1024, 1, sink, stamps, None) == -1
