@@ -296,15 +296,20 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
   p.n_qblk = (d->Nq + 32 * RB - 1) / (32 * RB);
   long long grid = (long long)p.n_units * p.n_qblk;
   if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
-  // Causal dense attention without a window: workgroup j of a unit runs
-  // query block n_qblk - 1 - j and then block j, so every workgroup streams
-  // about n_qblk + 1 key tiles and half as many workgroups pay the start-up
-  // and drain of a block.  Needs the eight-wave schedule without a score
-  // modifier, keys for every row (band_hi >= 0) and enough pairs to keep one
-  // workgroup on each of the 256 CUs.
+  // Causal dense attention: workgroup j of a unit runs query block
+  // n_qblk - 1 - j and then block j as one stream of key tiles, so half as
+  // many workgroups pay the start-up and drain of a block (without a window
+  // every workgroup also streams about n_qblk + 1 key tiles).  Needs the
+  // eight-wave schedule without an additive bias (ALiBi slopes are fine),
+  // key tiles for every block (band_hi >= 0 for the first, the last block's
+  // band starting inside the keys) and enough pairs to keep one workgroup on
+  // each of the 256 CUs.
   const long long pairs = (long long)p.n_units * (p.n_qblk / 2);
-  if (NW == 8 && !scoremod && p.longest_first && d->Nk > 0 && p.band_hi >= 0 && pairs >= 256) {
+  const long long last_lo = (long long)(p.n_qblk - 1) * (32 * RB) + p.band_lo;
+  if (NW == 8 && !use_sparse && d->bias == nullptr && d->causal && d->Nk > 0 && p.band_hi >= 0 &&
+      last_lo <= d->Nk - 1 && pairs >= 256) {
     p.pair = 1;
+    p.longest_first = 1;
     grid = (long long)p.n_units * ((p.n_qblk + 1) / 2);
   }
   f = FwdPlan{ATTNFUSE_PLAN_BF16, NW, hp, 32 * RB, grid};

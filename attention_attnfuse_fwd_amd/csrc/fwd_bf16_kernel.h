@@ -191,7 +191,7 @@ fwd_bf16_kernel(const AttnParams p) {
   const int qblk = p.longest_first ? (p.n_qblk - 1 - qrank) : qrank;
   // A paired workgroup (see AttnParams::pair) runs a second query block,
   // qrank, after qblk (-1: none).
-  constexpr bool PAIRABLE = PP && !FP8 && !SCOREMOD && !SPARSE;
+  constexpr bool PAIRABLE = PP && !FP8 && !SPARSE && !BIAS;
   const int qblk2 = (PAIRABLE && p.pair && qrank < qblk) ? qrank : -1;
   const int n_hg = p.G / hp;
   const int hg = unit % n_hg;
@@ -216,6 +216,17 @@ fwd_bf16_kernel(const AttnParams p) {
   const __bf16* vb = reinterpret_cast<const __bf16*>(p.v) + b * p.vsb + kvh * p.vsh;
 
   // ---- key tiles this workgroup visits ----
+  // Dense lists: the band's key range [j_lo, j_hi] of rows r0..rlast, as
+  // tiles [tb, tb + nt).
+  auto dense_range = [&](int r0, int rlast, int& tb, int& nt) {
+    int j_lo = 0, j_hi = p.Nk - 1;
+    if (p.has_band) {
+      j_lo = max(j_lo, r0 + max(p.band_lo, -kBandInf));
+      j_hi = min(j_hi, (int)min((long long)rlast + p.band_hi, (long long)kBandInf));
+    }
+    tb = j_lo / 64;
+    nt = (j_hi >= j_lo) ? (j_hi / 64 - tb + 1) : 0;
+  };
   int n_tiles, t_begin = 0, s_begin = 0, tpb = 1;
   if (SPARSE) {
     const int* rp = p.row_ptr + (p.bs_head_stride ? (long long)h * p.bs_head_stride : 0);
@@ -227,22 +238,14 @@ fwd_bf16_kernel(const AttnParams p) {
     tpb = p.bn / 64;
     n_tiles = (int)(e - a) * tpb;
   } else {
-    int j_lo = 0, j_hi = p.Nk - 1;
-    if (p.has_band) {
-      j_lo = max(j_lo, r0_wg + max(p.band_lo, -kBandInf));
-      j_hi = min(j_hi, (int)min((long long)wg_last + p.band_hi, (long long)kBandInf));
-    }
-    t_begin = j_lo / 64;
-    n_tiles = (j_hi >= j_lo) ? (j_hi / 64 - t_begin + 1) : 0;
+    dense_range(r0_wg, wg_last, t_begin, n_tiles);
   }
-  // Paired: the second block's tiles follow the first block's in one stream
-  // (both start at key 0: a causal band with no window); stream tile u >=
-  // seg_split is tile u - seg_split of the second block.
-  int seg_split = 1 << 30, n_first = n_tiles, n_second = 0;
+  // Paired: the second block's tiles follow the first block's in one stream;
+  // stream tile u >= seg_split is tile u - seg_split of the second block,
+  // whose key tiles start at t_begin2.
+  int seg_split = 1 << 30, n_first = n_tiles, n_second = 0, t_begin2 = 0;
   if (qblk2 >= 0) {
-    const int wg_last2 = min((qblk2 + 1) * rows_wg, p.Nq) - 1;
-    const int j_hi2 = min(p.Nk - 1, (int)min((long long)wg_last2 + p.band_hi, (long long)kBandInf));
-    n_second = j_hi2 >= 0 ? j_hi2 / 64 + 1 : 0;
+    dense_range(qblk2 * rows_wg, min((qblk2 + 1) * rows_wg, p.Nq) - 1, t_begin2, n_second);
     seg_split = n_tiles;
     n_tiles += n_second;
   }
@@ -263,7 +266,9 @@ fwd_bf16_kernel(const AttnParams p) {
       const int col = min(max(((cidx_t)p.col_idx)[s_begin + t / tpb], 0), nkb);
       return col * p.bn + (t % tpb) * 64;
     }
-    return (t_begin + (rev ? n_tiles - 1 - t : (t >= seg_split ? t - seg_split : t))) * 64;
+    const bool s2 = t >= seg_split;  // (rev: each block's tiles from its last key tile down)
+    const int loc = s2 ? t - seg_split : t;
+    return ((s2 ? t_begin2 : t_begin) + (rev ? (s2 ? n_second : n_first) - 1 - loc : loc)) * 64;
   };
 
   const int Nk = p.Nk, band_lo = p.band_lo, band_hi = p.band_hi;
@@ -592,21 +597,21 @@ fwd_bf16_kernel(const AttnParams p) {
       bias4[g] = *reinterpret_cast<const float4*>(brow + min(k0 + 8 * g + 4 * lh, Nk - 4));
   };
 
-  // Dense key lists: tile u starts at key 64 * (t_begin + u), so the tiles
-  // that need no mask (inside the key range and, with a band, wholly inside
-  // it for every row of this wave) form one interval [mlo, mhi], computed
-  // once here instead of per tile.
+  // Dense key lists: the block's tile in key order u starts at key
+  // 64 * (tb + u), so the tiles that need no mask (inside the key range and,
+  // with a band, wholly inside it for every row of this wave) form one
+  // interval [mlo, mhi], computed once per block instead of per tile.
   int mlo = 0, mhi = -1;
-  // (n_seg: tiles of the query block being processed.)
-  auto set_masks = [&](int n_seg) {
+  // (n_seg, tb: tiles and first key tile of the query block being processed.)
+  auto set_masks = [&](int n_seg, int tb) {
     mlo = 0;
     mhi = -1;
     if (!SPARSE) {
       auto fdiv = [](long long a) -> long long { return a >= 0 ? a / 64 : -((-a + 63) / 64); };
-      long long lo = 0, hi = min((long long)n_seg - 1, fdiv((long long)Nk - 64) - t_begin);
+      long long lo = 0, hi = min((long long)n_seg - 1, fdiv((long long)Nk - 64) - tb);
       if (has_band) {
-        lo = max(lo, -fdiv(-((long long)band_lo + w_last)) - t_begin);          // k0 - w_last >= band_lo
-        hi = min(hi, fdiv((long long)band_hi + w0 - 63) - t_begin);             // k0 + 63 - w0 <= band_hi
+        lo = max(lo, -fdiv(-((long long)band_lo + w_last)) - tb);          // k0 - w_last >= band_lo
+        hi = min(hi, fdiv((long long)band_hi + w0 - 63) - tb);             // k0 + 63 - w0 <= band_hi
       }
       if (lo <= hi) {
         mlo = (int)lo;
@@ -614,7 +619,7 @@ fwd_bf16_kernel(const AttnParams p) {
       }
     }
   };
-  set_masks(n_first);
+  set_masks(n_first, t_begin);
   // Masks of S^T tile u in place (only where the tile needs them: the key
   // tail, or the band edge crossing this wave's rows).  A tile past the list
   // (the last iteration's look-ahead) is masked out entirely.
@@ -630,7 +635,9 @@ fwd_bf16_kernel(const AttnParams p) {
       }
     } else {
       // tile's place in its block's key order (< 0 past the list)
-      const int pu = rev ? n_tiles - 1 - u : (u >= seg_split ? u - seg_split : u);
+      const bool s2 = u >= seg_split;
+      const int loc = s2 ? u - seg_split : u;
+      const int pu = rev ? (s2 ? n_second : n_first) - 1 - loc : loc;
       need_mask = (pu < mlo) | (pu > mhi);
     }
     if (need_mask) {
@@ -1180,7 +1187,7 @@ fwd_bf16_kernel(const AttnParams p) {
       ol = f32x16{};
       m_run = -INFINITY;
       minit = f32x16{};
-      set_masks(n_second);
+      set_masks(n_second, t_begin2);
       load_q_finish();
       first_tile_at(seg_split, pfa);
       // The second half sits out one slot, restoring the alternation.

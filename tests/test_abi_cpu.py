@@ -373,16 +373,27 @@ PLAN_CASES = [
      dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=64, paired=1, workgroups=256)),
     ("llama8b_full", dict(B=1, Hq=32, Hkv=8, N=4096, D=128),
      dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=64, paired=0, workgroups=512)),
+    # a causal window pairs too (each block streams its own window's tiles)
     ("llama8b_causal_window", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, window=1024),
-     dict(paired=0, workgroups=512)),
+     dict(paired=1, workgroups=256)),
+    # the ALiBi + causal + window workload (B=2, H=16, N=8192, W=1024): 32 units x 16 pairs
+    ("alibi_window", dict(B=2, Hq=16, Hkv=16, N=8192, D=128, rope=False, causal=1, window=1024,
+                          alibi_slopes=FAKE.value),
+     dict(kernel=2, waves=8, heads=1, rows=256, query_blocks=32, paired=1, workgroups=512)),
+    # non-causal: no pairing
+    ("two_sided_window", dict(B=2, Hq=16, Hkv=16, N=8192, D=128, rope=False, window=1024),
+     dict(paired=0, workgroups=1024)),
     # odd block count: the middle block runs alone
     ("odd_blocks", dict(B=2, Hq=64, Hkv=16, N=1200, D=128, causal=1),
      dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=19, paired=1, workgroups=32 * 10)),
     # too few pairs to fill the chip
     ("small_grid", dict(B=1, Hq=8, Hkv=2, N=1024, D=128, causal=1), dict(paired=0)),
-    # a score modifier keeps one block per workgroup
-    ("alibi", dict(B=1, Hq=32, Hkv=32, N=4096, D=128, rope=False, causal=1, alibi_slopes=FAKE.value),
+    # an additive bias keeps one block per workgroup (ALiBi slopes alone pair)
+    ("bias", dict(B=1, Hq=32, Hkv=32, N=4096, D=128, rope=False, causal=1, bias=FAKE.value,
+                  bias_stride=(0, 4096 * 4096, 4096, 1)),
      dict(paired=0)),
+    ("alibi", dict(B=1, Hq=32, Hkv=32, N=4096, D=128, rope=False, causal=1, alibi_slopes=FAKE.value),
+     dict(paired=1, workgroups=256)),
     # queries before the keys: early rows have no keys, no pairing
     ("rows_without_keys", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, k_pos0=64), dict(paired=0)),
     ("fp32", dict(B=1, Hq=4, Hkv=4, N=256, D=64, dtype=_abi.FP32, causal=1),

@@ -226,18 +226,28 @@ def test_full_size_elementwise(name):
 # n_qblk - 1 - j and block j in one workgroup, as one stream of key tiles.
 PAIRED = [
     # odd block count (19: the middle block runs alone) and a ragged last block
-    ("paired_odd_ragged_rope", dict(B=2, Hq=64, Hkv=16, Nq=1200, Nk=1200)),
+    ("paired_odd_ragged_rope", "llama3_8b_rope_causal_n4096", dict(B=2, Hq=64, Hkv=16, Nq=1200, Nk=1200)),
     # one q-head per workgroup (no GQA), 256-row blocks, d = 64, no RoPE
-    ("paired_mha_d64", dict(B=4, Hq=32, Hkv=32, Nq=1024, Nk=1024, D=64, rope_theta=None)),
+    ("paired_mha_d64", "llama3_8b_rope_causal_n4096",
+     dict(B=4, Hq=32, Hkv=32, Nq=1024, Nk=1024, D=64, rope_theta=None)),
     # queries after the keys: every block sees 200 keys beyond its diagonal
-    ("paired_queries_after_keys", dict(B=2, Hq=64, Hkv=16, Nq=1000, Nk=1200, q_pos0=200,
-                                       rope_theta=1e4)),
+    ("paired_queries_after_keys", "llama3_8b_rope_causal_n4096",
+     dict(B=2, Hq=64, Hkv=16, Nq=1000, Nk=1200, q_pos0=200, rope_theta=1e4)),
+    # causal window with RoPE: each block streams its own window's tiles; 18 blocks, ragged tail
+    ("paired_rope_window", "llama3_8b_rope_causal_n4096",
+     dict(B=2, Hq=64, Hkv=16, Nq=1100, Nk=1100, window=500)),
+    # ALiBi (tiles visited from the diagonal down) + window, 9 blocks of 256 rows, ragged tail
+    ("paired_alibi_window_odd_ragged", "alibi_causal_window1024_n8192",
+     dict(B=2, Hq=32, Hkv=32, Nq=2200, Nk=2200, window=300)),
+    # ALiBi causal, no window, queries after the keys
+    ("paired_alibi_after_keys", "alibi_causal_window1024_n8192",
+     dict(B=4, Hq=32, Hkv=32, Nq=1000, Nk=1100, window=0, q_pos0=100)),
 ]
 
 
-@pytest.mark.parametrize("name,over", PAIRED, ids=[c[0] for c in PAIRED])
-def test_paired_workgroups_elementwise(name, over):
-    w = W["llama3_8b_rope_causal_n4096"].with_(**over)
+@pytest.mark.parametrize("name,base,over", PAIRED, ids=[c[0] for c in PAIRED])
+def test_paired_workgroups_elementwise(name, base, over):
+    w = W[base].with_(**over)
     inp = workloads.make_inputs(w)
     log(f"case {name}: {w}")
     q, k, v = dev_inputs(inp)
