@@ -146,6 +146,28 @@ int largest_pow2_divisor(int g, int cap) {
   return hp;
 }
 
+// Causal dense attention: workgroup j of a unit runs query block
+// n_qblk - 1 - j and then block j as one stream of key tiles, so half as
+// many workgroups pay the start-up and drain of a block (without a window
+// every workgroup also streams about n_qblk + 1 key tiles).  Needs the
+// eight-wave schedule without an additive bias (ALiBi slopes are fine), key
+// tiles for every block (band_hi >= 0 for the first, the last block's band
+// starting inside the keys) and enough pairs to keep one workgroup on each
+// of the 256 CUs.  Sets p.pair (and the longest-first block order the
+// pairing uses) and returns the grid.
+long long pair_blocks(AttnParams& p, const attnfuse_variant_desc* d, int rows, bool eight_waves,
+                      bool sparse, long long grid) {
+  const long long pairs = (long long)p.n_units * (p.n_qblk / 2);
+  const long long last_lo = (long long)(p.n_qblk - 1) * rows + p.band_lo;
+  if (eight_waves && !sparse && d->bias == nullptr && d->causal && d->Nk > 0 && p.band_hi >= 0 &&
+      last_lo <= d->Nk - 1 && pairs >= 256) {
+    p.pair = 1;
+    p.longest_first = 1;
+    return (long long)p.n_units * ((p.n_qblk + 1) / 2);
+  }
+  return grid;
+}
+
 // Launch choice of attnfuse_fwd.
 struct FwdPlan {
   int kind = ATTNFUSE_PLAN_NONE;
@@ -225,8 +247,9 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
     p.hp = hp;
     p.n_units = d->B * d->Hkv * (p.G / hp);
     p.n_qblk = (d->Nq + 32 * (8 / hp) - 1) / (32 * (8 / hp));
-    const long long grid = (long long)p.n_units * p.n_qblk;
+    long long grid = (long long)p.n_units * p.n_qblk;
     if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+    grid = pair_blocks(p, d, 32 * (8 / hp), true, use_sparse, grid);
     // Products of codes: both dequantisation scales join the score scale.
     const double sc = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->D);
     p.scale_log2 = (float)(sc * 1.4426950408889634 * (double)d->q_scale * (double)d->k_scale);
@@ -296,22 +319,7 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
   p.n_qblk = (d->Nq + 32 * RB - 1) / (32 * RB);
   long long grid = (long long)p.n_units * p.n_qblk;
   if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
-  // Causal dense attention: workgroup j of a unit runs query block
-  // n_qblk - 1 - j and then block j as one stream of key tiles, so half as
-  // many workgroups pay the start-up and drain of a block (without a window
-  // every workgroup also streams about n_qblk + 1 key tiles).  Needs the
-  // eight-wave schedule without an additive bias (ALiBi slopes are fine),
-  // key tiles for every block (band_hi >= 0 for the first, the last block's
-  // band starting inside the keys) and enough pairs to keep one workgroup on
-  // each of the 256 CUs.
-  const long long pairs = (long long)p.n_units * (p.n_qblk / 2);
-  const long long last_lo = (long long)(p.n_qblk - 1) * (32 * RB) + p.band_lo;
-  if (NW == 8 && !use_sparse && d->bias == nullptr && d->causal && d->Nk > 0 && p.band_hi >= 0 &&
-      last_lo <= d->Nk - 1 && pairs >= 256) {
-    p.pair = 1;
-    p.longest_first = 1;
-    grid = (long long)p.n_units * ((p.n_qblk + 1) / 2);
-  }
+  grid = pair_blocks(p, d, 32 * RB, NW == 8, use_sparse, grid);
   f = FwdPlan{ATTNFUSE_PLAN_BF16, NW, hp, 32 * RB, grid};
   return ATTNFUSE_OK;
 }

@@ -191,7 +191,7 @@ fwd_bf16_kernel(const AttnParams p) {
   const int qblk = p.longest_first ? (p.n_qblk - 1 - qrank) : qrank;
   // A paired workgroup (see AttnParams::pair) runs a second query block,
   // qrank, after qblk (-1: none).
-  constexpr bool PAIRABLE = PP && !FP8 && !SPARSE && !BIAS;
+  constexpr bool PAIRABLE = PP && !SPARSE && !BIAS;
   const int qblk2 = (PAIRABLE && p.pair && qrank < qblk) ? qrank : -1;
   const int n_hg = p.G / hp;
   const int hg = unit % n_hg;
@@ -796,6 +796,58 @@ fwd_bf16_kernel(const AttnParams p) {
     to_frags(pw, pf);
   };
   auto first_tile = [&]() { first_tile_at(0, pfa); };
+  // Paired workgroups, at the switch between the blocks: the first block's
+  // output, O^T / l straight from registers in 8-byte pieces, and its lse,
+  // then the second block's rows (its Q loads can be issued after this) ...
+  auto finish_first_block = [&]() {
+    const int i_a = i;
+    const float l_a = ol[0], m_a = m_run;
+    const float inv = l_a > 0.f ? p.v_scale / l_a : 0.f;
+    __bf16* const orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh + (long long)i_a * p.osn;
+    if (i_a < p.Nq) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2 w;
+          w.x = pack_bf16x2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
+          w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * g + 4 * lh) = w;
+        }
+    }
+    if (i_a < p.Nq && p.lse && lh == 0)
+      p.lse[((long long)b * p.Hq + h) * p.Nq + i_a] =
+          l_a > 0.f ? (m_a + __builtin_log2f(l_a)) * kLn2 : -INFINITY;
+    set_rows(qblk2);
+  };
+  // ... and a fresh softmax state for the second block.
+  auto start_second_block = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
+    ol = f32x16{};
+    m_run = -INFINITY;
+    minit = f32x16{};
+    set_masks(n_second, t_begin2);
+  };
+  // A paired workgroup runs two query blocks over one stream of key tiles.
+  // The first block's last step computes S(seg_split) with its own Q, so
+  // that tile's softmax waits for the second block's Q.
+  const bool paired = PAIRABLE && qblk2 >= 0 && n_first > 0 && n_second > 0;
+  // Steps T0 .. T1-1 of a ping-pong schedule with step function STEP (P(t)
+  // sits in pfa for even t - T0); the last step takes the softmax of S(T1)
+  // only if LAST.  (A macro: every use is a separate copy of the loop, so
+  // none keeps another's state live.)
+#define ATTNFUSE_RUN_STEPS(STEP, T0, T1, LAST)                    \
+  {                                                               \
+    int t_ = (T0);                                                \
+    const int t1_ = (T1);                                         \
+    const bool last_ = (LAST);                                    \
+    for (; t_ + 1 < t1_; t_ += 2) {                               \
+      STEP(t_, pfa, pfb, true);                                   \
+      STEP(t_ + 1, pfb, pfa, last_ || t_ + 2 < t1_);              \
+    }                                                             \
+    if (t_ < t1_) STEP(t_, pfa, pfb, last_);                      \
+  }
   if constexpr (FP8) {
     // ---- fp8 ping-pong schedule ----
     // The two-waves-per-SIMD alternation of the bf16 schedule below, with
@@ -880,19 +932,23 @@ fwd_bf16_kernel(const AttnParams p) {
       if (n > 1) convert_v8(1);
     }
     __syncthreads();
-    if (n > 0) {
-      const int k00 = tile_k0(0);
+    // S(u0) -> P(u0) into pf from K(u0)'s ring slot (u0 = 0, or the first
+    // tile of a paired workgroup's second block).
+    auto first_tile8_at = [&](int u0, bf16x8 (&pf)[4]) {
+      const int k00 = tile_k0(u0);
+      const uint32_t ks0 = lds0 + (uint32_t)(u0 % RING) * L8::KSLOT;
       f32x16 s0[2];
 #pragma unroll
       for (int j = 0; j < NS8; ++j)
-        s0[j & 1] = mfma32_f8(kf8(lds0, j & 1, j >> 1), qf8[j >> 1], j < 2 ? f32x16{} : s0[j & 1]);
-      mask_scores(0, s0);
+        s0[j & 1] = mfma32_f8(kf8(ks0, j & 1, j >> 1), qf8[j >> 1], j < 2 ? f32x16{} : s0[j & 1]);
+      mask_scores(u0, s0);
       uint32_t pw[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) pw[x] = exp_pair(s0, x, k00);
       finish_tile(s0, -neg_m(), pw);
-      to_frags(pw, pfa);
-    }
+      to_frags(pw, pf);
+    };
+    if (n > 0) first_tile8_at(0, pfa);
     constexpr int PF = 2;
     f32x16 sn[2];
     auto mcluster8 = [&](int t, const bf16x8 (&pf)[4]) {
@@ -949,18 +1005,26 @@ fwd_bf16_kernel(const AttnParams p) {
       vcluster8(0, 0, false, pfb);
       __syncthreads();
     }
-    auto step8 = [&](int t, const bf16x8 (&pf_cur)[4], bf16x8 (&pf_nxt)[4]) {
+    auto step8 = [&](int t, const bf16x8 (&pf_cur)[4], bf16x8 (&pf_nxt)[4], bool has_s)
+        __attribute__((always_inline)) {
       mcluster8(t, pf_cur);
       __syncthreads();
-      vcluster8(t + dstep, t + 1, true, pf_nxt);
+      vcluster8(t + dstep, t + 1, has_s, pf_nxt);
       __syncthreads();
     };
-    int t = 0;
-    for (; t + 1 < n; t += 2) {
-      step8(t, pfa, pfb);
-      step8(t + 1, pfb, pfa);
+    ATTNFUSE_RUN_STEPS(step8, 0, paired ? seg_split : n, !paired)
+    if (paired) {
+      // The switch between the blocks of a paired workgroup, as in the bf16
+      // schedule below: the first half waits out one barrier slot, the
+      // second block's first tile comes from K(seg_split)'s ring slot.
+      if (m_first) __syncthreads();
+      finish_first_block();
+      load_q8();
+      start_second_block();
+      first_tile8_at(seg_split, pfa);
+      if (!m_first) __syncthreads();
+      ATTNFUSE_RUN_STEPS(step8, seg_split, n, true)
     }
-    if (t < n) step8(t, pfa, pfb);
     if (n > 0 && m_first) __syncthreads();
   } else if constexpr (PP) {
     // ---- ping-pong schedule (two waves per SIMD) ----
@@ -1134,65 +1198,21 @@ fwd_bf16_kernel(const AttnParams p) {
       vcluster(t + dstep, t + 1, has_s, pf_nxt);
       __syncthreads();
     };
-    // Steps T0 .. T1-1 (P(t) sits in pfa for even t - T0); the last step
-    // takes the softmax of S(T1) only if LAST.  (A macro: the two loops are
-    // separate copies, so neither keeps the other's state live.)
-#define ATTNFUSE_RUN_STEPS(T0, T1, LAST)                          \
-  {                                                               \
-    int t_ = (T0);                                                \
-    const int t1_ = (T1);                                         \
-    const bool last_ = (LAST);                                    \
-    for (; t_ + 1 < t1_; t_ += 2) {                               \
-      step(t_, pfa, pfb, true);                                   \
-      step(t_ + 1, pfb, pfa, last_ || t_ + 2 < t1_);              \
-    }                                                             \
-    if (t_ < t1_) step(t_, pfa, pfb, last_);                      \
-  }
-    // A paired workgroup runs two query blocks over one stream of key tiles.
-    // The first block's last step computes S(seg_split) with its own Q, so
-    // that tile's softmax waits for the second block's Q.
-    const bool paired = PAIRABLE && qblk2 >= 0 && n_first > 0 && n_second > 0;
-    ATTNFUSE_RUN_STEPS(0, paired ? seg_split : n, !paired)
+    ATTNFUSE_RUN_STEPS(step, 0, paired ? seg_split : n, !paired)
     if (paired) {
       // Both halves are past step seg_split - 1 here (the second half has
       // also run its vector cluster of step seg_split).  K'(seg_split),
       // K'(seg_split + 1), V(seg_split), V(seg_split + 1) are in their
       // slots; the next tiles' loads are in flight.
       if (m_first) __syncthreads();
-      const int i_a = i;
-      const float l_a = ol[0], m_a = m_run;
-      // The first block's output, O^T / l from registers in 8-byte pieces.
-      {
-        const float inv = l_a > 0.f ? p.v_scale / l_a : 0.f;
-        __bf16* const orow = reinterpret_cast<__bf16*>(p.o) + b * p.osb + h * p.osh + (long long)i_a * p.osn;
-        if (i_a < p.Nq) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              uint2 w;
-              w.x = pack_bf16x2(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
-              w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-              *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * g + 4 * lh) = w;
-            }
-        }
-        if (i_a < p.Nq && p.lse && lh == 0)
-          p.lse[((long long)b * p.Hq + h) * p.Nq + i_a] =
-              l_a > 0.f ? (m_a + __builtin_log2f(l_a)) * kLn2 : -INFINITY;
-      }
-      set_rows(qblk2);
+      finish_first_block();
       load_q_issue();  // the second block's Q rows and angles (direct loads: every slot is busy)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
-      ol = f32x16{};
-      m_run = -INFINITY;
-      minit = f32x16{};
-      set_masks(n_second, t_begin2);
+      start_second_block();
       load_q_finish();
       first_tile_at(seg_split, pfa);
       // The second half sits out one slot, restoring the alternation.
       if (!m_first) __syncthreads();
-      ATTNFUSE_RUN_STEPS(seg_split, n, true)
+      ATTNFUSE_RUN_STEPS(step, seg_split, n, true)
     }
 #undef ATTNFUSE_RUN_STEPS
     // Same barrier count in both halves: the first half's closing barrier

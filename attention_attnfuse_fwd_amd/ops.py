@@ -345,6 +345,7 @@ def fwd_plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
                    block_mask=block_mask, lse=None, keep=keep)
     if _E4M3 is not None and q.dtype == _E4M3:
         d.kv_fp8, d.q_fp8 = 1, 1
+        d.q_scale = d.k_scale = d.v_scale = 1.0  # (scales do not change the launch)
     if tile is not None:
         d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
     info = _abi.FwdPlanInfo()

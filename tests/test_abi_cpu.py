@@ -398,6 +398,10 @@ PLAN_CASES = [
     ("rows_without_keys", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, k_pos0=64), dict(paired=0)),
     ("fp32", dict(B=1, Hq=4, Hkv=4, N=256, D=64, dtype=_abi.FP32, causal=1),
      dict(kernel=1, waves=1, heads=1, rows=64, query_blocks=4, paired=0, workgroups=16)),
+    # fp8 inputs pair the same way (GQA 4:1, 19 blocks of 64 rows)
+    ("fp8_causal", dict(B=2, Hq=64, Hkv=16, N=1200, D=128, rope=False, causal=1, kv_fp8=1, q_fp8=1,
+                        q_scale=1.0, k_scale=1.0, v_scale=1.0),
+     dict(kernel=3, waves=8, heads=4, rows=64, query_blocks=19, paired=1, workgroups=320)),
     ("no_queries", dict(B=1, Hq=4, Hkv=4, N=256, D=64, Nq=0),
      dict(kernel=0, waves=0, workgroups=0)),
 ]

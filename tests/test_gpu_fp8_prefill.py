@@ -44,6 +44,42 @@ CASES = {
 }
 
 
+# Paired workgroups (block n_qblk - 1 - j, then block j, in one stream):
+# shapes with at least 256 pairs.
+PAIRED = {
+    # GQA 4:1, 19 blocks of 64 rows (odd: the middle block alone), ragged tail
+    "paired_gqa_causal_odd_ragged_d128": (2, 64, 16, 1200, 1200, 128, dict(causal=True)),
+    # ALiBi + window, MHA, 9 blocks of 256 rows
+    "paired_alibi_window_d128": (2, 32, 32, 2200, 2200, 128, dict(causal=True, window=300, alibi=True)),
+    # d = 64, queries after the keys
+    "paired_after_keys_d64": (4, 32, 32, 1000, 1100, 64, dict(causal=True, q_pos0=100)),
+}
+
+
+def _kw_pair(kw, Hq):
+    kw = dict(kw)
+    okw = {k: v for k, v in kw.items() if k != "alibi"}
+    if kw.pop("alibi", False):
+        sl = workloads.alibi_slopes(Hq)
+        kw["alibi_slopes"] = torch.from_numpy(sl).cuda()
+        okw["alibi_slopes"] = sl.astype(np.float64)
+    return kw, okw
+
+
+@pytest.mark.parametrize("name", sorted(PAIRED))
+def test_fp8_prefill_paired(name):
+    B, Hq, Hkv, Nq, Nk, D, kw = PAIRED[name]
+    qkv = _fp8_inputs(B, Hq, Hkv, Nq, Nk, D, seed=len(name))
+    kw, okw = _kw_pair(kw, Hq)
+    plan = af.fwd_plan(_dev8(qkv[0][0]), _dev8(qkv[1][0]), _dev8(qkv[2][0]), **kw)
+    log(f"case fp8 prefill {name}: plan {plan}")
+    assert plan["kernel"] == "fp8" and plan["paired"] == 1, plan
+    out, lse = _run(qkv, **kw)
+    ref, rlse = oracle_all_heads(qkv[0][1], qkv[1][1], qkv[2][1], B, Hq, **okw)
+    check_close(out, ref, "bf16", f"fp8 prefill {name} (all {out.size} elements)")
+    check_lse(lse, rlse, 2e-2, f"fp8 prefill {name}")
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_fp8_prefill_small(name):
     B, Hq, Hkv, Nq, Nk, D, kw = CASES[name]
