@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include <hip/hip_runtime.h>
@@ -150,22 +151,46 @@ int largest_pow2_divisor(int g, int cap) {
 // n_qblk - 1 - j and then block j as one stream of key tiles, so half as
 // many workgroups pay the start-up and drain of a block (without a window
 // every workgroup also streams about n_qblk + 1 key tiles).  Needs the
-// eight-wave schedule without an additive bias (ALiBi slopes are fine), key
-// tiles for every block (band_hi >= 0 for the first, the last block's band
-// starting inside the keys) and enough pairs to keep one workgroup on each
-// of the 256 CUs.  Sets p.pair (and the longest-first block order the
-// pairing uses) and returns the grid.
+// eight-wave schedule without an additive bias (ALiBi slopes are fine) and
+// key tiles for every block (band_hi >= 0 for the first, the last block's
+// band starting inside the keys).  Whether it pays depends on how the grid
+// fills the CUs (one eight-wave workgroup per CU at a time): a time model
+// in key tiles, with a fixed start-up and drain per workgroup, compares
+// rounds of pairs against the unpaired blocks spread over the CUs (e.g.
+// the GPT-2-small shape B4 H12 N4096 D64: 384 pairs are one and a half
+// rounds, 15% slower than 768 single blocks; the Llama-3-8B shape: 256
+// pairs, one round, faster).  Sets p.pair (and the longest-first block
+// order the pairing uses) and returns the grid.
 long long pair_blocks(AttnParams& p, const attnfuse_variant_desc* d, int rows, bool eight_waves,
                       bool sparse, long long grid) {
-  const long long pairs = (long long)p.n_units * (p.n_qblk / 2);
-  const long long last_lo = (long long)(p.n_qblk - 1) * rows + p.band_lo;
-  if (eight_waves && !sparse && d->bias == nullptr && d->causal && d->Nk > 0 && p.band_hi >= 0 &&
-      last_lo <= d->Nk - 1 && pairs >= 256) {
-    p.pair = 1;
-    p.longest_first = 1;
-    return (long long)p.n_units * ((p.n_qblk + 1) / 2);
+  constexpr long long kCUs = 256;     // MI355X compute units
+  constexpr long long kFixed = 4;     // start-up + drain of a workgroup, in key tiles
+  const long long n = p.n_qblk;
+  const long long last_lo = (n - 1) * rows + p.band_lo;
+  if (!eight_waves || sparse || d->bias != nullptr || !d->causal || d->Nk <= 0 || p.band_hi < 0 ||
+      last_lo > d->Nk - 1 || n < 2)
+    return grid;
+  // Key tiles of query block j (the kernel's band range).
+  auto tiles = [&](long long j) -> long long {
+    const long long r0 = j * rows, rlast = std::min(r0 + rows, (long long)d->Nq) - 1;
+    const long long lo = std::max(0LL, r0 + std::max((long long)p.band_lo, -(long long)kBandInf));
+    const long long hi = std::min((long long)d->Nk - 1, rlast + p.band_hi);
+    return hi >= lo ? hi / 64 - lo / 64 + 1 : 0;
+  };
+  long long sum = 0, longest = 0, longest_pair = 0;
+  for (long long j = 0; j < n; ++j) {
+    const long long t = tiles(j);
+    sum += t;
+    longest = std::max(longest, t);
+    if (j < n - 1 - j) longest_pair = std::max(longest_pair, t + tiles(n - 1 - j));
   }
-  return grid;
+  const long long units = p.n_units, pairs = units * ((n + 1) / 2);
+  const long long t_single = std::max((units * (sum + n * kFixed) + kCUs - 1) / kCUs, longest + kFixed);
+  const long long t_paired = (pairs + kCUs - 1) / kCUs * (longest_pair + kFixed + 1);
+  if (t_paired >= t_single) return grid;
+  p.pair = 1;
+  p.longest_first = 1;
+  return pairs;
 }
 
 // Launch choice of attnfuse_fwd.

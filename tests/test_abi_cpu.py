@@ -373,9 +373,16 @@ PLAN_CASES = [
      dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=64, paired=1, workgroups=256)),
     ("llama8b_full", dict(B=1, Hq=32, Hkv=8, N=4096, D=128),
      dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=64, paired=0, workgroups=512)),
-    # a causal window pairs too (each block streams its own window's tiles)
+    # a causal window of 1024: one round of 256 pairs of 34 tiles does not beat
+    # 512 single blocks (952 tiles per unit) spread over the CUs
     ("llama8b_causal_window", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, window=1024),
-     dict(paired=1, workgroups=256)),
+     dict(paired=0, workgroups=512)),
+    # GPT-2-small, N=4096: 384 pairs would be one and a half rounds
+    ("gpt2_small_causal", dict(B=4, Hq=12, Hkv=12, N=4096, D=64, causal=1),
+     dict(paired=0, workgroups=768)),
+    # N=8192: 768 pairs, three full rounds
+    ("gpt2_small_causal_8k", dict(B=4, Hq=12, Hkv=12, N=8192, D=64, causal=1),
+     dict(paired=1, workgroups=768)),
     # the ALiBi + causal + window workload (B=2, H=16, N=8192, W=1024): 32 units x 16 pairs
     ("alibi_window", dict(B=2, Hq=16, Hkv=16, N=8192, D=128, rope=False, causal=1, window=1024,
                           alibi_slopes=FAKE.value),
@@ -383,9 +390,12 @@ PLAN_CASES = [
     # non-causal: no pairing
     ("two_sided_window", dict(B=2, Hq=16, Hkv=16, N=8192, D=128, rope=False, window=1024),
      dict(paired=0, workgroups=1024)),
-    # odd block count: the middle block runs alone
-    ("odd_blocks", dict(B=2, Hq=64, Hkv=16, N=1200, D=128, causal=1),
-     dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=19, paired=1, workgroups=32 * 10)),
+    # odd block count: the middle block runs alone (32 units x 8 = 256 workgroups)
+    ("odd_blocks", dict(B=2, Hq=64, Hkv=16, N=950, D=128, causal=1),
+     dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=15, paired=1, workgroups=256)),
+    # 19 blocks: 320 pairs are one and a quarter rounds, so no pairing
+    ("odd_blocks_partial_round", dict(B=2, Hq=64, Hkv=16, N=1200, D=128, causal=1),
+     dict(query_blocks=19, paired=0, workgroups=32 * 19)),
     # too few pairs to fill the chip
     ("small_grid", dict(B=1, Hq=8, Hkv=2, N=1024, D=128, causal=1), dict(paired=0)),
     # an additive bias keeps one block per workgroup (ALiBi slopes alone pair)
@@ -398,10 +408,10 @@ PLAN_CASES = [
     ("rows_without_keys", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, k_pos0=64), dict(paired=0)),
     ("fp32", dict(B=1, Hq=4, Hkv=4, N=256, D=64, dtype=_abi.FP32, causal=1),
      dict(kernel=1, waves=1, heads=1, rows=64, query_blocks=4, paired=0, workgroups=16)),
-    # fp8 inputs pair the same way (GQA 4:1, 19 blocks of 64 rows)
-    ("fp8_causal", dict(B=2, Hq=64, Hkv=16, N=1200, D=128, rope=False, causal=1, kv_fp8=1, q_fp8=1,
+    # fp8 inputs pair the same way (GQA 4:1, 15 blocks of 64 rows)
+    ("fp8_causal", dict(B=2, Hq=64, Hkv=16, N=950, D=128, rope=False, causal=1, kv_fp8=1, q_fp8=1,
                         q_scale=1.0, k_scale=1.0, v_scale=1.0),
-     dict(kernel=3, waves=8, heads=4, rows=64, query_blocks=19, paired=1, workgroups=320)),
+     dict(kernel=3, waves=8, heads=4, rows=64, query_blocks=15, paired=1, workgroups=256)),
     ("no_queries", dict(B=1, Hq=4, Hkv=4, N=256, D=64, Nq=0),
      dict(kernel=0, waves=0, workgroups=0)),
 ]

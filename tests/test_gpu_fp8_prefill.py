@@ -47,10 +47,10 @@ CASES = {
 # Paired workgroups (block n_qblk - 1 - j, then block j, in one stream):
 # shapes with at least 256 pairs.
 PAIRED = {
-    # GQA 4:1, 19 blocks of 64 rows (odd: the middle block alone), ragged tail
-    "paired_gqa_causal_odd_ragged_d128": (2, 64, 16, 1200, 1200, 128, dict(causal=True)),
-    # ALiBi + window, MHA, 9 blocks of 256 rows
-    "paired_alibi_window_d128": (2, 32, 32, 2200, 2200, 128, dict(causal=True, window=300, alibi=True)),
+    # GQA 4:1, 15 blocks of 64 rows (odd: the middle block alone), ragged tail
+    "paired_gqa_causal_odd_ragged_d128": (2, 64, 16, 950, 950, 128, dict(causal=True)),
+    # ALiBi + window, MHA, 15 blocks of 256 rows, ragged tail
+    "paired_alibi_window_d128": (2, 32, 32, 3600, 3600, 128, dict(causal=True, window=300, alibi=True)),
     # d = 64, queries after the keys
     "paired_after_keys_d64": (4, 32, 32, 1000, 1100, 64, dict(causal=True, q_pos0=100)),
 }

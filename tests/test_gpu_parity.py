@@ -225,20 +225,20 @@ def test_full_size_elementwise(name):
 # Paired workgroups: causal dense launches with enough query blocks run block
 # n_qblk - 1 - j and block j in one workgroup, as one stream of key tiles.
 PAIRED = [
-    # odd block count (19: the middle block runs alone) and a ragged last block
-    ("paired_odd_ragged_rope", "llama3_8b_rope_causal_n4096", dict(B=2, Hq=64, Hkv=16, Nq=1200, Nk=1200)),
+    # odd block count (15: the middle block runs alone) and a ragged last block
+    ("paired_odd_ragged_rope", "llama3_8b_rope_causal_n4096", dict(B=2, Hq=64, Hkv=16, Nq=950, Nk=950)),
     # one q-head per workgroup (no GQA), 256-row blocks, d = 64, no RoPE
     ("paired_mha_d64", "llama3_8b_rope_causal_n4096",
      dict(B=4, Hq=32, Hkv=32, Nq=1024, Nk=1024, D=64, rope_theta=None)),
     # queries after the keys: every block sees 200 keys beyond its diagonal
     ("paired_queries_after_keys", "llama3_8b_rope_causal_n4096",
      dict(B=2, Hq=64, Hkv=16, Nq=1000, Nk=1200, q_pos0=200, rope_theta=1e4)),
-    # causal window with RoPE: each block streams its own window's tiles; 18 blocks, ragged tail
+    # causal window with RoPE: each block streams its own window's tiles; 15 blocks, ragged tail
     ("paired_rope_window", "llama3_8b_rope_causal_n4096",
-     dict(B=2, Hq=64, Hkv=16, Nq=1100, Nk=1100, window=500)),
-    # ALiBi (tiles visited from the diagonal down) + window, 9 blocks of 256 rows, ragged tail
+     dict(B=2, Hq=64, Hkv=16, Nq=915, Nk=915, window=200)),
+    # ALiBi (tiles visited from the diagonal down) + window, 15 blocks of 256 rows, ragged tail
     ("paired_alibi_window_odd_ragged", "alibi_causal_window1024_n8192",
-     dict(B=2, Hq=32, Hkv=32, Nq=2200, Nk=2200, window=300)),
+     dict(B=2, Hq=32, Hkv=32, Nq=3600, Nk=3600, window=300)),
     # ALiBi causal, no window, queries after the keys
     ("paired_alibi_after_keys", "alibi_causal_window1024_n8192",
      dict(B=4, Hq=32, Hkv=32, Nq=1000, Nk=1100, window=0, q_pos0=100)),
