@@ -6,8 +6,9 @@ AttnFuse pages ("AttnFuse: A Composable DSL for Compiling Attentions to Fused
 GPU Kernels"): ``fwd`` is the fused forward of "3.3 Runtime Dispatch" with its
 decode fast path, ``decode`` the split-KV path of "4.2 Flash Decoding",
 ``create_block_mask`` builds the CSR BlockMask of "4.3 Block-Sparse
-Attention", ``rope_tables`` the precomputed cos / sin tables of "4.1 Fused
-RoPE", and ``prerotate`` the separate rotation pass that fusion replaces.
+Attention" and ``bigbird_block_mask`` its BigBird instance, ``rope_tables``
+the precomputed cos / sin tables of "4.1 Fused RoPE", and ``prerotate`` the
+separate rotation pass that fusion replaces.
 """
 from __future__ import annotations
 
@@ -185,6 +186,44 @@ def create_block_mask(predicate: Callable, n_qblocks: int, n_kblocks: int, block
         rows.append(rp)
     row_ptr = np.asarray(rows if heads else rows[0], dtype=np.int32)
     return block_mask_from_csr(row_ptr, np.asarray(cols, dtype=np.int32), block_m, block_n, device)
+
+
+def bigbird_block_mask(N: int, block: int, n_window: int = 1, n_global: int = 2,
+                       n_random: int = 3, seed: int = 0, device="cpu",
+                       N_k: Optional[int] = None) -> BlockMask:
+    """BigBird block mask ("4.3 Block-Sparse Attention", BigBird reference [9]).
+
+    Square ``block`` x ``block`` tiles over ``N`` queries and ``N_k`` keys
+    (default ``N``).  Query block ``i`` attends to the key blocks of its
+    neighbourhood ``i - n_window .. i + n_window`` (clipped), to the first
+    ``n_global`` key blocks, and to ``n_random`` more key blocks drawn without
+    replacement from the ones not already active, with
+    ``numpy.random.default_rng(seed)`` consumed query block by query block in
+    increasing order.  Each row's key blocks are stored in increasing order.
+    The mask is shared by every batch and head; tail blocks of ragged ``N``
+    are whole blocks (the kernel masks the positions past the end).
+    """
+    if N < 0 or block <= 0 or min(n_window, n_global, n_random) < 0:
+        raise ValueError("bigbird_block_mask: N >= 0, block > 0 and non-negative counts required")
+    nk = N if N_k is None else N_k
+    nqb = -(-N // block)
+    nkb = -(-nk // block)
+    rng = np.random.default_rng(seed)
+    row_ptr = np.zeros(nqb + 1, dtype=np.int32)
+    cols = []
+    for i in range(nqb):
+        active = np.zeros(nkb, dtype=bool)
+        active[max(0, i - n_window):min(nkb, i + n_window + 1)] = True
+        active[:min(n_global, nkb)] = True
+        free = np.flatnonzero(~active)
+        take = min(n_random, free.size)
+        if take:
+            active[rng.choice(free, size=take, replace=False)] = True
+        row = np.flatnonzero(active)
+        cols.append(row)
+        row_ptr[i + 1] = row_ptr[i] + row.size
+    col_idx = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, dtype=np.int32)
+    return block_mask_from_csr(row_ptr, col_idx, block, block, device)
 
 
 # ----------------------------------------------------------------------------
