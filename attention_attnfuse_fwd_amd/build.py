@@ -30,6 +30,19 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The two- and four-wave forward instances run one
+# wave per SIMD, where the register allocator otherwise parks the MFMA
+# accumulators in AGPRs and copies every score out of them (about a hundred
+# extra moves per key tile); forcing the VGPR form of the MFMAs keeps them
+# under 256 VGPRs without spills.  The eight-wave instances use no AGPRs
+# either way, and the backward kernels would spill under it, so the flag
+# stays on these units only.
+EXTRA_FLAGS = {
+    f"fwd_bf16_d{d}_nw{nw}.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+    for d in (64, 128) for nw in (2, 4)
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -65,7 +78,8 @@ def kernel_resources(remarks: str) -> dict:
 
 def _compile(hipcc: str, src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []),
+           "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
