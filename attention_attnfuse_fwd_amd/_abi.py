@@ -57,6 +57,7 @@ class FwdPlanInfo(ctypes.Structure):
         ("query_blocks", ctypes.c_int32),
         ("paired", ctypes.c_int32),
         ("workgroups", ctypes.c_int64),
+        ("chain", ctypes.c_int32),
     ]
 
 
@@ -109,6 +110,7 @@ class VariantDesc(ctypes.Structure):
         ("v_scale", ctypes.c_float),
         ("q_fp8", ctypes.c_int32),
         ("q_scale", ctypes.c_float),
+        ("tile_chain", ctypes.c_int32),
     ]
 
     @classmethod

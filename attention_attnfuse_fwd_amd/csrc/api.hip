@@ -136,6 +136,7 @@ AttnParams base_params(const void* q, const void* k, const void* v, void* out,
   p.bs_head_stride = d->bs_head_stride;
   p.bs_nnz = d->bs_nnz;
   p.lse = d->lse;
+  p.chain = 1;
   return p;
 }
 
@@ -193,6 +194,38 @@ long long pair_blocks(AttnParams& p, const attnfuse_variant_desc* d, int rows, b
   return pairs;
 }
 
+// Block-sparse chains: on the two- and four-wave kernels (one wave per
+// SIMD, start-up and drain not hidden by a partner wave) a workgroup runs
+// `chain` consecutive query blocks of its head as one stream of key tiles,
+// when its rows are one CSR block row and there is no additive bias.  The
+// library's choice: as many blocks per chain as the single blocks would take
+// rounds of the CUs (workgroups per CU from the kernel's LDS: four K and four
+// V slots of 64 keys plus, with RoPE, the table slot), at most 8.  E.g. the
+// BigBird workload (B2 H16 N4096, 64-row blocks, two waves, 72 KB of LDS):
+// 2048 blocks on 512 workgroup slots, chains of 4.  Sets p.chain and the
+// grid; returns a status (a requested chain where none can run is
+// unsupported).
+int chain_blocks(AttnParams& p, const attnfuse_variant_desc* d, int NW, int rows, bool sparse,
+                 bool rope, long long& grid) {
+  constexpr long long kCUs = 256;             // MI355X compute units
+  constexpr long long kLdsPerCU = 160 * 1024;  // bytes
+  const bool can = sparse && NW < 8 && d->bias == nullptr && d->bs_block_m == rows;
+  // (A block mask with no keys launches the dense kernel: nothing to chain.)
+  if (d->tile_chain > 1 && !can && !(d->bs_row_ptr && !sparse)) return ATTNFUSE_ERR_UNSUPPORTED;
+  if (!can || d->tile_chain == 1) return ATTNFUSE_OK;
+  long long c = d->tile_chain;
+  if (c == 0) {
+    const long long lds = 2LL * 4 * 128 * d->D + (rope ? (d->D / 16) * 2048LL : 0);
+    const long long slots = kCUs * std::max(1LL, kLdsPerCU / lds);
+    c = std::min(8LL, grid / slots);
+  }
+  c = std::min(c, (long long)p.n_qblk);
+  if (c <= 1) return ATTNFUSE_OK;
+  p.chain = (int)c;
+  grid = (long long)p.n_units * ((p.n_qblk + c - 1) / c);
+  return ATTNFUSE_OK;
+}
+
 // Launch choice of attnfuse_fwd.
 struct FwdPlan {
   int kind = ATTNFUSE_PLAN_NONE;
@@ -209,6 +242,7 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
   int st = validate_common(desc);
   if (st != ATTNFUSE_OK) return st;
   const attnfuse_variant_desc* d = desc;
+  if (d->tile_chain < 0) return ATTNFUSE_ERR_INVALID;
   // fp8 inputs: Q, K and V together, with neither RoPE nor an additive bias.
   const bool fp8 = d->kv_fp8 || d->q_fp8;
   if (fp8) {
@@ -250,6 +284,7 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
     p.n_qblk = (d->Nq + 63) / 64;
     const long long grid = (long long)d->B * d->Hq * p.n_qblk;
     if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
+    if (d->tile_chain > 1) return ATTNFUSE_ERR_UNSUPPORTED;
     f = FwdPlan{ATTNFUSE_PLAN_FP32, 1, 1, 64, grid};
     return ATTNFUSE_OK;
   }
@@ -275,6 +310,7 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
     long long grid = (long long)p.n_units * p.n_qblk;
     if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
     grid = pair_blocks(p, d, 32 * (8 / hp), true, use_sparse, grid);
+    if (d->tile_chain > 1) return ATTNFUSE_ERR_UNSUPPORTED;
     // Products of codes: both dequantisation scales join the score scale.
     const double sc = d->scale > 0.f ? (double)d->scale : 1.0 / sqrt((double)d->D);
     p.scale_log2 = (float)(sc * 1.4426950408889634 * (double)d->q_scale * (double)d->k_scale);
@@ -345,6 +381,8 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
   long long grid = (long long)p.n_units * p.n_qblk;
   if (grid >= (1LL << 31)) return ATTNFUSE_ERR_UNSUPPORTED;
   grid = pair_blocks(p, d, 32 * RB, NW == 8, use_sparse, grid);
+  st = chain_blocks(p, d, NW, 32 * RB, use_sparse, rope, grid);
+  if (st != ATTNFUSE_OK) return st;
   f = FwdPlan{ATTNFUSE_PLAN_BF16, NW, hp, 32 * RB, grid};
   return ATTNFUSE_OK;
 }
@@ -410,6 +448,7 @@ int attnfuse_fwd_plan(const attnfuse_variant_desc* desc, attnfuse_fwd_plan_info*
     info->query_blocks = p.n_qblk;
     info->paired = p.pair;
     info->workgroups = f.grid;
+    info->chain = p.chain;
   }
   return ATTNFUSE_OK;
 }

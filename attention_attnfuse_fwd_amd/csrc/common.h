@@ -67,6 +67,10 @@ struct AttnParams {
   // Paired workgroups (causal, dense, eight waves): workgroup j of a unit runs
   // query block n_qblk - 1 - j and then block j, as one stream of key tiles.
   int pair;
+  // Chained workgroups (block-sparse, two- and four-wave kernels): workgroup
+  // j of a unit runs query blocks chain * j .. chain * j + chain - 1 (those
+  // that exist) as one stream of key tiles; 1 = one block per workgroup.
+  int chain;
   // split-KV decode
   int splits, chunk, n_hgrp;
   float* ws;

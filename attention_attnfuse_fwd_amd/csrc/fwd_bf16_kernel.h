@@ -188,10 +188,13 @@ fwd_bf16_kernel(const AttnParams p) {
   const int rows_wg = 32 * RB;
   const int unit = blockIdx.x % p.n_units;
   const int qrank = blockIdx.x / p.n_units;
-  const int qblk = p.longest_first ? (p.n_qblk - 1 - qrank) : qrank;
   // A paired workgroup (see AttnParams::pair) runs a second query block,
-  // qrank, after qblk (-1: none).
+  // qrank, after qblk (-1: none).  A chained workgroup (block-sparse, two or
+  // four waves, see AttnParams::chain) runs p.chain consecutive query blocks
+  // of its head, from qblk on.
   constexpr bool PAIRABLE = PP && !SPARSE && !BIAS;
+  constexpr bool CHAIN = SPARSE && !PP && !BIAS;
+  const int qblk = p.longest_first ? (p.n_qblk - 1 - qrank) : (CHAIN ? qrank * p.chain : qrank);
   const int qblk2 = (PAIRABLE && p.pair && qrank < qblk) ? qrank : -1;
   const int n_hg = p.G / hp;
   const int hg = unit % n_hg;
@@ -228,13 +231,21 @@ fwd_bf16_kernel(const AttnParams p) {
     nt = (j_hi >= j_lo) ? (j_hi / 64 - tb + 1) : 0;
   };
   int n_tiles, t_begin = 0, s_begin = 0, tpb = 1;
+  // Chained blocks: the CSR rows of consecutive query blocks are adjacent,
+  // so their key lists form one stream; block c's tiles end at stream tile
+  // seg_end(c).  (A workgroup's rows must be one CSR block row.)
+  int n_chain = 1, qbs0 = 0;
+  const int* rp = nullptr;
+  long long rp_a = 0;
   if (SPARSE) {
-    const int* rp = p.row_ptr + (p.bs_head_stride ? (long long)h * p.bs_head_stride : 0);
-    const int qbs = r0_wg / p.bm;
+    rp = p.row_ptr + (p.bs_head_stride ? (long long)h * p.bs_head_stride : 0);
+    qbs0 = r0_wg / p.bm;
+    if (CHAIN && p.bm == rows_wg) n_chain = max(1, min(p.chain, p.n_qblk - qblk));
     const long long nnz = p.bs_nnz;
-    const long long a = min(max((long long)rp[qbs], 0LL), nnz);
-    const long long e = min(max((long long)rp[qbs + 1], a), nnz);
+    const long long a = min(max((long long)rp[qbs0], 0LL), nnz);
+    const long long e = min(max((long long)rp[qbs0 + n_chain], a), nnz);
     s_begin = (int)a;
+    rp_a = a;
     tpb = p.bn / 64;
     n_tiles = (int)(e - a) * tpb;
   } else {
@@ -269,6 +280,13 @@ fwd_bf16_kernel(const AttnParams p) {
     const bool s2 = t >= seg_split;  // (rev: each block's tiles from its last key tile down)
     const int loc = s2 ? t - seg_split : t;
     return ((s2 ? t_begin2 : t_begin) + (rev ? (s2 ? n_second : n_first) - 1 - loc : loc)) * 64;
+  };
+
+  // End of chained block c's tiles in the stream, kept within [lo, n_tiles]
+  // (a malformed row_ptr gives wrong numbers, never a bad access).
+  auto seg_end = [&](int c, int lo) -> int {
+    const long long e = min(max((long long)rp[qbs0 + c + 1], rp_a), p.bs_nnz);
+    return min(max((int)(e - rp_a) * tpb, lo), n_tiles);
   };
 
   const int Nk = p.Nk, band_lo = p.band_lo, band_hi = p.band_hi;
@@ -796,10 +814,10 @@ fwd_bf16_kernel(const AttnParams p) {
     to_frags(pw, pf);
   };
   auto first_tile = [&]() { first_tile_at(0, pfa); };
-  // Paired workgroups, at the switch between the blocks: the first block's
-  // output, O^T / l straight from registers in 8-byte pieces, and its lse,
-  // then the second block's rows (its Q loads can be issued after this) ...
-  auto finish_first_block = [&]() {
+  // Paired and chained workgroups, at the switch between two blocks: the
+  // finished block's output, O^T / l straight from registers in 8-byte
+  // pieces, and its lse ...
+  auto store_block_regs = [&]() {
     const int i_a = i;
     const float l_a = ol[0], m_a = m_run;
     const float inv = l_a > 0.f ? p.v_scale / l_a : 0.f;
@@ -818,15 +836,23 @@ fwd_bf16_kernel(const AttnParams p) {
     if (i_a < p.Nq && p.lse && lh == 0)
       p.lse[((long long)b * p.Hq + h) * p.Nq + i_a] =
           l_a > 0.f ? (m_a + __builtin_log2f(l_a)) * kLn2 : -INFINITY;
-    set_rows(qblk2);
   };
-  // ... and a fresh softmax state for the second block.
-  auto start_second_block = [&]() {
+  // ... and a fresh softmax state for the next block.
+  auto reset_softmax = [&]() {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     ol = f32x16{};
     m_run = -INFINITY;
     minit = f32x16{};
+  };
+  // A paired workgroup's switch: then the second block's rows (its Q loads
+  // can be issued after this) and masks.
+  auto finish_first_block = [&]() {
+    store_block_regs();
+    set_rows(qblk2);
+  };
+  auto start_second_block = [&]() {
+    reset_softmax();
     set_masks(n_second, t_begin2);
   };
   // A paired workgroup runs two query blocks over one stream of key tiles.
@@ -1214,7 +1240,6 @@ fwd_bf16_kernel(const AttnParams p) {
       if (!m_first) __syncthreads();
       ATTNFUSE_RUN_STEPS(step, seg_split, n, true)
     }
-#undef ATTNFUSE_RUN_STEPS
     // Same barrier count in both halves: the first half's closing barrier
     // matches the second half's extra vector cluster.
     if (n > 0 && m_first) __syncthreads();
@@ -1276,7 +1301,9 @@ fwd_bf16_kernel(const AttnParams p) {
       for (int j = slot * IPDB; j < (slot + 1) * IPDB; ++j)
         if (j < TPK * NKW_HI + NVW && 2 * nkw + j < grp) dma_item(g, 2 * nkw + j);
     };
-    auto iteration = [&](int t, const bf16x8 (&pf)[4], bf16x8 (&pf_next)[4]) {
+    // has_s = false: S(t+1) belongs to the next chained block (its Q is not
+    // loaded yet), so its softmax is not taken.
+    auto iteration = [&](int t, const bf16x8 (&pf)[4], bf16x8 (&pf_next)[4], bool has_s) {
       wait_group();
       const Group g = make_group(t + 4, t + 3, t + 3);
 
@@ -1381,18 +1408,34 @@ fwd_bf16_kernel(const AttnParams p) {
       for (int x = (NSB - 1) * XPB; x < NSB * XPB; ++x) exp_stage2(sn, x, ex[x]);
   #pragma unroll
       for (int x = (NSB - 2) * XPB; x < NSB * XPB; ++x) pw[x] = exp_stage3(x, ex[x]);
-      finish_tile(sn, -neg_m(), pw);
+      if (has_s) finish_tile(sn, -neg_m(), pw);
       to_frags(pw, pf_next);
       __syncthreads();
     };
-    // Unrolled by two so that the P tiles swap roles without copies.
-    int t = 0;
-    for (; t + 1 < n; t += 2) {
-      iteration(t, pfa, pfb);
-      iteration(t + 1, pfb, pfa);
+    // Steps unrolled by two so that the P tiles swap roles without copies,
+    // one block of a chain at a time.  At a switch: the finished block's
+    // output from registers, the next block's rows, Q (loaded and rotated)
+    // and softmax state, then S of its first tile from that tile's ring
+    // slot (K' is in place: tile u is rotated in iteration u - 2, and its
+    // slot is refilled in iteration u, after the barrier below).
+    int seg0 = 0;
+    for (int c = 0; c < n_chain; ++c) {
+      const bool last_seg = c == n_chain - 1;
+      const int seg1 = last_seg ? n : seg_end(c, seg0);
+      if (c > 0) {
+        store_block_regs();
+        set_rows(qblk + c);
+        load_q_issue();
+        reset_softmax();
+        load_q_finish();
+        if (seg1 > seg0) first_tile_at(seg0, pfa);
+        __syncthreads();
+      }
+      ATTNFUSE_RUN_STEPS(iteration, seg0, seg1, last_seg)
+      seg0 = seg1;
     }
-    if (t < n) iteration(t, pfa, pfb);
   }
+#undef ATTNFUSE_RUN_STEPS
   // No DMA may land in LDS after the workgroup ends, and the epilogue reuses
   // the ring slots: every wave's loads must have landed first.
   vmcnt_wait<0>();

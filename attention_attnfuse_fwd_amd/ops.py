@@ -294,6 +294,13 @@ def _make_desc(q, k, v, out, *, scale, causal, window, rope_theta, q_pos0, k_pos
     return d
 
 
+def _set_tile(d, tile):
+    """``tile = (waves, heads)`` or ``(waves, heads, chain)``; 0 = the library's choice."""
+    d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
+    if len(tile) > 2:
+        d.tile_chain = int(tile[2])
+
+
 def _check_inputs(q, k, v):
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
@@ -321,7 +328,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
 
     A single query row (Nq == 1, bf16, no bias or block mask) takes the split-KV
     decode path, as the pages' runtime dispatch does.  ``tile = (waves, heads)``
-    overrides the library's tile table for the bf16 prefill kernel.  With
+    or ``(waves, heads, chain)`` overrides the library's tile table for the
+    bf16 prefill kernel (0 = the library's choice; ``chain``: query blocks per
+    workgroup of a block-sparse launch on two or four waves).  With
     ``torch.float8_e4m3fn`` q, k and v (E4M3 codes whose rows are
     ``q_scale * code`` etc.) the fp8 prefill runs and the output is bf16.
     """
@@ -359,7 +368,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         d.kv_fp8, d.q_fp8 = 1, 1
         d.q_scale, d.k_scale, d.v_scale = float(q_scale), float(k_scale), float(v_scale)
     if tile is not None:
-        d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
+        _set_tile(d, tile)
     _check(_abi.load().attnfuse_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(d),
                                     _stream(q.device)), "fwd")
     if cacheable:
@@ -376,7 +385,8 @@ def fwd_plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
              scale: Optional[float] = None, tile: Optional[tuple] = None) -> dict:
     """The launch ``fwd`` would make for these arguments (prefill kernels; the
     single-query decode path is not considered): kernel, waves and q-heads per
-    workgroup, query rows per block, blocks per unit, pairing and grid."""
+    workgroup, query rows per block, blocks per unit, pairing, grid and
+    block-sparse chain length."""
     _check_inputs(q, k, v)
     keep = []
     d = _make_desc(q, k, v, q, scale=scale, causal=causal, window=window, rope_theta=rope_theta,
@@ -386,7 +396,7 @@ def fwd_plan(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
         d.kv_fp8, d.q_fp8 = 1, 1
         d.q_scale = d.k_scale = d.v_scale = 1.0  # (scales do not change the launch)
     if tile is not None:
-        d.tile_waves, d.tile_heads = int(tile[0]), int(tile[1])
+        _set_tile(d, tile)
     info = _abi.FwdPlanInfo()
     _check(_abi.load().attnfuse_fwd_plan(ctypes.byref(d), ctypes.byref(info)), "fwd_plan")
     out = {f: getattr(info, f) for f, _ in _abi.FwdPlanInfo._fields_}

@@ -192,6 +192,19 @@ typedef struct attnfuse_variant_desc {
    * 0 = q has desc->dtype. */
   int32_t q_fp8;
   float q_scale;
+
+  /* Block-sparse chains (attnfuse_fwd's bf16 prefill with a block mask on
+   * the two- and four-wave kernels, without additive_bias, when a
+   * workgroup's rows are one CSR block row): tile_chain = consecutive query
+   * blocks of one head per workgroup, streamed as one list of key tiles so
+   * that a workgroup's start-up and drain are paid once per chain ("4.3
+   * Block-Sparse Attention": the work stays proportional to the active
+   * blocks).  0 = the library's choice (chains when the single blocks would
+   * take several rounds of the CUs); 1 = one block per workgroup.  Larger
+   * values than the unit's query blocks act as that count.  Negative values
+   * return ATTNFUSE_ERR_INVALID; a value above 1 where no chain can run
+   * returns ATTNFUSE_ERR_UNSUPPORTED.  Ignored by the other entry points. */
+  int32_t tile_chain;
 } attnfuse_variant_desc;
 
 /* Fused attention forward: out = attention(q, k, v) under `desc`.
@@ -210,7 +223,8 @@ int attnfuse_fwd(const void* q, const void* k, const void* v, void* out,
  * blocks per (batch, kv-head, head group) unit; paired: 1 when every
  * workgroup of a causal dense launch runs two query blocks, block
  * query_blocks - 1 - j and block j, so that all workgroups stream about the
- * same number of key tiles; workgroups: the grid.  Validates `desc` exactly
+ * same number of key tiles; workgroups: the grid; chain: query blocks per
+ * workgroup of a block-sparse launch (tile_chain above), else 1.  Validates `desc` exactly
  * as attnfuse_fwd does, except for the data pointers, which are not
  * examined; returns the status attnfuse_fwd would return for valid
  * pointers.  `info` is host memory owned by the caller; on an error it is
@@ -227,6 +241,7 @@ typedef struct attnfuse_fwd_plan_info {
   int32_t query_blocks;
   int32_t paired;
   int64_t workgroups;
+  int32_t chain;
 } attnfuse_fwd_plan_info;
 
 int attnfuse_fwd_plan(const attnfuse_variant_desc* desc, attnfuse_fwd_plan_info* info);

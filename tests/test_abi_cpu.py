@@ -368,6 +368,8 @@ def test_plan_struct_layout_matches_c(tmp_path):
 # Hkv=8, N=4096, d=128): four q-heads of a group per eight-wave workgroup,
 # 64-row blocks, 8 units x 64 blocks; causal without a window pairs block
 # 63 - j with block j in 256 workgroups.
+_BS64 = dict(bs_row_ptr=FAKE.value, bs_col_idx=FAKE.value, bs_block_m=64, bs_block_n=64, bs_nnz=1)
+
 PLAN_CASES = [
     ("llama8b_causal", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1),
      dict(kernel=2, waves=8, heads=4, rows=64, query_blocks=64, paired=1, workgroups=256)),
@@ -414,6 +416,24 @@ PLAN_CASES = [
      dict(kernel=3, waves=8, heads=4, rows=64, query_blocks=15, paired=1, workgroups=256)),
     ("no_queries", dict(B=1, Hq=4, Hkv=4, N=256, D=64, Nq=0),
      dict(kernel=0, waves=0, workgroups=0)),
+    # BigBird (B2 H16 N4096 D64, 64x64 blocks): two waves, 2048 blocks on 512
+    # workgroup slots (two 72 KB workgroups per CU) -> chains of 4
+    ("bigbird_chain", dict(B=2, Hq=16, Hkv=16, N=4096, D=64, **_BS64),
+     dict(kernel=2, waves=2, heads=1, rows=64, query_blocks=64, paired=0, chain=4, workgroups=512)),
+    # half as many blocks: chains of 2
+    ("bigbird_chain_2", dict(B=1, Hq=16, Hkv=16, N=4096, D=64, **_BS64), dict(chain=2, workgroups=512)),
+    # one round of single blocks: no chain
+    ("bigbird_small", dict(B=1, Hq=4, Hkv=4, N=1024, D=64, **_BS64), dict(chain=1, workgroups=64)),
+    # the caller's chain length; 16 blocks, chains of 3 (the last holds one)
+    ("bigbird_chain_3", dict(B=1, Hq=4, Hkv=4, N=1000, D=64, tile_chain=3, **_BS64),
+     dict(chain=3, query_blocks=16, workgroups=4 * 6)),
+    # longer than the blocks: one chain per unit
+    ("bigbird_chain_long", dict(B=1, Hq=2, Hkv=2, N=300, D=64, tile_chain=50, **_BS64),
+     dict(chain=5, workgroups=2)),
+    # dense launches and eight-wave block-sparse ones run single blocks
+    ("dense_chain_1", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, tile_chain=1), dict(chain=1, workgroups=512)),
+    ("gqa_bigbird_eight_waves", dict(B=1, Hq=16, Hkv=4, N=4096, D=64, **_BS64),
+     dict(waves=8, heads=4, chain=1)),
 ]
 
 
@@ -425,6 +445,28 @@ def test_fwd_plan(lib, name, kw, want):
     assert st == _abi.OK
     for f, v in want.items():
         assert info[f] == v, (f, info)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tile_chain=-1, **_BS64), _abi.ERR_INVALID),
+    # chains need a block mask, two or four waves, one CSR block row per workgroup, no bias
+    (dict(tile_chain=2), _abi.ERR_UNSUPPORTED),
+    (dict(tile_chain=2, tile_waves=8, tile_heads=4, **_BS64), _abi.ERR_UNSUPPORTED),
+    (dict(tile_chain=2, tile_waves=2, tile_heads=1, **dict(_BS64, bs_block_m=128)), _abi.ERR_UNSUPPORTED),
+    (dict(tile_chain=2, **dict(_BS64, bs_block_m=128)), _abi.OK),  # four waves: 128 rows
+    (dict(tile_chain=2, bias=FAKE.value, bias_stride=(0, 0, 64, 1), **_BS64), _abi.ERR_UNSUPPORTED),
+    (dict(tile_chain=2, dtype=_abi.FP32, **_BS64), _abi.ERR_UNSUPPORTED),
+    (dict(tile_chain=1, dtype=_abi.FP32, **_BS64), _abi.OK),
+    (dict(tile_chain=2, **_BS64), _abi.OK),
+])
+def test_fwd_plan_chain_choices(lib, kw, status):
+    d = _shape_desc(1, 4, 4, 256, 64, rope=False, **kw)
+    st, info = _plan(lib, d)
+    assert st == status, (kw, st)
+    if st != _abi.OK:
+        assert _fwd(lib, d) == st  # rejected before any HIP call (never launched here)
+    elif kw.get("dtype") != _abi.FP32:
+        assert info["chain"] == kw["tile_chain"]
 
 
 def test_fwd_plan_status_matches_fwd(lib):

@@ -260,6 +260,85 @@ def test_paired_workgroups_elementwise(name, base, over):
     check_lse(lse, rlse, 2e-2, f"{name} (all {lse.size} rows)")
 
 
+# Chained workgroups: block-sparse launches on two or four waves run `chain`
+# consecutive query blocks of one head as one stream of key tiles (the
+# full-size BigBird workload above runs the library's chains of 4).  Besides
+# the oracle, the same launch with single blocks must give the same bits:
+# chaining changes the grid, not the arithmetic of a block.
+CHAINED = [
+    # (name, base workload, overrides, tile = (waves, heads, chain))
+    # 16 blocks in chains of 3 (the last holds one), ragged tail
+    ("chain3_bigbird_ragged", "bigbird_rope_n4096", dict(B=1, Hq=2, Hkv=2, Nq=1000, Nk=1000), (0, 0, 3)),
+    # causal band inside the chains, D = 128, ALiBi, queries after the keys
+    ("chain4_causal_alibi_d128", "bigbird_rope_n4096",
+     dict(B=1, Hq=4, Hkv=4, Nq=900, Nk=1000, D=128, causal=True, alibi=True, q_pos0=100), (0, 0, 4)),
+    # four waves on 128-row blocks, GQA (one q-head per workgroup)
+    ("chain2_four_waves_gqa", "bigbird_rope_n4096",
+     dict(B=1, Hq=4, Hkv=2, Nq=1100, Nk=1100, bigbird_block=128), (4, 1, 2)),
+    # window, no RoPE, two batches
+    ("chain5_window_norope", "bigbird_rope_n4096",
+     dict(B=2, Hq=2, Hkv=2, Nq=640, Nk=640, window=100, rope_theta=None), (0, 0, 5)),
+]
+
+
+@pytest.mark.parametrize("name,base,over,tile", CHAINED, ids=[c[0] for c in CHAINED])
+def test_chained_workgroups_elementwise(name, base, over, tile):
+    w = W[base].with_(**over)
+    inp = workloads.make_inputs(w)
+    log(f"case {name}: {w}, tile {tile}")
+    q, k, v = dev_inputs(inp)
+    plan = af.fwd_plan(q, k, v, tile=tile, **_gpu_kw(w, inp))
+    log(f"plan {plan}")
+    assert plan["kernel"] == "bf16" and plan["waves"] < 8, plan
+    assert plan["chain"] == min(tile[2], plan["query_blocks"]) > 1, plan
+    out, lse = _run(w, inp, tile=tile)
+    ref, rlse = oracle_all_heads(inp.q, inp.k, inp.v, w.B, w.Hq, **_oracle_kw(w, inp))
+    check_close(out, ref, w.dtype, f"{name} (all {out.size} elements)")
+    check_lse(lse, rlse, 2e-2, f"{name} (all {lse.size} rows)")
+    out1, lse1 = _run(w, inp, tile=(tile[0], tile[1], 1))
+    np.testing.assert_array_equal(out, out1)
+    np.testing.assert_array_equal(lse, lse1)
+
+
+@pytest.mark.parametrize("chain", [2, 3, 6])
+def test_chained_per_head_masks_with_empty_blocks(chain):
+    # Per-head masks (one q-head per workgroup) with empty query blocks at the
+    # start of a chain, inside it, at its end, and a head with no blocks at all.
+    rng = np.random.default_rng(21)
+    B, H, N, D, bs = 1, 4, 384, 64, 64
+    (qb, q), (kb, k), (vb, v) = (workloads.normal_bf16((B, H, N, D), rng) for _ in range(3))
+    nb = N // bs
+    rp, ci = workloads.random_csr(nb, nb, 0.5, seed=5, n_heads=H)
+    rows = [[list(ci[rp[h, r]:rp[h, r + 1]]) or [r] for r in range(nb)] for h in range(H)]
+    rows[0][0] = []
+    rows[1][2] = rows[1][3] = []
+    rows[2][nb - 1] = []
+    rows[3] = [[] for _ in range(nb)]
+    flat, rps = [], []
+    for h in range(H):
+        r = [len(flat)]
+        for rr in rows[h]:
+            flat.extend(rr)
+            r.append(len(flat))
+        rps.append(r)
+    rp = np.asarray(rps, dtype=np.int32)
+    ci = np.asarray(flat, dtype=np.int32)
+    mask = af.block_mask_from_csr(rp, ci, bs, bs, "cuda")
+    qd, kd, vd = (to_dev(x, "bf16") for x in (qb, kb, vb))
+    plan = af.fwd_plan(qd, kd, vd, block_mask=mask, rope_theta=1e4, tile=(0, 0, chain))
+    log(f"case chained per-head masks, chain {chain}, nnz={ci.size}, plan {plan}")
+    assert plan["chain"] == chain and plan["waves"] == 2, plan
+    out, lse = af.fwd(qd, kd, vd, return_lse=True, block_mask=mask, rope_theta=1e4, tile=(0, 0, chain))
+    ref, rlse = oracle.attention(q, k, v, rope_theta=1e4, block_mask=(rp, ci, bs, bs))
+    out, lse = host(out), host(lse)
+    check_close(out, ref, "bf16", f"chained per-head masks, chain {chain}")
+    check_lse(lse, rlse, 2e-2, f"chained per-head masks, chain {chain}")
+    for h, r in ((0, 0), (1, 2), (1, 3), (2, nb - 1)):
+        assert np.all(out[0, h, r * bs:(r + 1) * bs] == 0.0)
+        assert np.all(np.isneginf(lse[0, h, r * bs:(r + 1) * bs]))
+    assert np.all(out[0, 3] == 0.0) and np.all(np.isneginf(lse[0, 3]))
+
+
 # ----------------------------------------------------------------------------
 # Decode (split-KV + LSE combine)
 # ----------------------------------------------------------------------------
