@@ -194,15 +194,15 @@ long long pair_blocks(AttnParams& p, const attnfuse_variant_desc* d, int rows, b
   return pairs;
 }
 
-// Block-sparse chains: on the two- and four-wave kernels (one wave per
+// Block-sparse chains: on the two- and four-wave kernels (few waves per
 // SIMD, start-up and drain not hidden by a partner wave) a workgroup runs
 // `chain` consecutive query blocks of its head as one stream of key tiles,
 // when its rows are one CSR block row and there is no additive bias.  The
 // library's choice: as many blocks per chain as the single blocks would take
-// rounds of the CUs (workgroups per CU from the kernel's LDS: four K and four
-// V slots of 64 keys plus, with RoPE, the table slot), at most 8.  E.g. the
-// BigBird workload (B2 H16 N4096, 64-row blocks, two waves, 72 KB of LDS):
-// 2048 blocks on 512 workgroup slots, chains of 4.  Sets p.chain and the
+// rounds of the CUs (workgroups per CU from the kernel's LDS), at most 8.
+// E.g. the BigBird workload (B2 H16 N4096, 64-row blocks, two waves, the
+// shallow schedule's 40 KB of LDS): 2048 blocks on 1024 workgroup slots,
+// chains of 2.  Sets p.chain and the
 // grid; returns a status (a requested chain where none can run is
 // unsupported).
 int chain_blocks(AttnParams& p, const attnfuse_variant_desc* d, int NW, int rows, bool sparse,
@@ -215,7 +215,7 @@ int chain_blocks(AttnParams& p, const attnfuse_variant_desc* d, int NW, int rows
   if (!can || d->tile_chain == 1) return ATTNFUSE_OK;
   long long c = d->tile_chain;
   if (c == 0) {
-    const long long lds = 2LL * 4 * 128 * d->D + (rope ? (d->D / 16) * 2048LL : 0);
+    const long long lds = attnfuse::fwd_bf16_lds_bytes(d->D, NW, rope, sparse, d->bias != nullptr);
     const long long slots = kCUs * std::max(1LL, kLdsPerCU / lds);
     c = std::min(8LL, grid / slots);
   }

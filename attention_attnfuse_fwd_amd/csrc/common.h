@@ -30,6 +30,22 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBandInf = 1 << 30;  // "unbounded" band edge in index space
 
 // Kernel parameters (host fills, passed by value).
+// bf16 prefill kernel shapes shared by the kernel and the host's launch
+// model.  The two-wave block-sparse instance at D = 64 (no additive bias)
+// keeps two-slot K and V rings (40 KB of LDS with the RoPE table slot), so
+// four workgroups, two waves per SIMD, share a CU; the other instances keep
+// four-slot rings.
+constexpr bool fwd_bf16_shallow(int D, int NW, bool sparse, bool bias) {
+  return D == 64 && NW == 2 && sparse && !bias;
+}
+// LDS bytes of a bf16 prefill workgroup (not the fp8 instances): K and V
+// rings of 64-key slots, the RoPE table slot, and for eight waves one more
+// Q staging area.
+constexpr int fwd_bf16_lds_bytes(int D, int NW, bool rope, bool sparse, bool bias) {
+  return 2 * (fwd_bf16_shallow(D, NW, sparse, bias) ? 2 : 4) * 128 * D + (rope ? (D / 16) * 2048 : 0) +
+         (NW == 8 ? 128 * D : 0);
+}
+
 struct AttnParams {
   const void* q;
   const void* k;

@@ -46,9 +46,9 @@ namespace attnfuse {
 // reads are free of bank conflicts; a DMA instruction fills 1 KiB of
 // consecutive LDS, which the swizzle turns into a permutation of the chunks
 // the lanes fetch.
-template <int D>
+template <int D, int R = 4>
 struct TileLds {
-  static constexpr int RING = 4;
+  static constexpr int RING = R;
   static constexpr int KSLOT = 128 * D;     // one K slot
   static constexpr int KHI = 64 * D;        // offset of the high halves in a K slot
   static constexpr int VSLOT = 128 * D;     // one V slot
@@ -146,7 +146,9 @@ __device__ __forceinline__ constexpr int k8swz(int j) {
 template <int D, int NW, bool ROPE, bool SCOREMOD, bool SPARSE, bool BIAS, bool FP8 = false>
 __global__ void __launch_bounds__(NW * 64)
 fwd_bf16_kernel(const AttnParams p) {
-  using L = TileLds<D>;
+  // Two-slot rings for the shallow schedule (see fwd_bf16_shallow).
+  constexpr bool SHALLOW = !FP8 && fwd_bf16_shallow(D, NW, SPARSE, BIAS);
+  using L = TileLds<D, SHALLOW ? 2 : 4>;
   using L8 = Fp8Lds<D>;
   static_assert(!FP8 || (NW == 8 && !ROPE && !BIAS), "fp8 instances: eight waves, no RoPE, no bias");
   constexpr int NKK = D / 16;  // MFMA k-steps over the head dim
@@ -160,6 +162,8 @@ fwd_bf16_kernel(const AttnParams p) {
   // The epilogue stages 32 rows of 2 * D + 16 bytes per wave.
   constexpr int LDS_EPI = NW * 32 * (2 * D + 16);
   constexpr int LDS_BYTES = FP8 ? (L8::BYTES > LDS_EPI ? L8::BYTES : LDS_EPI) : LDS_BF16;
+  static_assert(FP8 || LDS_BYTES == fwd_bf16_lds_bytes(D, NW, ROPE, SPARSE, BIAS), "host LDS model");
+  static_assert(LDS_EPI <= LDS_BF16, "the epilogue staging fits in the rings");
   // DMA instructions per wave and tile.  V is spread evenly; K pairs may not
   // be (D = 64 with 8 waves: waves 0..3 take one pair each).
   static_assert(L::NVI % NW == 0, "V instructions must spread evenly over the waves");
@@ -406,7 +410,7 @@ fwd_bf16_kernel(const AttnParams p) {
   // A whole group at once (prologue); with_v = false issues the K part only,
   // with_t = false skips the table part.
   constexpr int GRP_MAX = (2 + TPK) * NKW_HI + NVW;
-  auto issue_group = [&](int uk, int ut, int uv, bool with_t, bool with_v) {
+  auto issue_group = [&](int uk, int ut, int uv, bool with_t, bool with_v) __attribute__((always_inline)) {
     const Group g = make_group(uk, ut, uv);
 #pragma unroll
     for (int i = 0; i < GRP_MAX; ++i) {
@@ -1243,6 +1247,134 @@ fwd_bf16_kernel(const AttnParams p) {
     // Same barrier count in both halves: the first half's closing barrier
     // matches the second half's extra vector cluster.
     if (n > 0 && m_first) __syncthreads();
+  } else if constexpr (SHALLOW) {
+    // ---- shallow schedule: two-slot rings; four workgroups share a CU, so
+    // each SIMD runs two waves of different workgroups ----
+    // Iteration t: wait for the loads of iteration t-1 (V(t), K(t+1) and
+    // its table entries); load K(t+2) into K(t)'s slot and V(t+1) into
+    // V(t-1)'s (both last read before the previous barrier); O^T += V^T P^T
+    // for tile t with the rotation of K(t+1) between its MFMAs, then this
+    // thread's table entries of K(t+2) (its entries of K(t+1) are consumed);
+    // barrier; S(t+1) = K'(t+1) Q'^T, masks, softmax into P(t+1); barrier.
+    // Every load has an iteration to land, and the other workgroup's wave on
+    // the SIMD runs while a wave waits.
+    auto issue_t = [&](int ut) __attribute__((always_inline)) {
+      const Group g = make_group(ut, ut, ut);
+#pragma unroll
+      for (int i = 0; i < GRP_MAX; ++i)
+        if (i >= 2 * nkw && i < (2 + TPK) * nkw) dma_item(g, i);
+    };
+    // Prologue: K(0), its table entries and V(0); Q; K(0) rotated; K(1) and
+    // its table entries in flight; P(0).
+    if (n > 0) issue_group(0, 0, 0, true, true);
+    load_q_issue();
+    if (SCOREMOD && p.alibi) slope2 = p.alibi[h] * kLog2e;
+    vmcnt_wait<0>();
+    const char* const tl = smem + L::T_OFF + lane * 16;
+    // This thread's chunks of K(u), pair m: operands (rot_read), then the
+    // rotation and the stores (rot_write).
+    struct RotPair {
+      uint4 lo, hi, t0, t1;
+      uint32_t off;  // byte offset of the low chunk in smem
+    };
+    auto rot_read = [&](int u, int m) -> RotPair {
+      const int kp = wave + NW * m;
+      RotPair r;
+      r.off = (uint32_t)((u % RING) * L::KSLOT + kp * 1024 + lane * 16);
+      r.t0 = ld16(tl + kp * L::TPAIR);
+      r.t1 = ld16(tl + kp * L::TPAIR + 1024);
+      r.lo = ld16(smem + r.off);
+      r.hi = ld16(smem + r.off + L::KHI);
+      return r;
+    };
+    auto rot_write = [&](RotPair r) {
+      rope_rotate_bf16x8_t(r.lo, r.hi, r.t0, r.t1);
+      st16(smem + r.off, r.lo);
+      st16(smem + r.off + L::KHI, r.hi);
+    };
+    if (n > 0) {
+      if (ROPE) {
+#pragma unroll
+        for (int m = 0; m < NKW_HI; ++m)
+          if (m < nkw) rot_write(rot_read(0, m));
+      }
+      issue_group(1, 1, 1, true, false);
+    }
+    __syncthreads();
+    load_q_finish();
+    if (n > 0) first_tile();
+    // Iteration 0 refills K slot 0, which every wave has just read for S(0).
+    __syncthreads();
+
+    constexpr int NSA = 2 * NKK;  // S MFMAs per tile
+    constexpr int NSB = 4 * NDT;  // P V MFMAs per tile
+    constexpr int PF = 2;         // fragment prefetch distance
+    static_assert(2 * NKW_HI <= NSB, "rotation steps fit the P V steps");
+    auto iteration = [&](int t, const bf16x8 (&pf)[4], bf16x8 (&pf_next)[4], bool has_s)
+        __attribute__((always_inline)) {
+      vmcnt_wait<0>();
+      issue_group(t + 2, t + 2, t + 1, false, true);
+      // O^T += V^T P^T (tile t); pair m of the rotation of K(t+1): operands
+      // at step 2m, arithmetic and stores at step 2m + 1.
+      const uint32_t vs = lds0 + L::V_OFF + (uint32_t)(t % RING) * L::VSLOT;
+      bf16x8 vfr[PF + 1];
+      RotPair rp[NKW_HI];
+#pragma unroll
+      for (int k = 0; k < PF; ++k) vfr[k] = v_frag(vs, k / NDT, k % NDT);
+#pragma unroll
+      for (int k = 0; k < NSB; ++k) {
+        if (k + PF < NSB) vfr[(k + PF) % (PF + 1)] = v_frag(vs, (k + PF) / NDT, (k + PF) % NDT);
+        o[k % NDT] = mfma32(vfr[k % (PF + 1)], pf[k / NDT], o[k % NDT]);
+        if (k % NDT == NDT - 1) ol = mfma32(ones8, pf[k / NDT], ol);
+        if (ROPE) {
+#pragma unroll
+          for (int m = 0; m < NKW_HI; ++m)
+            if (m < nkw) {
+              if (k == 2 * m) rp[m] = rot_read(t + 1, m);
+              if (k == 2 * m + 1) rot_write(rp[m]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ROPE) issue_t(t + 2);
+      __syncthreads();
+      // S(t+1) = K'(t+1) Q'^T, masks, softmax into P(t+1).
+      const char* ks = smem + ((t + 1) % RING) * L::KSLOT;
+      const int k0n = tile_k0(min(t + 1, n - 1));
+      f32x16 sn[2];
+      bf16x8 afr[PF + 1];
+#pragma unroll
+      for (int k = 0; k < PF; ++k) afr[k] = k_frag(ks, k & 1, k >> 1);
+#pragma unroll
+      for (int k = 0; k < NSA; ++k) {
+        if (k + PF < NSA) afr[(k + PF) % (PF + 1)] = k_frag(ks, (k + PF) & 1, (k + PF) >> 1);
+        sn[k & 1] = mfma32(afr[k % (PF + 1)], qf[k >> 1], k < 2 ? (SCOREMOD ? (CSPLAT ? f32x16{} + mod_base(k0n) : f32x16{}) : minit) : sn[k & 1]);
+      }
+      mask_scores(t + 1, sn);
+      uint32_t pw[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) pw[x] = exp_pair(sn, x, k0n);
+      if (has_s) finish_tile(sn, -neg_m(), pw);
+      to_frags(pw, pf_next);
+      __syncthreads();
+    };
+    // One block of a chain at a time, as in the four-slot schedule below.
+    int seg0 = 0;
+    for (int c = 0; c < n_chain; ++c) {
+      const bool last_seg = c == n_chain - 1;
+      const int seg1 = last_seg ? n : seg_end(c, seg0);
+      if (c > 0) {
+        store_block_regs();
+        set_rows(qblk + c);
+        load_q_issue();
+        reset_softmax();
+        load_q_finish();
+        if (seg1 > seg0) first_tile_at(seg0, pfa);
+        __syncthreads();
+      }
+      ATTNFUSE_RUN_STEPS(iteration, seg0, seg1, last_seg)
+      seg0 = seg1;
+    }
   } else {
     // Prologue: K(0), K(1) loaded and rotated, V(0) loaded; the groups of
     // iterations -2 and -1 ({K(2), V(1)}, {K(3), V(2)}) in flight; P(0).

@@ -416,13 +416,16 @@ PLAN_CASES = [
      dict(kernel=3, waves=8, heads=4, rows=64, query_blocks=15, paired=1, workgroups=256)),
     ("no_queries", dict(B=1, Hq=4, Hkv=4, N=256, D=64, Nq=0),
      dict(kernel=0, waves=0, workgroups=0)),
-    # BigBird (B2 H16 N4096 D64, 64x64 blocks): two waves, 2048 blocks on 512
-    # workgroup slots (two 72 KB workgroups per CU) -> chains of 4
+    # BigBird (B2 H16 N4096 D64, 64x64 blocks): two waves on the shallow
+    # schedule (40 KB, four workgroups per CU), 2048 blocks on 1024 workgroup
+    # slots -> chains of 2
     ("bigbird_chain", dict(B=2, Hq=16, Hkv=16, N=4096, D=64, **_BS64),
-     dict(kernel=2, waves=2, heads=1, rows=64, query_blocks=64, paired=0, chain=4, workgroups=512)),
-    # half as many blocks: chains of 2
-    ("bigbird_chain_2", dict(B=1, Hq=16, Hkv=16, N=4096, D=64, **_BS64), dict(chain=2, workgroups=512)),
+     dict(kernel=2, waves=2, heads=1, rows=64, query_blocks=64, paired=0, chain=2, workgroups=1024)),
+    # at D = 128 (four-slot rings, 144 KB: one workgroup per CU): chains of 8
+    ("bigbird_d128_chain", dict(B=2, Hq=16, Hkv=16, N=4096, D=128, **_BS64),
+     dict(waves=2, chain=8, workgroups=256)),
     # one round of single blocks: no chain
+    ("bigbird_one_round", dict(B=1, Hq=16, Hkv=16, N=4096, D=64, **_BS64), dict(chain=1, workgroups=1024)),
     ("bigbird_small", dict(B=1, Hq=4, Hkv=4, N=1024, D=64, **_BS64), dict(chain=1, workgroups=64)),
     # the caller's chain length; 16 blocks, chains of 3 (the last holds one)
     ("bigbird_chain_3", dict(B=1, Hq=4, Hkv=4, N=1000, D=64, tile_chain=3, **_BS64),
