@@ -30,16 +30,17 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The two- and four-wave forward instances run one
-# wave per SIMD, where the register allocator otherwise parks the MFMA
-# accumulators in AGPRs and copies every score out of them (about a hundred
-# extra moves per key tile); forcing the VGPR form of the MFMAs keeps them
-# under 256 VGPRs without spills.  The eight-wave instances use no AGPRs
-# either way, and the backward kernels would spill under it, so the flag
-# stays on these units only.
+# Per-source extra flags.  In the two- and four-wave forward instances (one
+# wave per SIMD) and the backward's block-sparse dQ kernels the register
+# allocator otherwise parks the MFMA accumulators in AGPRs and copies every
+# score out of them (about a hundred extra moves per key tile in the
+# forward); forcing the VGPR form of the MFMAs keeps them in VGPRs without
+# new spills.  The eight-wave forward instances and the other backward
+# kernels use no AGPRs either way.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 EXTRA_FLAGS = {
-    f"fwd_bf16_d{d}_nw{nw}.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-    for d in (64, 128) for nw in (2, 4)
+    **{f"fwd_bf16_d{d}_nw{nw}.hip": _VGPR_FORM for d in (64, 128) for nw in (2, 4)},
+    **{f"bwd_d{d}.hip": _VGPR_FORM for d in (64, 128)},
 }
 
 

@@ -19,6 +19,11 @@
 // (dO^T, Q'^T, K'^T) are read with ds_read_b64_tr_b16.  Each wave classifies
 // its part of a tile as fully visible (no mask arithmetic), fully masked
 // (skipped) or partial (per-element band and bound tests).
+//
+// The kernels live in this header; bwd_d64.hip and bwd_d128.hip instantiate
+// them for one head dim each (compiled with different register options).
+#pragma once
+
 #include <climits>
 #include <type_traits>
 
@@ -812,12 +817,6 @@ static hipError_t launch_bwd_d(const AttnParams& p, const BwdParams& g, hipStrea
     hipLaunchKernelGGL(bwd_kv_reduce_kernel<D>, dim3((unsigned)((rows_k * CH + 255) / 256)), dim3(256), 0,
                        stream, p, g);
   return hipGetLastError();
-}
-
-hipError_t launch_bwd(const AttnParams& p, const BwdParams& g, int D, hipStream_t stream) {
-  if (D == 64) return launch_bwd_d<64>(p, g, stream);
-  if (D == 128) return launch_bwd_d<128>(p, g, stream);
-  return hipErrorInvalidValue;
 }
 
 }  // namespace attnfuse
