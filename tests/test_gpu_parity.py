@@ -278,6 +278,10 @@ CHAINED = [
     # window, no RoPE, two batches
     ("chain5_window_norope", "bigbird_rope_n4096",
      dict(B=2, Hq=2, Hkv=2, Nq=640, Nk=640, window=100, rope_theta=None), (0, 0, 5)),
+    # the shallow two-slot schedule (D = 64, two waves) with ALiBi, causal,
+    # queries after the keys, ragged tails
+    ("chain2_shallow_alibi_causal", "bigbird_rope_n4096",
+     dict(B=1, Hq=4, Hkv=4, Nq=700, Nk=800, causal=True, alibi=True, q_pos0=100), (0, 0, 2)),
 ]
 
 
