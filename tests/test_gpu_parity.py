@@ -73,6 +73,10 @@ SMALL = [
     ("alibi_window_small", "alibi_causal_window1024_n8192", dict(B=1, Hq=4, Hkv=4, Nq=777, Nk=777, window=100)),
     ("bigbird_small", "bigbird_rope_n4096", dict(B=1, Hq=4, Hkv=4, Nq=1024, Nk=1024)),
     ("bigbird_ragged", "bigbird_rope_n4096", dict(B=1, Hq=2, Hkv=2, Nq=1000, Nk=1000)),
+    # the shallow two-slot schedule at its smallest: one ragged query block and
+    # two key blocks; and more keys than queries (a ragged last key tile)
+    ("bigbird_tiny_ragged", "bigbird_rope_n4096", dict(B=1, Hq=2, Hkv=2, Nq=50, Nk=70)),
+    ("bigbird_keys_past_queries", "bigbird_rope_n4096", dict(B=2, Hq=3, Hkv=3, Nq=333, Nk=777)),
 ]
 
 
