@@ -356,6 +356,19 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
     while (NW > 2 && NW > hp && (NW / hp) / 2 >= rb_need) NW /= 2;
     while (NW > 2 && grid_of(NW) < 128) NW /= 2;
     if (scoremod && NW == 8 && grid_of(8) < 256) NW = 4;
+    // D = 64 with one q-head per workgroup (the GPT-2-small geometry): under
+    // a band (causal or a window) four waves (128-row blocks, two workgroups
+    // and so two waves per SIMD per CU) beat eight (256-row blocks, less of
+    // whose band is visible): a window by 10-40%, causal by 2-16% (N 1k-4k),
+    // unless the eight-wave blocks pair (causal N=8192: 444 us paired
+    // against 452 us on four waves).  Dense launches keep eight waves.
+    if (d->D == 64 && NW == 8 && hp == 1 && (d->causal || d->window > 0)) {
+      AttnParams pp = p;
+      pp.n_units = d->B * d->Hkv * p.G;
+      pp.n_qblk = (d->Nq + 255) / 256;
+      const long long g8 = (long long)pp.n_units * pp.n_qblk;
+      if (pair_blocks(pp, d, 256, true, false, g8) == g8) NW = 4;
+    }
     if (hp > NW) hp = NW;
   }
   if (!attnfuse::fwd_bf16_supported(d->D, NW, rope, scoremod, use_sparse)) {

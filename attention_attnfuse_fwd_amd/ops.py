@@ -335,12 +335,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     ``q_scale * code`` etc.) the fp8 prefill runs and the output is bf16.
     """
     cacheable = (out is not None and not return_lse and alibi_slopes is None and bias is None
-                 and block_mask is None and tile is None)
+                 and block_mask is None)
     if cacheable:
         key = (q.shape, q.stride(), k.shape, k.stride(), v.shape, v.stride(), out.shape, out.stride(),
                q.dtype, k.dtype, v.dtype, out.dtype, q.device, k.device, v.device, out.device,
                causal, window, rope_theta, q_pos0, k_pos0, scale, decode_fast_path, q_scale, k_scale,
-               v_scale)
+               v_scale, None if tile is None else tuple(int(x) for x in tile))
         hit = _FWD_DESCS.get(key)
         if hit is not None:
             dref, entry = hit

@@ -379,12 +379,18 @@ PLAN_CASES = [
     # 512 single blocks (952 tiles per unit) spread over the CUs
     ("llama8b_causal_window", dict(B=1, Hq=32, Hkv=8, N=4096, D=128, causal=1, window=1024),
      dict(paired=0, workgroups=512)),
-    # GPT-2-small, N=4096: 384 pairs would be one and a half rounds
+    # GPT-2-small, N=4096: 384 pairs would be one and a half rounds, so the
+    # causal band takes four waves (128-row blocks)
     ("gpt2_small_causal", dict(B=4, Hq=12, Hkv=12, N=4096, D=64, causal=1),
-     dict(paired=0, workgroups=768)),
-    # N=8192: 768 pairs, three full rounds
+     dict(waves=4, rows=128, query_blocks=32, paired=0, workgroups=1536)),
+    # a two-sided window at D = 64: four waves
+    ("gpt2_small_window", dict(B=4, Hq=12, Hkv=12, N=4096, D=64, window=256),
+     dict(waves=4, rows=128, paired=0, workgroups=1536)),
+    # dense at D = 64 keeps eight waves
+    ("gpt2_small_dense", dict(B=4, Hq=12, Hkv=12, N=4096, D=64), dict(waves=8, workgroups=768)),
+    # N=8192: 768 pairs, three full rounds (eight waves, paired)
     ("gpt2_small_causal_8k", dict(B=4, Hq=12, Hkv=12, N=8192, D=64, causal=1),
-     dict(paired=1, workgroups=768)),
+     dict(waves=8, paired=1, workgroups=768)),
     # the ALiBi + causal + window workload (B=2, H=16, N=8192, W=1024): 32 units x 16 pairs
     ("alibi_window", dict(B=2, Hq=16, Hkv=16, N=8192, D=128, rope=False, causal=1, window=1024,
                           alibi_slopes=FAKE.value),
