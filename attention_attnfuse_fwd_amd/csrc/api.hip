@@ -369,6 +369,18 @@ int plan_fwd(const void* q, const void* k, const void* v, const void* out,
       const long long g8 = (long long)pp.n_units * pp.n_qblk;
       if (pair_blocks(pp, d, 256, true, false, g8) == g8) NW = 4;
     }
+    // Dense D = 64, one q-head per workgroup: eight waves run rounds of 256
+    // workgroups, four waves rounds of 512 (two per CU) at about 1.08 times
+    // the eight-wave time per round, a last round of at most 256 at about
+    // 0.65; four waves when that is clearly shorter (a grid of one and a half
+    // eight-wave rounds, e.g. B4 H12 N2048: 8-12% faster on four waves).
+    if (d->D == 64 && NW == 8 && hp == 1 && !d->causal && d->window == 0 && !scoremod) {
+      const long long g8 = grid_of(8), g4 = grid_of(4);
+      const double cost8 = (double)((g8 + 255) / 256);
+      const long long rem4 = g4 % 512;
+      const double cost4 = (double)(g4 / 512) * 1.08 + (rem4 == 0 ? 0.0 : rem4 <= 256 ? 0.65 : 1.08);
+      if (cost4 < 0.95 * cost8) NW = 4;
+    }
     if (hp > NW) hp = NW;
   }
   if (!attnfuse::fwd_bf16_supported(d->D, NW, rope, scoremod, use_sparse)) {

@@ -386,8 +386,11 @@ PLAN_CASES = [
     # a two-sided window at D = 64: four waves
     ("gpt2_small_window", dict(B=4, Hq=12, Hkv=12, N=4096, D=64, window=256),
      dict(waves=4, rows=128, paired=0, workgroups=1536)),
-    # dense at D = 64 keeps eight waves
+    # dense at D = 64 keeps eight waves in whole rounds (768 = 3 x 256) ...
     ("gpt2_small_dense", dict(B=4, Hq=12, Hkv=12, N=4096, D=64), dict(waves=8, workgroups=768)),
+    ("gpt2_small_dense_1k", dict(B=4, Hq=12, Hkv=12, N=1024, D=64), dict(waves=8, workgroups=192)),
+    # ... and takes four waves when eight would make one and a half rounds (384)
+    ("gpt2_small_dense_2k", dict(B=4, Hq=12, Hkv=12, N=2048, D=64), dict(waves=4, workgroups=768)),
     # N=8192: 768 pairs, three full rounds (eight waves, paired)
     ("gpt2_small_causal_8k", dict(B=4, Hq=12, Hkv=12, N=8192, D=64, causal=1),
      dict(waves=8, paired=1, workgroups=768)),
