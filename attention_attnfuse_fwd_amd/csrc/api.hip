@@ -619,6 +619,11 @@ int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, c
   const attnfuse_variant_desc* d = desc;
   if (d->dtype != ATTNFUSE_BF16 || d->kv_fp8 || d->q_fp8) return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->bs_row_ptr && (d->bs_block_m % 64 || d->bs_block_n % 64)) return ATTNFUSE_ERR_UNSUPPORTED;
+  // The gradient kernels address a tile's rows by 32-bit offsets from the
+  // tile's first row.
+  if (d->q_stride[2] >= kMaxRowStride || d->k_stride[2] >= kMaxRowStride ||
+      d->v_stride[2] >= kMaxRowStride || d->o_stride[2] >= kMaxRowStride)
+    return ATTNFUSE_ERR_UNSUPPORTED;
   if (d->Nq > 0 && (!q || !out || !dout || !lse || !dq)) return ATTNFUSE_ERR_INVALID;
   if (d->Nk > 0 && (!k || !v || !dk || !dv)) return ATTNFUSE_ERR_INVALID;
   if (!fp32_tables_ok(d)) return ATTNFUSE_ERR_INVALID;

@@ -14,8 +14,10 @@
 //
 // All products run on bf16 MFMA (32x32x16, fp32 accumulate) with P and dS
 // rounded to bf16.  Tiles are staged through swizzled row-major LDS, double
-// buffered: the next tile's global loads are in flight during the current
-// tile's products and one barrier separates tiles.  The transposed operands
+// buffered: the next tile's loads are in flight during the current tile's
+// products (the dK/dV pass moves its Q' and dO tiles by direct global -> LDS
+// DMA, which holds no registers) and one barrier separates tiles.  LDS
+// operands of the products are read two products ahead.  The transposed operands
 // (dO^T, Q'^T, K'^T) are read with ds_read_b64_tr_b16.  Each wave classifies
 // its part of a tile as fully visible (no mask arithmetic), fully masked
 // (skipped) or partial (per-element band and bound tests).
@@ -452,13 +454,31 @@ __global__ void __launch_bounds__(SPARSE ? 128 : kDqThreads, 1) bwd_dq_kernel(co
       if (skip) continue;  // dS = 0
       const bool full = i0 + 31 < p.Nq && ka + 31 < p.Nk &&
                         (!p.has_band || (ka - (i0 + 31) >= p.band_lo && ka + 31 - i0 <= p.band_hi));
-      // S^T and dP^T (lane = query column).
-      f32x16 sa = f32x16{}, da = f32x16{};
+      // S^T and dP^T (lane = query column), alternating products; each
+      // product's LDS operand is read PF products ahead, so that its latency
+      // hides behind the products in between.
+      constexpr int NS = 2 * NKK, PF = 2;
+      auto s_frag = [&](int k) { return lo.rowf((k & 1) ? vs_lds : ks_lds, 32 * st, k >> 1); };
+      bf16x8 fr[PF + 1];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sa = mfma32(lo.rowf(ks_lds, 32 * st, kk), qf[kk], sa);
-        da = mfma32(lo.rowf(vs_lds, 32 * st, kk), df[kk], da);
+      for (int k = 0; k < PF; ++k) fr[k] = s_frag(k);
+      f32x16 sa, da;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        if (k + PF < NS) fr[(k + PF) % (PF + 1)] = s_frag(k + PF);
+        if (k & 1)
+          da = mfma32(fr[k % (PF + 1)], df[k >> 1], k < 2 ? f32x16{} : da);
+        else
+          sa = mfma32(fr[k % (PF + 1)], qf[k >> 1], k < 2 ? f32x16{} : sa);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // The first transposed K' operands of the dQ products are read before
+      // the exponentials.
+      constexpr int NQ = 2 * NDT;
+      auto q_frag = [&](int k) { return lo.trf(ks_lds, 32 * st + 16 * (k / NDT), k % NDT); };
+      bf16x8 tq[PF + 1];
+#pragma unroll
+      for (int k = 0; k < PF; ++k) tq[k] = q_frag(k);
       // dS^T = P^T (dP^T - delta), packed to bf16 in 16-key chunks.
       bf16x8 dsf[2], unused[2];
       if (full)
@@ -468,10 +488,11 @@ __global__ void __launch_bounds__(SPARSE ? 128 : kDqThreads, 1) bwd_dq_kernel(co
       // dQ'^T += K'^T dS^T (chunk-major, so that consecutive products
       // update different accumulators).
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          acc[dt] = mfma32(lo.trf(ks_lds, 32 * st + 16 * c, dt), dsf[c], acc[dt]);
+      for (int k = 0; k < NQ; ++k) {
+        if (k + PF < NQ) tq[(k + PF) % (PF + 1)] = q_frag(k + PF);
+        acc[k % NDT] = mfma32(tq[k % (PF + 1)], dsf[k / NDT], acc[k % NDT]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (t + 1 < ntiles) {  // the other buffer was last read before the previous barrier
       __bf16* nk = smem + ((t + 1) & 1) * 2 * TILE;
@@ -546,12 +567,27 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
   const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 64 + 1 : 0;
   const int t_begin = (int)((long long)part * ntq * p.G / g.kv_parts);
   const int t_end = (int)((long long)(part + 1) * ntq * p.G / g.kv_parts);
-  RowStage<D, 64, kKvThreads> qst, dst;
+  // A step's Q' and dO tiles (64 rows each) go global -> LDS by direct DMA:
+  // wave w moves 1 KB pieces w * DPW .. w * DPW + DPW - 1 of each tile (RPD
+  // rows of 16-byte chunks per piece, lane l writing position l % CPR of row
+  // l / CPR, which holds chunk (l % CPR) ^ swz(row)).  Rows past Nq are
+  // clamped to the last row.  The lse and delta of the step's rows go
+  // through registers (64 threads) into the stat area.
+  constexpr int CPR = D / 8, RPD = 64 / CPR, DPW = (64 * CPR / 64) / 8;
+  static_assert(DPW * 8 * RPD == 64, "the eight waves cover the 64 rows of a tile");
   float st_l2 = 0.f, st_delta = 0.f;
-  auto load_step = [&](int t) {
+  auto dma_step = [&](int t, int buf) {
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
-    qst.load(g.qr + b * g.qr_sb + h * g.qr_sh, g.qr_sn, q0, p.Nq);
-    dst.load(g.dout + b * p.osb + h * p.osh, p.osn, q0, p.Nq);
+    const __bf16* qb = g.qr + b * g.qr_sb + h * g.qr_sh + (long long)q0 * g.qr_sn;
+    const __bf16* ob = g.dout + b * p.osb + h * p.osh + (long long)q0 * p.osn;
+    const uint32_t t_lds = lds_addr(tiles + buf * 2 * TILE);
+#pragma unroll
+    for (int m = 0; m < DPW; ++m) {
+      const int piece = wave * DPW + m, r = piece * RPD + lane / CPR;
+      const int rc = min(r, p.Nq - 1 - q0), c = (lane % CPR) ^ swz<D>(r);
+      dma16_off(t_lds + 1024 * piece, qb, (uint32_t)((long long)rc * g.qr_sn * 2 + 16 * c));
+      dma16_off(t_lds + TILE * 2 + 1024 * piece, ob, (uint32_t)((long long)rc * p.osn * 2 + 16 * c));
+    }
     if (threadIdx.x < 64) {
       const int ii = q0 + (int)threadIdx.x;
       const long long rr = ((long long)b * p.Hq + h) * p.Nq + min(ii, p.Nq - 1);
@@ -560,9 +596,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
       st_delta = g.delta[rr];
     }
   };
-  auto store_step = [&](int buf) {
-    qst.store(tiles + buf * 2 * TILE);
-    dst.store(tiles + buf * 2 * TILE + TILE);
+  auto store_stat = [&](int buf) {
     if (threadIdx.x < 64) {
       stat[buf][0][threadIdx.x] = st_l2;
       stat[buf][1][threadIdx.x] = st_delta;
@@ -609,12 +643,15 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
   int cur = next_vis(t_begin);
   int nxt = cur < t_end ? next_vis(cur + 1) : t_end;
   if (cur < t_end) {
-    load_step(cur);
-    store_step(0);
-    if (nxt < t_end) load_step(nxt);
+    dma_step(cur, 0);
+    store_stat(0);
+    vmcnt_wait<0>();
   }
   __syncthreads();
   for (int buf = 0; cur < t_end; buf ^= 1) {
+    // The next step's tiles go to the other buffer while this step runs
+    // (that buffer was last read before the previous barrier).
+    if (nxt < t_end) dma_step(nxt, buf ^ 1);
     const int t = cur;
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
     const __bf16* qs = tiles + buf * 2 * TILE;
@@ -625,21 +662,32 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
     const bool skip = ia >= p.Nq || jw >= p.Nk ||
                       (p.has_band && (jwl - ia < p.band_lo || jw - ib > p.band_hi)) ||
                       (SPARSE && !(vis(t) & wbit));
-    // S and dP (32 query rows x the wave's 32 keys; lane = key column).
+    // S and dP (32 query rows x the wave's 32 keys; lane = key column),
+    // alternating products; each product's two LDS operands are read PF
+    // products ahead.
     f32x16 sa = f32x16{}, da = f32x16{};
     if (!skip) {
+      constexpr int NS = 2 * NKK, PF = 2;
+      auto a_frag = [&](int k) { return row_frag<D>((k & 1) ? dos : qs, 32 * st + lq, k >> 1); };
+      auto b_frag = [&](int k) { return row_frag<D>((k & 1) ? vblk_s : kblk_s, 32 * kw + lq, k >> 1); };
+      bf16x8 fa[PF + 1], fb[PF + 1];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sa = mfma32(row_frag<D>(qs, 32 * st + lq, kk), row_frag<D>(kblk_s, 32 * kw + lq, kk), sa);
-        da = mfma32(row_frag<D>(dos, 32 * st + lq, kk), row_frag<D>(vblk_s, 32 * kw + lq, kk), da);
+      for (int k = 0; k < PF; ++k) {
+        fa[k] = a_frag(k);
+        fb[k] = b_frag(k);
       }
-    }
-    // The next step's tiles go to the other buffer while the products run
-    // (that buffer was last read before the previous barrier).
-    const int nn = nxt < t_end ? next_vis(nxt + 1) : t_end;
-    if (nxt < t_end) {
-      store_step(buf ^ 1);
-      if (nn < t_end) load_step(nn);
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        if (k + PF < NS) {
+          fa[(k + PF) % (PF + 1)] = a_frag(k + PF);
+          fb[(k + PF) % (PF + 1)] = b_frag(k + PF);
+        }
+        if (k & 1)
+          da = mfma32(fa[k % (PF + 1)], fb[k % (PF + 1)], da);
+        else
+          sa = mfma32(fa[k % (PF + 1)], fb[k % (PF + 1)], sa);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (!skip) {  // else P = dS = 0
       const bool full = ia + 31 < p.Nq && jw + 31 < p.Nk &&
@@ -671,9 +719,11 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
       chunk(std::integral_constant<int, 0>{});
       chunk(std::integral_constant<int, 1>{});
     }
+    if (nxt < t_end) store_stat(buf ^ 1);
+    vmcnt_wait<0>();  // the next step's tiles have landed
     __syncthreads();
     cur = nxt;
-    nxt = nn;
+    nxt = nxt < t_end ? next_vis(nxt + 1) : t_end;
   }
   // Waves 4..7 hand their sums to waves 0..3 (dK' in the tile area, dV in the
   // block area; every wave has passed the loop's last barrier).

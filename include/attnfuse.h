@@ -336,7 +336,8 @@ size_t attnfuse_bwd_workspace_size(const attnfuse_variant_desc* desc);
  * alibi, additive_bias (a constant of the forward: no bias gradient) and
  * block_sparse (both gradient passes visit only listed blocks; bs_block_m
  * and bs_block_n multiples of 64, else ATTNFUSE_ERR_UNSUPPORTED); fp32
- * returns ATTNFUSE_ERR_UNSUPPORTED.
+ * returns ATTNFUSE_ERR_UNSUPPORTED, and so do row strides (q_stride[2],
+ * k_stride[2], v_stride[2], o_stride[2]) of 2^24 elements or more.
  * All pointers 16-byte aligned.  Runs three to six kernels on `stream` (with
  * rope the two rotations first; with split key blocks a final reduction).  */
 int attnfuse_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,

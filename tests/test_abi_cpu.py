@@ -195,6 +195,11 @@ def test_bwd_validation(lib):
     assert call(_good_desc(bs_row_ptr=0x1000, bs_col_idx=0x2000, bs_block_m=64, bs_block_n=32,
                            bs_nnz=1), FAKE, need) == _abi.ERR_UNSUPPORTED
     assert call(_good_desc(dtype=_abi.FP32), FAKE, 10**9) == _abi.ERR_UNSUPPORTED
+    # the gradient kernels address a tile's rows by 32-bit offsets: row strides below 2^24
+    for field in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        dw = _good_desc()
+        getattr(dw, field)[2] = 1 << 24
+        assert call(dw, FAKE, need) == _abi.ERR_UNSUPPORTED, field
     # the backward reads the fp32 cos / sin tables
     assert call(_good_desc(rope=1, rope_theta=1e4, rope_cs_f16=0x1000, rope_cs_bf16=0x2000,
                            rope_table_len=10**5), FAKE, need) == _abi.ERR_INVALID
