@@ -157,6 +157,32 @@ struct RowStage {
   }
 };
 
+// Rows [r0, r0 + 64) of a [N, D] bf16 plane (row stride sn elements, rows
+// clamped to N - 1; r0 may lie past the last row) into a swizzled LDS tile
+// by direct global -> LDS DMA.  The tile's D / 8 pieces of 1 KB (RPD rows
+// each) are shared by the NW waves; lane l of a piece writes position l % CPR
+// of row l / CPR, which holds chunk (l % CPR) ^ swz(row).  The load is
+// counted by vmcnt only (the caller waits for it before the barrier that
+// publishes the tile).  Row offsets from the first row are 32-bit: the host
+// keeps row strides below 2^24 elements.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile64(uint32_t tile_lds, const __bf16* plane, long long sn, int r0,
+                                           int N) {
+  constexpr int CPR = D / 8, RPD = 64 / CPR, PIECES = 64 / RPD, PPW = PIECES / NW;
+  static_assert(PPW * NW == PIECES, "the waves share the pieces of a tile evenly");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = min(r0, N - 1);
+  const __bf16* base = plane + (long long)rb * sn;
+#pragma unroll
+  for (int m = 0; m < PPW; ++m) {
+    const int piece = wave * PPW + m, r = piece * RPD + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(r);
+    const int row = min(r0 + r, N - 1);
+    dma16_off(tile_lds + 1024 * piece, base, (uint32_t)((long long)(row - rb) * sn * 2 + 16 * c));
+  }
+}
+
 // Register fragments of one row (lane's row) as a B operand over the head
 // dim: f[kk] = row[16 kk + 8 kb .. +7].
 template <int D>
@@ -567,27 +593,15 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
   const int ntq = i_hi >= i_lo ? (i_hi - qt0) / 64 + 1 : 0;
   const int t_begin = (int)((long long)part * ntq * p.G / g.kv_parts);
   const int t_end = (int)((long long)(part + 1) * ntq * p.G / g.kv_parts);
-  // A step's Q' and dO tiles (64 rows each) go global -> LDS by direct DMA:
-  // wave w moves 1 KB pieces w * DPW .. w * DPW + DPW - 1 of each tile (RPD
-  // rows of 16-byte chunks per piece, lane l writing position l % CPR of row
-  // l / CPR, which holds chunk (l % CPR) ^ swz(row)).  Rows past Nq are
-  // clamped to the last row.  The lse and delta of the step's rows go
-  // through registers (64 threads) into the stat area.
-  constexpr int CPR = D / 8, RPD = 64 / CPR, DPW = (64 * CPR / 64) / 8;
-  static_assert(DPW * 8 * RPD == 64, "the eight waves cover the 64 rows of a tile");
+  // A step's Q' and dO tiles (64 rows each) go global -> LDS by direct DMA;
+  // the lse and delta of its rows go through registers (64 threads) into the
+  // stat area.
   float st_l2 = 0.f, st_delta = 0.f;
   auto dma_step = [&](int t, int buf) {
     const int h = kvh * p.G + t / ntq, q0 = qt0 + 64 * (t % ntq);
-    const __bf16* qb = g.qr + b * g.qr_sb + h * g.qr_sh + (long long)q0 * g.qr_sn;
-    const __bf16* ob = g.dout + b * p.osb + h * p.osh + (long long)q0 * p.osn;
     const uint32_t t_lds = lds_addr(tiles + buf * 2 * TILE);
-#pragma unroll
-    for (int m = 0; m < DPW; ++m) {
-      const int piece = wave * DPW + m, r = piece * RPD + lane / CPR;
-      const int rc = min(r, p.Nq - 1 - q0), c = (lane % CPR) ^ swz<D>(r);
-      dma16_off(t_lds + 1024 * piece, qb, (uint32_t)((long long)rc * g.qr_sn * 2 + 16 * c));
-      dma16_off(t_lds + TILE * 2 + 1024 * piece, ob, (uint32_t)((long long)rc * p.osn * 2 + 16 * c));
-    }
+    dma_tile64<D, kKvThreads / 64>(t_lds, g.qr + b * g.qr_sb + h * g.qr_sh, g.qr_sn, q0, p.Nq);
+    dma_tile64<D, kKvThreads / 64>(t_lds + TILE * 2, g.dout + b * p.osb + h * p.osh, p.osn, q0, p.Nq);
     if (threadIdx.x < 64) {
       const int ii = q0 + (int)threadIdx.x;
       const long long rr = ((long long)b * p.Hq + h) * p.Nq + min(ii, p.Nq - 1);
