@@ -719,15 +719,25 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkdv_kernel(const AttnParam
           L2[4 * a4] = l4.x; L2[4 * a4 + 1] = l4.y; L2[4 * a4 + 2] = l4.z; L2[4 * a4 + 3] = l4.w;
           Dl[4 * a4] = d4.x; Dl[4 * a4 + 1] = d4.y; Dl[4 * a4 + 2] = d4.z; Dl[4 * a4 + 3] = d4.w;
         }
+        constexpr int NG = 2 * NDT, PF = 2;
+        auto t_frag = [&](int k) { return tr_frag<D>((k & 1) ? qs_lds : dos_lds, 32 * st + 16 * c, 32 * (k >> 1)); };
+        bf16x8 tf[PF + 1];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) tf[k] = t_frag(k);
         bf16x8 pf[2], dsf[2];
         if (full)
           p_ds<false, SM, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, bias_bh, pf, dsf);
         else
           p_ds<true, SM, true, true, c, c + 1>(sa, da, L2, Dl, ia, j, p, slope2, dpos, bias_bh, pf, dsf);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          dv[dt] = mfma32(tr_frag<D>(dos_lds, 32 * st + 16 * c, 32 * dt), pf[c], dv[dt]);
-          dk[dt] = mfma32(tr_frag<D>(qs_lds, 32 * st + 16 * c, 32 * dt), dsf[c], dk[dt]);
+        for (int k = 0; k < NG; ++k) {
+          if (k + PF < NG) tf[(k + PF) % (PF + 1)] = t_frag(k + PF);
+          if (k & 1)
+            dk[k >> 1] = mfma32(tf[k % (PF + 1)], dsf[c], dk[k >> 1]);
+          else
+            dv[k >> 1] = mfma32(tf[k % (PF + 1)], pf[c], dv[k >> 1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       };
       chunk(std::integral_constant<int, 0>{});
