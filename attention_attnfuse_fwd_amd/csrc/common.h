@@ -161,6 +161,18 @@ __device__ __forceinline__ f32x16 mfma32_f8(const i32x8& a, const i32x8& b, cons
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Streaming loads (non-temporal hint): data read once, such as a decode's
+// KV cache, should not displace what the caches hold for reuse.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8_stream(const void* p) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // 8 consecutive fp32 values (two 16-byte loads).

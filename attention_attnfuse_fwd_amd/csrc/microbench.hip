@@ -84,8 +84,9 @@ __global__ __launch_bounds__(256) void mb_mfma_bf16_ops_kernel(int iters, const 
   }
 }
 
-// Grid-stride read of n16 16-byte words, four loads in flight per thread; the
-// XOR of everything read goes to sink so that no load can be dropped.
+// Grid-stride read of n16 16-byte words, four streaming (non-temporal) loads
+// in flight per thread, the load the decode uses for its KV cache; the XOR of
+// everything read goes to sink so that no load can be dropped.
 __global__ __launch_bounds__(256) void mb_read_kernel(const uint4* __restrict__ src,
                                                       unsigned long long n16, float* sink,
                                                       unsigned long long* stamps) {
@@ -99,15 +100,15 @@ __global__ __launch_bounds__(256) void mb_read_kernel(const uint4* __restrict__ 
   unsigned long long i = (unsigned long long)blockIdx.x * 256 + threadIdx.x;
   uint32_t acc = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = src[i];
-    const uint4 v1 = src[i + stride];
-    const uint4 v2 = src[i + 2 * stride];
-    const uint4 v3 = src[i + 3 * stride];
+    const uint4 v0 = ld16_stream(src + i);
+    const uint4 v1 = ld16_stream(src + i + stride);
+    const uint4 v2 = ld16_stream(src + i + 2 * stride);
+    const uint4 v3 = ld16_stream(src + i + 3 * stride);
     acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
     acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
   }
   for (; i < n16; i += stride) {
-    const uint4 v = src[i];
+    const uint4 v = ld16_stream(src + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   sink[blockIdx.x * 256 + threadIdx.x] = __uint_as_float(acc);

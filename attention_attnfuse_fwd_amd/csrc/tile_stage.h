@@ -71,11 +71,11 @@ struct KStage {
         const int kj = min(k0 + j, key_end - 1);
         const T* src = kb + (long long)kj * p.ksn + 8 * c;
         if constexpr (KV8) {
-          lo8[u] = *reinterpret_cast<const uint2*>(src);
-          hi8[u] = *reinterpret_cast<const uint2*>(src + D / 2);
+          lo8[u] = ld8_stream(src);
+          hi8[u] = ld8_stream(src + D / 2);
         } else {
-          lo[u] = ld16(src);
-          hi[u] = ld16(src + D / 2);
+          lo[u] = ld16_stream(src);
+          hi[u] = ld16_stream(src + D / 2);
         }
       }
     }
@@ -136,8 +136,8 @@ struct VStage {
         for (int b = 0; b < 4; ++b) {
           const int kj = min(k0 + 4 * run + b, key_end - 1);
           const T* src = vb + (long long)kj * p.vsn + 8 * dc;
-          if constexpr (KV8) v8[u][b] = *reinterpret_cast<const uint2*>(src);
-          else v[u][b] = ld16(src);
+          if constexpr (KV8) v8[u][b] = ld8_stream(src);
+          else v[u][b] = ld16_stream(src);
         }
       }
     }
