@@ -1186,12 +1186,23 @@ fwd_bf16_kernel(const AttnParams p) {
       }
       if (has_s) {
         const int k0s = tile_k0(min(st, n - 1));
-        mask_scores(st, sn);
-        uint32_t pw[16];
+        // A tile no key of which this wave's rows may see (the band's far
+        // edge, a window's start, past the keys): P = 0 without the masks
+        // and the exponentials; it leaves m, l and O as they are.  (Not in
+        // the RoPE instances: at their register limit the test spills.)
+        const bool dead = !ROPE && (st >= n || k0s >= Nk ||
+                                    (has_band && (k0s + 63 - w0 < band_lo || k0s - w_last > band_hi)));
+        if (dead) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) pw[x] = exp_pair(sn, x, k0s);
-        finish_tile(sn, -neg_m(), pw);
-        to_frags(pw, pf_next);
+          for (int c = 0; c < 4; ++c) pf_next[c] = bf16x8{};
+        } else {
+          mask_scores(st, sn);
+          uint32_t pw[16];
+#pragma unroll
+          for (int x = 0; x < 16; ++x) pw[x] = exp_pair(sn, x, k0s);
+          finish_tile(sn, -neg_m(), pw);
+          to_frags(pw, pf_next);
+        }
         if (st + 1 < n) bias_fetch(tile_k0(st + 1));
       }
       if (ROPE) {
