@@ -9,6 +9,7 @@ head mapping, the log base of the saved statistic, a dropped bias term, ...).
 import os
 import types
 
+import numpy as np
 import pytest
 
 from oracle_pins import ALL_PINS
@@ -59,7 +60,9 @@ def test_some_pin_catches_mutation(name):
     caught = []
     for pin in ALL_PINS:
         try:
-            pin(mod)
+            # a planted mistake may produce inf - inf; that is part of being caught
+            with np.errstate(invalid="ignore"):
+                pin(mod)
         except Exception:  # an assertion or a shape error both mean "caught"
             caught.append(pin.__name__)
     assert caught, f"no pin caught mutation {name}"
