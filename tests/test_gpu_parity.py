@@ -264,6 +264,37 @@ def test_paired_workgroups_elementwise(name, base, over):
     check_lse(lse, rlse, 2e-2, f"{name} (all {lse.size} rows)")
 
 
+# The eight-wave kernel without RoPE skips the masks and exponentials of the
+# key tiles a wave's 32 rows cannot see (a window's start, keys past a
+# block's diagonal or past the end of the keys): every element against the
+# oracle, the eight-wave tile forced.
+DEAD_TILES = [
+    # plain causal window, GQA, ragged tail
+    ("dead_plain_window_gqa", "llama3_8b_rope_causal_n4096",
+     dict(B=2, Hq=16, Hkv=4, Nq=915, Nk=915, window=200, rope_theta=None)),
+    # queries after the keys, a window shorter than a key tile
+    ("dead_plain_window_after_keys", "llama3_8b_rope_causal_n4096",
+     dict(B=1, Hq=8, Hkv=2, Nq=700, Nk=900, q_pos0=200, window=50, rope_theta=None)),
+    # per-head additive bias under a causal window
+    ("dead_bias_window", "bias_heads_causal_n2048", dict(B=1, Hq=4, Hkv=4, Nq=600, Nk=600, window=120)),
+]
+
+
+@pytest.mark.parametrize("name,base,over", DEAD_TILES, ids=[c[0] for c in DEAD_TILES])
+def test_eight_wave_tiles_a_wave_cannot_see(name, base, over):
+    w = W[base].with_(**over)
+    inp = workloads.make_inputs(w)
+    log(f"case {name}: {w}")
+    q, k, v = dev_inputs(inp)
+    plan = af.fwd_plan(q, k, v, tile=(8, 0), **_gpu_kw(w, inp))
+    log(f"plan {plan}")
+    assert plan["kernel"] == "bf16" and plan["waves"] == 8, plan
+    out, lse = _run(w, inp, tile=(8, 0))
+    ref, rlse = oracle_all_heads(inp.q, inp.k, inp.v, w.B, w.Hq, **_oracle_kw(w, inp))
+    check_close(out, ref, w.dtype, f"{name} (all {out.size} elements)")
+    check_lse(lse, rlse, 2e-2, f"{name} (all {lse.size} rows)")
+
+
 # Chained workgroups: block-sparse launches on two or four waves run `chain`
 # consecutive query blocks of one head as one stream of key tiles (the
 # full-size BigBird workload above runs the library's chains of 4).  Besides
